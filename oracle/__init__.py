@@ -1,0 +1,171 @@
+"""Plain CPU oracle for the DeepSeek Sparse Attention decode hot path.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` are the only callers.  The product path
+(``sparse_attention_indexer_amd``) never imports this package, and this
+package never imports the product.
+
+The arithmetic lives in ``dsa_oracle.c`` (plain C, fp64 sums, OpenMP over
+query rows), built with gcc into ``liboracle.so``.  This module only
+marshals numpy arrays.  Conventions for array arguments:
+
+* bf16 tensors are ``np.uint16`` arrays of raw bfloat16 bits;
+* fp8 tensors are ``np.uint8`` arrays of OCP e4m3fn codes;
+* everything else is ``np.float32`` / ``np.int32`` as documented per call.
+
+Every function accepts ``rows``: an optional list of flattened query rows
+``b*T + t`` to compute (the rest of the output is left as NaN / -2), so a
+large workload can be checked on a sample of rows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+FP8_E4M3 = 1
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (IEEE semantics: no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _load(path: str | None = None):
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _bind(lib):
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.oracle_index_scores.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                        vp, i64, vp]
+    lib.oracle_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, i64, vp]
+    lib.oracle_mla.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                               vp, i64, vp, vp]
+    for fn in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_mla):
+        fn.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = {-1: "bad argument", -2: "non-finite input", -3: "position out of range"}
+        raise ValueError(f"oracle {what}: {msg.get(status, status)}")
+
+
+def index_scores(q, w, k_cache, end_pos, scale, T=None, q_scale=None, k_scale=None, rows=None,
+                 lib=None):
+    """Indexer scores I[b,t,s] = scale * sum_h w[b,t,h] * ReLU(q[b,t,h] . k[b,s]).
+
+    q: [B,T,H,D] uint16 (bf16 bits) or uint8 (e4m3 codes, then q_scale [B,T,H]
+    and k_scale [B,S_max] are required); w: [B,T,H] float32; k_cache:
+    [B,S_max,D] same dtype as q; end_pos: [B] int32.  Returns float32
+    [B,T,S_max] with NaN past each row's causal bound (and in skipped rows).
+    """
+    lib = lib or _load()
+    dtype = BF16 if q.dtype == np.uint16 else FP8_E4M3
+    if dtype == FP8_E4M3 and q.dtype != np.uint8:
+        raise TypeError("q must be uint16 (bf16 bits) or uint8 (e4m3 codes)")
+    B, T_, H, D = q.shape
+    S_max = k_cache.shape[1]
+    q = _c(q, q.dtype)
+    k_cache = _c(k_cache, k_cache.dtype)
+    w = _c(w, np.float32)
+    end_pos = _c(end_pos, np.int32)
+    q_scale = _c(q_scale, np.float32)
+    k_scale = _c(k_scale, np.float32)
+    out = np.full((B, T_, S_max), np.nan, dtype=np.float32)
+    r, nr = _rows(rows)
+    st = lib.oracle_index_scores(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                                 _ptr(end_pos), B, T_, S_max, H, D, float(scale), dtype,
+                                 _ptr(r), nr, _ptr(out))
+    _check(st, "index_scores")
+    return out
+
+
+def topk(scores, end_pos, k, rows=None, lib=None):
+    """Top-k positions per row: ascending order, ties to the smaller position, -1 padded.
+
+    scores: [B,T,S_max] float32; end_pos: [B] int32.  Returns int32 [B,T,k]
+    (rows not in ``rows`` are filled with -2).
+    """
+    lib = lib or _load()
+    B, T, S_max = scores.shape
+    scores = _c(scores, np.float32)
+    end_pos = _c(end_pos, np.int32)
+    out = np.full((B, T, k), -2, dtype=np.int32)
+    r, nr = _rows(rows)
+    st = lib.oracle_topk(_ptr(scores), _ptr(end_pos), B, T, S_max, int(k), _ptr(r), nr, _ptr(out))
+    _check(st, "topk")
+    return out
+
+
+def mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, softmax_scale, indices=None, rows=None,
+        lib=None):
+    """Absorbed MLA attention with an additive index mask (dense if indices is None).
+
+    q_nope: [B,T,H,Dc], q_pe: [B,T,H,Dr], kv_cache: [B,S_max,Dc], pe_cache:
+    [B,S_max,Dr], all uint16 bf16 bits; indices: [B,T,k] int32 (-1 = empty)
+    or None; end_pos: [B] int32.  Returns (out float64 [B,T,H,Dc],
+    lse float64 [B,T,H]), NaN in rows that were not computed.
+    """
+    lib = lib or _load()
+    B, T, H, Dc = q_nope.shape
+    Dr = q_pe.shape[-1]
+    S_max = kv_cache.shape[1]
+    arrs = [_c(a, np.uint16) for a in (q_nope, q_pe, kv_cache, pe_cache)]
+    idx = _c(indices, np.int32)
+    k = 0 if idx is None else idx.shape[-1]
+    end_pos = _c(end_pos, np.int32)
+    out = np.full((B, T, H, Dc), np.nan, dtype=np.float64)
+    lse = np.full((B, T, H), np.nan, dtype=np.float64)
+    r, nr = _rows(rows)
+    st = lib.oracle_mla(*[_ptr(a) for a in arrs], _ptr(idx), _ptr(end_pos), B, T, S_max, H, Dc,
+                        Dr, k, float(softmax_scale), _ptr(r), nr, _ptr(out), _ptr(lse))
+    _check(st, "mla")
+    return out, lse

@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``check_*`` function takes a loaded oracle library (``lib``), so the same
+pins can be run against deliberately broken builds of the oracle source (see
+test_oracle_mutants.py).  What each pin compares against:
+
+* hand-derived worked examples stored under tests/golden/ (with citations);
+* library routines on special cases: torch matmul (single-head indexer),
+  torch's own bf16/fp8 decoding, torch stable sort (top-k), torch
+  scaled_dot_product_attention and logsumexp in float64 (attention);
+* brute force over every subset of tiny rows (top-k);
+* exact algebraic invariants on integer inputs (sum over heads, linearity in
+  the weights, head permutation) and closed forms (one kept row returns that
+  row, a zero query returns the mean of the kept rows).
+"""
+from __future__ import annotations
+
+import itertools
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def read_golden(name):
+    """Parse a tests/golden fixture: '# comment' lines and 'key = values' entries."""
+    out = {}
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = (s.strip() for s in line.split("=", 1))
+            out[key] = [float(x) for x in val.split()]
+    return out
+
+
+# --- encodings done by torch (independent of the oracle's decoders) ----------
+
+def bf16(x) -> np.ndarray:
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_val(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+
+
+def fp8_val(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def valid_mask(end_pos, T, S_max):
+    """[B,T,S_max] bool: s <= end_pos[b] - T + t."""
+    ep = np.asarray(end_pos).reshape(-1, 1, 1)
+    t = np.arange(T).reshape(1, -1, 1)
+    s = np.arange(S_max).reshape(1, 1, -1)
+    return s <= ep - T + t
+
+
+def close32(a, b, rel=2.0 ** -21):
+    """Agreement of fp32 results whose fp64 sums may have run in another order."""
+    return np.all(np.abs(a - b) <= rel * np.abs(b) + 1e-30)
+
+
+# --- indexer -------------------------------------------------------------------
+
+def check_indexer_golden(lib):
+    g = read_golden("indexer_worked_example.txt")
+    q = bf16(np.array(g["q_t0"] + g["q_t1"]).reshape(1, 2, 2, 2))
+    w = np.array([g["w_t0"], g["w_t1"]], np.float32).reshape(1, 2, 2)
+    k = bf16(np.array(g["k"]).reshape(1, 4, 2))
+    ep = np.array([3], np.int32)
+    out = oracle.index_scores(q, w, k, ep, g["scale"][0], lib=lib)
+    expect = np.array([g["scores_t0"], g["scores_t1"]], np.float32)[None]
+    assert np.array_equal(out, expect, equal_nan=True), out
+    for kk in (2, 4):
+        sel = oracle.topk(out, ep, kk, lib=lib)
+        assert sel[0, 0].tolist() == [int(x) for x in g[f"topk{kk}_t0"]], sel
+        assert sel[0, 1].tolist() == [int(x) for x in g[f"topk{kk}_t1"]], sel
+
+
+def check_fp8_decoding(lib):
+    """Every finite e4m3 code decodes like torch.float8_e4m3fn (q=code, k=+-1, H=D=1)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    B = codes.size
+    q = codes.reshape(B, 1, 1, 1)
+    k = np.tile(np.array([0x38, 0xB8], np.uint8).reshape(1, 2, 1), (B, 1, 1))  # +1, -1
+    ones_q = np.ones((B, 1, 1), np.float32)
+    ones_k = np.ones((B, 2), np.float32)
+    out = oracle.index_scores(q, ones_q, k, np.full(B, 2, np.int32), 1.0, q_scale=ones_q,
+                              k_scale=ones_k, lib=lib)
+    got = out[:, 0, 0].astype(np.float64) - out[:, 0, 1].astype(np.float64)
+    assert np.array_equal(got, fp8_val(codes)), np.nonzero(got != fp8_val(codes))
+
+
+def check_bf16_decoding(lib):
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 1 << 16, size=600, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF][:512]  # finite only
+    B = bits.size
+    q = bits.reshape(B, 1, 1, 1)
+    k = np.tile(bf16([1.0, -1.0]).reshape(1, 2, 1), (B, 1, 1))
+    out = oracle.index_scores(q, np.ones((B, 1, 1), np.float32), k, np.full(B, 2, np.int32), 1.0,
+                              lib=lib)
+    got = out[:, 0, 0].astype(np.float64) - out[:, 0, 1].astype(np.float64)
+    assert np.array_equal(got, bf16_val(bits))
+
+
+def check_single_head_matmul(lib):
+    """H=1: I = fl32(fl32(w * ReLU(q.k)) * scale), with q.k from torch matmul; causal tail unwritten."""
+    rng = np.random.default_rng(3)
+    B, T, S, D = 2, 3, 40, 5
+    ep = np.array([37, 40], np.int32)
+    q = bf16(rng.standard_normal((B, T, 1, D)))
+    k = bf16(rng.standard_normal((B, S, D)))
+    w = rng.standard_normal((B, T, 1)).astype(np.float32)
+    scale = np.float32(0.37)
+    out = oracle.index_scores(q, w, k, ep, scale, lib=lib)
+    dots = torch.matmul(torch.from_numpy(bf16_val(q)[:, :, 0, :]),
+                        torch.from_numpy(bf16_val(k)).transpose(1, 2)).numpy()
+    acc = w.astype(np.float64) * np.maximum(dots, 0.0)
+    expect = acc.astype(np.float32) * scale
+    m = valid_mask(ep, T, S)
+    assert close32(out[m], expect[m])
+    assert np.all(np.isnan(out[~m]))
+
+
+def check_fp8_single_head_matmul(lib):
+    """fp8 values are code * block scale: compare with torch's decoding and matmul."""
+    rng = np.random.default_rng(5)
+    B, T, S, D = 2, 2, 24, 16
+    ep = np.array([24, 19], np.int32)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    q = rng.choice(codes, size=(B, T, 1, D)).astype(np.uint8)
+    k = rng.choice(codes, size=(B, S, D)).astype(np.uint8)
+    q_scale = (rng.random((B, T, 1)) * 0.01 + 1e-3).astype(np.float32)
+    k_scale = (rng.random((B, S)) * 0.01 + 1e-3).astype(np.float32)
+    w = rng.standard_normal((B, T, 1)).astype(np.float32)
+    out = oracle.index_scores(q, w, k, ep, 0.25, q_scale=q_scale, k_scale=k_scale, lib=lib)
+    qd = fp8_val(q)[:, :, 0, :] * q_scale.astype(np.float64)
+    kd = fp8_val(k) * k_scale.astype(np.float64)[..., None]
+    dots = torch.matmul(torch.from_numpy(qd), torch.from_numpy(kd).transpose(1, 2)).numpy()
+    expect = (w.astype(np.float64) * np.maximum(dots, 0.0)).astype(np.float32) * np.float32(0.25)
+    m = valid_mask(ep, T, S)
+    assert close32(out[m], expect[m])
+
+
+def _int_case(rng, B, T, H, D, S):
+    q = bf16(rng.integers(-4, 5, size=(B, T, H, D)))
+    k = bf16(rng.integers(-4, 5, size=(B, S, D)))
+    w = (rng.choice([-1.0, 1.0], size=(B, T, H)) *
+         np.exp2(rng.integers(-3, 4, size=(B, T, H)))).astype(np.float32)
+    return q, k, w
+
+
+def check_head_sum_and_linearity(lib):
+    """Integer inputs (exact): the score is the sum of single-head scores, each equal to the
+    H=1 result on that head's slice; linear in w; invariant under head permutation."""
+    rng = np.random.default_rng(9)
+    B, T, H, D, S = 2, 2, 4, 6, 11
+    ep = np.array([11, 7], np.int32)
+    q, k, w = _int_case(rng, B, T, H, D, S)
+    m = valid_mask(ep, T, S)
+    full = oracle.index_scores(q, w, k, ep, 1.0, lib=lib).astype(np.float64)
+    parts = np.zeros_like(full)
+    for h in range(H):
+        wh = np.zeros_like(w)
+        wh[:, :, h] = w[:, :, h]
+        part = oracle.index_scores(q, wh, k, ep, 1.0, lib=lib)
+        single = oracle.index_scores(np.ascontiguousarray(q[:, :, h:h + 1]),
+                                     np.ascontiguousarray(w[:, :, h:h + 1]), k, ep, 1.0, lib=lib)
+        assert np.array_equal(part[m], single[m])
+        parts += part
+    assert np.array_equal(full[m], parts[m])
+    double = oracle.index_scores(q, 2 * w, k, ep, 1.0, lib=lib).astype(np.float64)
+    assert np.array_equal(double[m], 2 * full[m])
+    perm = rng.permutation(H)
+    permuted = oracle.index_scores(np.ascontiguousarray(q[:, :, perm]),
+                                   np.ascontiguousarray(w[:, :, perm]), k, ep, 1.0, lib=lib)
+    assert np.array_equal(permuted[m], full[m])
+
+
+# --- top-k -----------------------------------------------------------------------
+
+def _brute_topk(vals, k):
+    """The unique subset of size min(k,n) such that every kept x beats every dropped y:
+    vals[x] > vals[y], or equal and x < y.  Found by enumerating all subsets."""
+    n = len(vals)
+    ke = min(k, n)
+    found = []
+    for sub in itertools.combinations(range(n), ke):
+        s = set(sub)
+        ok = all(vals[x] > vals[y] or (vals[x] == vals[y] and x < y)
+                 for x in s for y in range(n) if y not in s)
+        if ok:
+            found.append(list(sub))
+    assert len(found) == 1
+    return found[0] + [-1] * (k - ke)
+
+
+def check_topk_bruteforce(lib):
+    rng = np.random.default_rng(21)
+    S = 8
+    pools = [np.array([0.0, -0.0, 1.0, -1.0, 2.0], np.float32),
+             np.array([3.0, 3.0, 3.0, 1.5], np.float32)]
+    for trial in range(12):
+        B = 4
+        ep = rng.integers(1, S + 1, size=B).astype(np.int32)
+        if trial < 6:
+            scores = rng.choice(pools[trial % 2], size=(B, 1, S)).astype(np.float32)
+        else:
+            scores = rng.standard_normal((B, 1, S)).astype(np.float32)
+        for k in range(1, S + 2):
+            got = oracle.topk(scores, ep, k, lib=lib)
+            for b in range(B):
+                assert got[b, 0].tolist() == _brute_topk(scores[b, 0, :ep[b]].tolist(), k)
+
+
+def check_topk_stable_sort(lib):
+    """Against torch's stable descending sort (ties keep the smaller position first)."""
+    from sparse_attention_indexer_amd import inputs
+    B, T, S = 3, 4, 300
+    ep = np.array([300, 250, 17], np.int32)
+    for kind in ("normal", "ties", "zeros", "relu", "wide"):
+        scores = inputs.make_scores(B, T, S, kind=kind, seed=4).numpy()
+        for k in (1, 5, 64, 300):
+            got = oracle.topk(scores, ep, k, lib=lib)
+            for b in range(B):
+                for t in range(T):
+                    n = ep[b] - T + t + 1
+                    row = torch.from_numpy(scores[b, t, :n].copy())
+                    order = torch.sort(row, descending=True, stable=True).indices[:min(k, n)]
+                    exp = sorted(order.tolist()) + [-1] * (k - min(k, n))
+                    assert got[b, t].tolist() == exp, (kind, k, b, t)
+
+
+def check_topk_special_cases(lib):
+    g = read_golden("short_context.txt")
+    n, k = int(g["n"][0]), int(g["k"][0])
+    scores = np.random.default_rng(2).standard_normal((1, 1, n)).astype(np.float32)
+    got = oracle.topk(scores, np.array([n], np.int32), k, lib=lib)[0, 0]
+    assert got[:int(g["kept"][0])].tolist() == list(range(n))
+    assert np.all(got[n:] == -1) and got.size - n == int(g["padding"][0])
+    eq = np.ones((1, 1, 5000), np.float32)
+    got = oracle.topk(eq, np.array([5000], np.int32), 2048, lib=lib)[0, 0]
+    assert got.tolist() == list(range(2048))
+
+
+# --- attention ---------------------------------------------------------------------
+
+def check_mla_golden(lib):
+    g = read_golden("mla_worked_example.txt")
+    kv = bf16(np.array(g["kv"]).reshape(1, 3, 2))
+    pe = bf16(np.array(g["pe"]).reshape(1, 3, 1))
+    ep = np.array([3], np.int32)
+    for case in ("A", "B"):
+        qn = bf16(np.array(g[f"{case}_q_nope"]).reshape(1, 1, 1, 2))
+        qp = bf16(np.array(g[f"{case}_q_pe"]).reshape(1, 1, 1, 1))
+        o, lse = oracle.mla(qn, qp, kv, pe, ep, 1.0, lib=lib)
+        assert np.allclose(o[0, 0, 0], g[f"{case}_dense_o"], rtol=1e-14, atol=0)
+        assert np.allclose(lse[0, 0, 0], g[f"{case}_dense_lse"][0], rtol=1e-14, atol=0)
+    qn = bf16(np.array(g["A_q_nope"]).reshape(1, 1, 1, 2))
+    qp = bf16(np.array(g["A_q_pe"]).reshape(1, 1, 1, 1))
+    for idx, key in (([0, 2], "idx02"), ([2, 0], "idx02"), ([1, -1], "idx1")):
+        o, lse = oracle.mla(qn, qp, kv, pe, ep, 1.0, indices=np.array(idx, np.int32)
+                            .reshape(1, 1, 2), lib=lib)
+        assert np.allclose(o[0, 0, 0], g[f"A_{key}_o"], rtol=1e-14, atol=0), (idx, o)
+        assert np.allclose(lse[0, 0, 0], g[f"A_{key}_lse"][0], rtol=1e-14, atol=0), (idx, lse)
+
+
+def _mla_case(rng, B, T, H, Dc, Dr, S):
+    return (bf16(rng.standard_normal((B, T, H, Dc))), bf16(rng.standard_normal((B, T, H, Dr))),
+            bf16(rng.standard_normal((B, S, Dc))), bf16(rng.standard_normal((B, S, Dr))))
+
+
+def _sdpa(qn, qp, kv, pe, rows, scale):
+    """torch SDPA (float64) of one (b,t) over the given cached rows; returns (o [H,Dc], lse [H])."""
+    q = torch.from_numpy(np.concatenate([bf16_val(qn), bf16_val(qp)], -1))       # [H, Dc+Dr]
+    kk = torch.from_numpy(np.concatenate([bf16_val(kv[rows]), bf16_val(pe[rows])], -1))
+    v = torch.from_numpy(bf16_val(kv[rows]))
+    o = torch.nn.functional.scaled_dot_product_attention(q[None], kk[None].expand(1, -1, -1),
+                                                         v[None], scale=scale)[0]
+    lse = torch.logsumexp(q @ kk.T * scale, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+def check_mla_sdpa(lib):
+    """Dense (causal) and index-masked attention against torch SDPA over the gathered rows."""
+    rng = np.random.default_rng(31)
+    B, T, H, Dc, Dr, S, k = 2, 2, 3, 8, 4, 20, 6
+    ep = np.array([20, 13], np.int32)
+    qn, qp, kv, pe = _mla_case(rng, B, T, H, Dc, Dr, S)
+    scale = float(np.float32(0.3))
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = ep[b] - T + t + 1
+            ke = min(k - t, n)  # leave some empty slots
+            idx[b, t, :ke] = np.sort(rng.choice(n, size=ke, replace=False))
+    od, lsed = oracle.mla(qn, qp, kv, pe, ep, scale, lib=lib)
+    osp, lsesp = oracle.mla(qn, qp, kv, pe, ep, scale, indices=idx, lib=lib)
+    for b in range(B):
+        for t in range(T):
+            n = ep[b] - T + t + 1
+            o_ref, l_ref = _sdpa(qn[b, t], qp[b, t], kv[b], pe[b], np.arange(n), scale)
+            assert np.allclose(od[b, t], o_ref, rtol=1e-12, atol=1e-12)
+            assert np.allclose(lsed[b, t], l_ref, rtol=1e-12, atol=1e-12)
+            rows = idx[b, t][idx[b, t] >= 0]
+            o_ref, l_ref = _sdpa(qn[b, t], qp[b, t], kv[b], pe[b], rows, scale)
+            assert np.allclose(osp[b, t], o_ref, rtol=1e-12, atol=1e-12)
+            assert np.allclose(lsesp[b, t], l_ref, rtol=1e-12, atol=1e-12)
+
+
+def check_mla_closed_forms(lib):
+    rng = np.random.default_rng(41)
+    B, T, H, Dc, Dr, S, k = 1, 1, 4, 16, 8, 30, 7
+    ep = np.array([30], np.int32)
+    qn, qp, kv, pe = _mla_case(rng, B, T, H, Dc, Dr, S)
+    # one kept row -> that row, exactly
+    one = np.full((1, 1, k), -1, np.int32)
+    one[0, 0, 0] = 17
+    o, lse = oracle.mla(qn, qp, kv, pe, ep, 0.5, indices=one, lib=lib)
+    assert np.array_equal(o[0, 0], np.tile(bf16_val(kv[0, 17]), (H, 1)))
+    # zero query -> mean of kept rows
+    sel = np.sort(rng.choice(30, size=k, replace=False)).astype(np.int32)
+    zq = np.zeros_like(qn)
+    zp = np.zeros_like(qp)
+    o, lse = oracle.mla(zq, zp, kv, pe, ep, 0.5, indices=sel.reshape(1, 1, k), lib=lib)
+    mean = bf16_val(kv[0, sel]).mean(0)
+    assert np.allclose(o[0, 0], np.tile(mean, (H, 1)), rtol=1e-14, atol=1e-15)
+    assert np.allclose(lse[0, 0], np.log(k), rtol=1e-14)
+    # every valid position kept == dense, bit for bit; index order does not matter
+    allk = np.arange(30, dtype=np.int32).reshape(1, 1, 30)
+    od, ld = oracle.mla(qn, qp, kv, pe, ep, 0.5, lib=lib)
+    oa, la = oracle.mla(qn, qp, kv, pe, ep, 0.5, indices=allk, lib=lib)
+    assert np.array_equal(od, oa) and np.array_equal(ld, la)
+    shuffled = np.ascontiguousarray(allk[..., rng.permutation(30)])
+    os_, ls_ = oracle.mla(qn, qp, kv, pe, ep, 0.5, indices=shuffled, lib=lib)
+    assert np.array_equal(os_, oa) and np.array_equal(ls_, la)
+
+
+ALL_CHECKS = [
+    check_indexer_golden, check_fp8_decoding, check_bf16_decoding, check_single_head_matmul,
+    check_fp8_single_head_matmul, check_head_sum_and_linearity, check_topk_bruteforce,
+    check_topk_stable_sort, check_topk_special_cases, check_mla_golden, check_mla_sdpa,
+    check_mla_closed_forms,
+]
