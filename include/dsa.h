@@ -1,0 +1,174 @@
+/*
+ * dsa.h - C ABI of libdsa.so: the DeepSeek Sparse Attention (DSA) decode hot
+ * path on AMD Instinct MI355X (gfx950).
+ *
+ * The path has three stages, each a HIP kernel:
+ *   (a) lightning-indexer scores  I[b,t,s] = scale * sum_h w[b,t,h] *
+ *       ReLU(q[b,t,h,:] . k[b,s,:]) over 64 heads x 128 dims, for the
+ *       causally valid positions (dsa_index_scores);
+ *   (b) per-query selection of the top-k positions by that score
+ *       (dsa_topk);
+ *   (c) absorbed-MLA attention over only the selected cached rows: 128
+ *       heads, 512-wide latent plus 64-wide rope part, softmax, 512-wide
+ *       latent output (dsa_sparse_mla).
+ * dsa_forward runs (a)->(b)->(c) on one stream; dsa_dense_mla is (c) over
+ * every valid position (the dense baseline).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are DEVICE pointers to row-major, contiguous arrays with the
+ *   shapes given below, 16-byte aligned, owned by the caller.  The library
+ *   never allocates, frees or synchronises; every launch is enqueued on
+ *   `stream` (NULL = the null stream) and the pointers must stay valid until
+ *   that work has completed.  Intermediates live in a caller-provided
+ *   workspace whose size the matching *_workspace_size function returns.
+ * - Sequence b holds T new queries; query t sits at position
+ *   end_pos[b] - T + t and may attend to cached positions
+ *   0 .. end_pos[b] - T + t (its causal bound).  end_pos lives on the
+ *   device, so the host cannot check it: the caller guarantees
+ *   T <= end_pos[b] <= max_end_pos <= S_max.  Kernels clamp every position
+ *   to [0, S_max) and never read out of bounds, whatever end_pos holds.
+ * - bf16 is bfloat16; fp8 is OCP FP8 E4M3 ("e4m3fn", max 448), the native
+ *   fp8 of gfx950.
+ * - Every call returns DSA_OK (0) or a negative status.  Arguments are
+ *   validated on the host before anything is launched; on failure nothing
+ *   is enqueued.  DSA_ERR_HIP reports a failed launch (hipGetLastError).
+ *   No global mutable state: calls are re-entrant and thread-safe.
+ *
+ * Sources of the definitions (web pages on DeepSeek-V3.2's sparse
+ * attention): the indexer score and its output shape follow kernelpool's
+ * fix in "mlx-lm PR #512 [WIP] deepseek v32" (ReLU of each head's dot, then
+ * the head weight, then the sum over heads, no head dimension in the
+ * output) and the Indexer.forward excerpt on "DeepSeek-V3.2-Exp - Keep top-k
+ * positions" (fp8_index(q, weights, k_cache, k_scale), causal mask, then
+ * topk(min(index_topk, end_pos))); the attention follows the MQA decode
+ * excerpt on "DeepSeek-V3.2-Exp - Apply sparse mask" (absorbed query,
+ * latent+rope scores times softmax_scale, index mask, softmax, latent-
+ * weighted sum).  Sizes: 64 indexer heads x 128 dims and top-2048 from the
+ * config list of "MaxText PR #2933"; 128 heads x (512+64) from the cost
+ * model in "llama.cpp discussion #17692".
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (identical to the typedef in hip_runtime_api.h). */
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = -1,   /* null pointer, non-positive or inconsistent size */
+  DSA_ERR_UNSUPPORTED = -2,        /* dtype or shape outside the compiled specialisation */
+  DSA_ERR_MISALIGNED = -3,         /* a tensor pointer is not 16-byte aligned */
+  DSA_ERR_WORKSPACE_TOO_SMALL = -4,
+  DSA_ERR_HIP = -5                 /* a kernel launch failed */
+};
+
+typedef enum { DSA_BF16 = 0, DSA_FP8_E4M3 = 1 } dsa_dtype;
+
+/* Fixed sizes of this specialisation. */
+#define DSA_INDEX_HEADS 64
+#define DSA_INDEX_DIM 128
+#define DSA_MLA_HEADS 128
+#define DSA_LATENT_DIM 512
+#define DSA_ROPE_DIM 64
+#define DSA_MAX_TOPK 2048
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* dsa_status_string(int status);
+
+/* (a) Indexer scores - the fp8_index(q, weights, k_cache, k_scale) call of
+ * Indexer.forward ("DeepSeek-V3.2-Exp - Keep top-k positions"), with the
+ * ReLU -> weight -> head-sum order of "mlx-lm PR #512":
+ *   I[b,t,s] = scale * sum_{h<64} w'[b,t,h] * ReLU(q[b,t,h,:] . k[b,s,:]) * ks[b,s]
+ * with w' = w and ks = 1 for bf16, and w' = w*q_scale, ks = k_scale for fp8
+ * (the scales are positive, so this equals the score of the dequantised
+ * values code*scale).
+ *   q        [B,T,64,128] bf16 or fp8 codes
+ *   q_scale  [B,T,64] fp32, one scale per 128-element head block (fp8 only, else NULL)
+ *   weights  [B,T,64] fp32 per-head weights (the caller folds in any
+ *            n_heads^-0.5 / softmax-scale factors)
+ *   k_cache  [B,S_max,128] bf16 or fp8 codes (one shared key per cached token)
+ *   k_scale  [B,S_max] fp32, one scale per key (fp8 only, else NULL)
+ *   end_pos  [B] int32 (device)
+ *   scale    applied once, after the head sum
+ *   index_score [B,T,S_max] fp32 out; entries past each query's causal
+ *            bound are left untouched.
+ * Arithmetic: products on MFMA with fp32 accumulation; ReLU, weighting,
+ * head sum and scaling in fp32.  1 <= T <= max_end_pos <= S_max. */
+int dsa_index_scores(const void* q, const float* q_scale, const float* weights,
+                     const void* k_cache, const float* k_scale, const int32_t* end_pos,
+                     int32_t B, int32_t T, int32_t S_max, int32_t max_end_pos, float scale,
+                     int32_t dtype, float* index_score, hipStream_t stream);
+
+/* (b) Top-k selection - topk(min(index_topk, end_pos)) after the causal mask
+ * in Indexer.forward ("DeepSeek-V3.2-Exp - Keep top-k positions").
+ * For each query row the k_eff = min(k, bound+1) positions with the largest
+ * score are kept; equal scores (IEEE equality, so -0 == +0) go to the
+ * smaller position.  Output: topk_indices [B,T,k] int32 with the kept
+ * positions in ASCENDING order followed by -1 in the k - k_eff empty slots.
+ * Scores must not be NaN (the order of NaN is unspecified).
+ * Integer-only selection (order-preserving 32-bit keys): the result is
+ * exact.  1 <= k <= 2048. */
+size_t dsa_topk_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k);
+int dsa_topk(const float* index_score, const int32_t* end_pos, int32_t B, int32_t T,
+             int32_t S_max, int32_t max_end_pos, int32_t k, int32_t* topk_indices,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* (c) Sparse absorbed-MLA attention - the MQA decode branch of
+ * "DeepSeek-V3.2-Exp - Apply sparse mask", restricted to the selected rows:
+ *   z[h,j] = (q_nope[h,:] . kv[idx_j,:] + q_pe[h,:] . pe[idx_j,:]) * softmax_scale
+ *   p = softmax_j(z),  out[h,:] = sum_j p[h,j] * kv[idx_j,:]
+ * over the valid entries idx_j of the query's index row (entries that are
+ * negative or >= S_max are empty slots and are skipped; valid entries must
+ * be distinct).  The 512-wide latent is both key and value; the query has
+ * already been absorbed into the latent space.
+ *   q_nope   [B,T,128,512] bf16     q_pe     [B,T,128,64] bf16
+ *   kv_cache [B,S_max,512] bf16     pe_cache [B,S_max,64] bf16
+ *   topk_indices [B,T,k] int32 (as produced by dsa_topk)
+ *   out      [B,T,128,512] bf16 (fp32 accumulation, rounded to nearest even)
+ *   lse      [B,T,128] fp32 natural-log sum of exp(z) over the kept rows, or NULL
+ * A row with no valid entry produces out = 0 and lse = -inf.
+ * Arithmetic: both contractions on bf16 MFMA with fp32 accumulation, fp32
+ * online softmax; the probabilities enter the value contraction as bf16. */
+size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t T, int32_t k);
+int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
+                   const void* pe_cache, const int32_t* topk_indices, int32_t B, int32_t T,
+                   int32_t S_max, int32_t k, float softmax_scale, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* (a)+(b)+(c) on one stream: the decode step of "DeepSeek-V3.2-Exp - Apply
+ * sparse mask" with the indexer of "Keep top-k positions".  Arguments are
+ * those of the three calls; index_score and the indices live in the
+ * workspace.  topk_indices_out [B,T,k] receives a copy of the selection if
+ * not NULL.  When every query has at most k valid positions every position
+ * is kept, which equals dense attention (the short-context case). */
+size_t dsa_forward_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k);
+int dsa_forward(const void* q, const float* q_scale, const float* weights, const void* k_cache,
+                const float* k_scale, const int32_t* end_pos, const void* q_nope,
+                const void* q_pe, const void* kv_cache, const void* pe_cache, int32_t B,
+                int32_t T, int32_t S_max, int32_t max_end_pos, int32_t k, float index_scale,
+                float softmax_scale, int32_t dtype, void* out, float* lse,
+                int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Dense baseline: (c) over every causally valid position 0..bound, no index
+ * list (the unmasked form of the same decode branch).  Same tensors and
+ * arithmetic as dsa_sparse_mla.  Used to measure where sparse wins. */
+size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max);
+int dsa_dense_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
+                  const void* pe_cache, const int32_t* end_pos, int32_t B, int32_t T,
+                  int32_t S_max, int32_t max_end_pos, float softmax_scale, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -118,36 +118,35 @@ int oracle_index_scores(const void* q, const float* q_scale, const float* w, con
     if (end_pos[b] < T || end_pos[b] > S_max) return -3;
   if (!rows) n_rows = (int64_t)B * T;
   int status = 0;
+  double* qv = (double*)malloc(sizeof(double) * (size_t)H * D);
 
-#pragma omp parallel for schedule(dynamic, 1)
+  /* Rows one after another; the positions of a row are shared among threads. */
   for (int64_t i = 0; i < n_rows; ++i) {
     int64_t row = row_at(rows, i);
     if (row < 0 || row >= (int64_t)B * T) {
-#pragma omp atomic write
       status = -1;
       continue;
     }
     int b = (int)(row / T), t = (int)(row % T);
     int64_t bound = (int64_t)end_pos[b] - T + t;
-    double* qv = (double*)malloc(sizeof(double) * (size_t)H * D);
     for (int h = 0; h < H; ++h) {
       double qs = dtype == ORACLE_FP8_E4M3 ? (double)q_scale[row * H + h] : 1.0;
       for (int d = 0; d < D; ++d) {
         double v = elem(q, dtype, ((size_t)row * H + h) * D + d) * qs;
-        if (!isfinite(v)) {
-#pragma omp atomic write
-          status = -2;
-        }
+        if (!isfinite(v)) status = -2;
         qv[h * D + d] = v;
       }
     }
+#pragma omp parallel for schedule(static) if (bound >= 4096)
     for (int64_t s = 0; s <= bound; ++s) {
       size_t krow = (size_t)b * S_max + (size_t)s;
       double ks = dtype == ORACLE_FP8_E4M3 ? (double)k_scale[krow] : 1.0;
+      double kvals[D];
+      for (int d = 0; d < D; ++d) kvals[d] = (elem(k, dtype, krow * D + d) * ks);
       double acc = 0.0;
       for (int h = 0; h < H; ++h) {
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += qv[h * D + d] * (elem(k, dtype, krow * D + d) * ks);
+        for (int d = 0; d < D; ++d) dot += qv[h * D + d] * kvals[d];
         double relu = dot > 0.0 ? dot : 0.0;
         acc += (double)w[row * H + h] * relu;
       }
@@ -158,8 +157,8 @@ int oracle_index_scores(const void* q, const float* q_scale, const float* w, con
       float acc32 = (float)acc;
       out[(size_t)row * S_max + (size_t)s] = acc32 * scale;
     }
-    free(qv);
   }
+  free(qv);
   return status;
 }
 

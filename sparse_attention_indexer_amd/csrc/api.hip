@@ -1,0 +1,223 @@
+// C ABI of libdsa.so (declared in include/dsa.h): argument validation on the
+// host, workspace carving, and kernel launches on the caller's stream.  No
+// allocation, no synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa_launch.h"
+
+#define DSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+enum {
+  kOk = 0,
+  kErrInvalid = -1,
+  kErrUnsupported = -2,
+  kErrMisaligned = -3,
+  kErrWorkspace = -4,
+  kErrHip = -5,
+};
+
+constexpr int kMaxTopk = 2048;
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Shared checks of the (B, T, S_max, max_end_pos) geometry.
+int check_geometry(int32_t B, int32_t T, int32_t S_max, int32_t max_end_pos) {
+  if (B < 1 || T < 1 || S_max < 1) return kErrInvalid;
+  if (max_end_pos < T || max_end_pos > S_max) return kErrInvalid;
+  return kOk;
+}
+
+int check_indexer(const void* q, const float* q_scale, const float* w, const void* k_cache,
+                  const float* k_scale, const int32_t* end_pos, int32_t B, int32_t T,
+                  int32_t S_max, int32_t max_end_pos, int32_t dtype) {
+  if (!q || !w || !k_cache || !end_pos) return kErrInvalid;
+  int st = check_geometry(B, T, S_max, max_end_pos);
+  if (st) return st;
+  if (dtype != 0 && dtype != 1) return kErrUnsupported;
+  if (dtype == 1 && (!q_scale || !k_scale)) return kErrInvalid;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w) || !aligned4(end_pos))
+    return kErrMisaligned;
+  if (dtype == 1 && (!aligned16(q_scale) || !aligned4(k_scale))) return kErrMisaligned;
+  return kOk;
+}
+
+int check_topk(const float* scores, const int32_t* end_pos, int32_t B, int32_t T, int32_t S_max,
+               int32_t max_end_pos, int32_t k, const int32_t* out) {
+  if (!scores || !end_pos || !out) return kErrInvalid;
+  int st = check_geometry(B, T, S_max, max_end_pos);
+  if (st) return st;
+  if (k < 1) return kErrInvalid;
+  if (k > kMaxTopk) return kErrUnsupported;
+  if (!aligned4(scores) || !aligned4(end_pos) || !aligned4(out)) return kErrMisaligned;
+  return kOk;
+}
+
+int check_mla_tensors(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
+                      const void* out, const float* lse) {
+  if (!q_nope || !q_pe || !kv || !pe || !out) return kErrInvalid;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv) || !aligned16(pe) ||
+      !aligned16(out) || (lse && !aligned4(lse)))
+    return kErrMisaligned;
+  return kOk;
+}
+
+int check_workspace(const void* ws, size_t have, size_t need) {
+  if (have < need) return kErrWorkspace;
+  if (need > 0 && !ws) return kErrInvalid;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1)) != 0) return kErrMisaligned;
+  return kOk;
+}
+
+size_t sparse_mla_ws(int32_t B, int32_t T, int32_t k) {
+  return dsa::mla_workspace_bytes(B, T, dsa::sparse_mla_plan(B, T, k));
+}
+
+struct ForwardLayout {
+  size_t scores, indices, topk_ws, mla_ws, total;
+};
+
+ForwardLayout forward_layout(int32_t B, int32_t T, int32_t S_max, int32_t k) {
+  ForwardLayout L;
+  const size_t rows = (size_t)B * T;
+  L.scores = 0;
+  L.indices = L.scores + align_up(rows * (size_t)S_max * sizeof(float));
+  L.topk_ws = L.indices + align_up(rows * (size_t)k * sizeof(int32_t));
+  L.mla_ws = L.topk_ws + align_up(dsa::topk_workspace_bytes(B, T, S_max, k));
+  L.total = L.mla_ws + align_up(sparse_mla_ws(B, T, k));
+  return L;
+}
+
+}  // namespace
+
+DSA_EXPORT const char* dsa_status_string(int status) {
+  switch (status) {
+    case kOk: return "DSA_OK: success";
+    case kErrInvalid: return "DSA_ERR_INVALID_ARGUMENT: null pointer or inconsistent size";
+    case kErrUnsupported: return "DSA_ERR_UNSUPPORTED: dtype or shape outside the specialisation";
+    case kErrMisaligned: return "DSA_ERR_MISALIGNED: tensor or workspace pointer misaligned";
+    case kErrWorkspace: return "DSA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than required";
+    case kErrHip: return "DSA_ERR_HIP: kernel launch failed";
+    default: return "unknown dsa status";
+  }
+}
+
+DSA_EXPORT int dsa_index_scores(const void* q, const float* q_scale, const float* weights,
+                                const void* k_cache, const float* k_scale,
+                                const int32_t* end_pos, int32_t B, int32_t T, int32_t S_max,
+                                int32_t max_end_pos, float scale, int32_t dtype,
+                                float* index_score, hipStream_t stream) {
+  int st = check_indexer(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
+                         max_end_pos, dtype);
+  if (st) return st;
+  if (!index_score) return kErrInvalid;
+  if (!aligned4(index_score)) return kErrMisaligned;
+  return dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
+                                  max_end_pos, scale, dtype, index_score, stream);
+}
+
+DSA_EXPORT size_t dsa_topk_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k) {
+  if (B < 1 || T < 1 || S_max < 1 || k < 1) return 0;
+  return dsa::topk_workspace_bytes(B, T, S_max, k);
+}
+
+DSA_EXPORT int dsa_topk(const float* index_score, const int32_t* end_pos, int32_t B, int32_t T,
+                        int32_t S_max, int32_t max_end_pos, int32_t k, int32_t* topk_indices,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_topk(index_score, end_pos, B, T, S_max, max_end_pos, k, topk_indices);
+  if (st) return st;
+  st = check_workspace(workspace, workspace_bytes, dsa::topk_workspace_bytes(B, T, S_max, k));
+  if (st) return st;
+  return dsa::launch_topk(index_score, end_pos, B, T, S_max, max_end_pos, k, topk_indices,
+                          workspace, stream);
+}
+
+DSA_EXPORT size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t T, int32_t k) {
+  if (B < 1 || T < 1 || k < 1) return 0;
+  return sparse_mla_ws(B, T, k);
+}
+
+DSA_EXPORT int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
+                              const void* pe_cache, const int32_t* topk_indices, int32_t B,
+                              int32_t T, int32_t S_max, int32_t k, float softmax_scale,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int st = check_mla_tensors(q_nope, q_pe, kv_cache, pe_cache, out, lse);
+  if (st) return st;
+  if (!topk_indices) return kErrInvalid;
+  if (B < 1 || T < 1 || S_max < 1 || k < 1) return kErrInvalid;
+  if (k > kMaxTopk) return kErrUnsupported;
+  if (!aligned4(topk_indices)) return kErrMisaligned;
+  st = check_workspace(workspace, workspace_bytes, sparse_mla_ws(B, T, k));
+  if (st) return st;
+  return dsa::launch_sparse_mla(q_nope, q_pe, kv_cache, pe_cache, topk_indices, B, T, S_max, k,
+                                softmax_scale, out, lse, workspace, stream);
+}
+
+DSA_EXPORT size_t dsa_forward_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k) {
+  if (B < 1 || T < 1 || S_max < 1 || k < 1) return 0;
+  return forward_layout(B, T, S_max, k).total;
+}
+
+DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* weights,
+                           const void* k_cache, const float* k_scale, const int32_t* end_pos,
+                           const void* q_nope, const void* q_pe, const void* kv_cache,
+                           const void* pe_cache, int32_t B, int32_t T, int32_t S_max,
+                           int32_t max_end_pos, int32_t k, float index_scale,
+                           float softmax_scale, int32_t dtype, void* out, float* lse,
+                           int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  // Validate everything before the first launch.
+  int st = check_indexer(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
+                         max_end_pos, dtype);
+  if (st) return st;
+  st = check_mla_tensors(q_nope, q_pe, kv_cache, pe_cache, out, lse);
+  if (st) return st;
+  if (k < 1) return kErrInvalid;
+  if (k > kMaxTopk) return kErrUnsupported;
+  if (topk_indices_out && !aligned4(topk_indices_out)) return kErrMisaligned;
+  const ForwardLayout L = forward_layout(B, T, S_max, k);
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st) return st;
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* indices =
+      topk_indices_out ? topk_indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
+  st = dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
+                                max_end_pos, index_scale, dtype, scores, stream);
+  if (st) return st;
+  st = dsa::launch_topk(scores, end_pos, B, T, S_max, max_end_pos, k, indices, ws + L.topk_ws,
+                        stream);
+  if (st) return st;
+  return dsa::launch_sparse_mla(q_nope, q_pe, kv_cache, pe_cache, indices, B, T, S_max, k,
+                                softmax_scale, out, lse, ws + L.mla_ws, stream);
+}
+
+DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {
+  if (B < 1 || T < 1 || S_max < 1) return 0;
+  return dsa::mla_workspace_bytes(B, T, dsa::dense_mla_plan(B, T, S_max, S_max));
+}
+
+DSA_EXPORT int dsa_dense_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
+                             const void* pe_cache, const int32_t* end_pos, int32_t B, int32_t T,
+                             int32_t S_max, int32_t max_end_pos, float softmax_scale, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  int st = check_mla_tensors(q_nope, q_pe, kv_cache, pe_cache, out, lse);
+  if (st) return st;
+  if (!end_pos) return kErrInvalid;
+  st = check_geometry(B, T, S_max, max_end_pos);
+  if (st) return st;
+  if (!aligned4(end_pos)) return kErrMisaligned;
+  st = check_workspace(workspace, workspace_bytes,
+                       dsa::mla_workspace_bytes(B, T, dsa::dense_mla_plan(B, T, S_max, S_max)));
+  if (st) return st;
+  return dsa::launch_dense_mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, B, T, S_max,
+                               max_end_pos, softmax_scale, out, lse, workspace, stream);
+}

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of libdsa.
+//
+// MFMA lane layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_16x16x32_bf16: A[m][k] is held by lane m + 16*(k/8), element k%8;
+//     B[k][n] by lane n + 16*(k/8), element k%8; C[m][n] by lane n + 16*(m/4),
+//     element m%4.
+//   v_mfma_f32_16x16x128_f8f6f4 (fp8 e4m3 operands): A row m and B column n sit
+//     in lanes m + 16*g and n + 16*g (g = 0..3), 32 bytes each; a lane's A and
+//     B bytes at the same (g, byte) position are multiplied together, so any
+//     assignment of the 128 dot-product terms to (g, byte) slots works as long
+//     as A and B use the same one.  C as for the bf16 form.
+//   ds_read_tr16_b64 (LDS transposing read): within each group of 16 lanes,
+//     lane i receives element i%4 of the 8-byte rows addressed by lanes
+//     4*j + i/4, j = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const bf16x8& a, const bf16x8& b,
+                                                    const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp8 e4m3 x fp8 e4m3, K = 128, unscaled.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b,
+                                                    const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here; NaN keeps a quiet payload).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map from an fp32 score to an unsigned key: larger score,
+// larger key.  -0 is first turned into +0 so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T xor_shfl(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace dsa

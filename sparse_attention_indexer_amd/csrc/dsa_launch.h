@@ -1,0 +1,37 @@
+// Host-side launchers of the libdsa kernels (one per .hip file).  Arguments
+// are assumed validated by the C ABI layer; each returns 0 or -5 (launch
+// failure) and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+int launch_index_scores(const void* q, const float* q_scale, const float* w, const void* k,
+                        const float* k_scale, const int32_t* end_pos, int B, int T, int S_max,
+                        int max_end_pos, float scale, int dtype, float* out, hipStream_t stream);
+
+size_t topk_workspace_bytes(int B, int T, int S_max, int k);
+int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S_max,
+                int max_end_pos, int k, int32_t* out, void* workspace, hipStream_t stream);
+
+// Split plan of the attention kernel: rows per split and number of splits.
+struct MlaPlan {
+  int rows_per_split;
+  int n_splits;
+};
+MlaPlan sparse_mla_plan(int B, int T, int k);
+MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos);
+size_t mla_workspace_bytes(int B, int T, const MlaPlan& plan);
+
+int launch_sparse_mla(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
+                      const int32_t* idx, int B, int T, int S_max, int k, float softmax_scale,
+                      void* out, float* lse, void* workspace, hipStream_t stream);
+int launch_dense_mla(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
+                     const int32_t* end_pos, int B, int T, int S_max, int max_end_pos,
+                     float softmax_scale, void* out, float* lse, void* workspace,
+                     hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,105 @@
+"""The C ABI on the CPU: exports match the header, validation happens before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_attention_indexer_amd as dsa
+    return dsa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_dense_mla",
+              "dsa_status_string", "dsa_topk_workspace_size", "dsa_sparse_mla_workspace_size",
+              "dsa_forward_workspace_size", "dsa_dense_mla_workspace_size"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in dsa.h but not exported"
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5):
+        s = L.dsa_status_string(st).decode()
+        assert s.startswith("DSA_")
+    assert L.dsa_status_string(-99).decode() == "unknown dsa status"
+
+
+P = ctypes.c_void_p(256)  # an aligned non-null address; never dereferenced on failure paths
+ODD = ctypes.c_void_p(258)
+
+
+def idx_args(**over):
+    a = dict(q=P, q_scale=None, w=P, k=P, k_scale=None, end_pos=P, B=1, T=1, S_max=100,
+             max_end_pos=100, scale=1.0, dtype=0, out=P, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=None), -1), (dict(w=None), -1), (dict(k=None), -1), (dict(end_pos=None), -1),
+    (dict(out=None), -1), (dict(B=0), -1), (dict(T=0), -1), (dict(S_max=0), -1),
+    (dict(max_end_pos=101), -1), (dict(T=5, max_end_pos=4), -1), (dict(dtype=2), -2),
+    (dict(dtype=1), -1), (dict(q=ODD), -3), (dict(k=ODD), -3),
+    (dict(dtype=1, q_scale=P, k_scale=None), -1),
+])
+def test_index_scores_validation(L, over, expect):
+    assert L.dsa_index_scores(*idx_args(**over)) == expect
+
+
+@pytest.mark.parametrize("k,expect", [(0, -1), (2049, -2), (-3, -1)])
+def test_topk_validation(L, k, expect):
+    assert L.dsa_topk(P, P, 1, 1, 100, 100, k, P, None, 0, None) == expect
+
+
+def test_sparse_mla_validation(L):
+    args = [P, P, P, P, P, 1, 1, 100, 2048, 1.0, P, None]
+    need = L.dsa_sparse_mla_workspace_size(1, 1, 2048)
+    assert need > 0  # batch 1 splits the row list
+    assert L.dsa_sparse_mla(*args, P, need - 1, None) == -4
+    assert L.dsa_sparse_mla(*args, None, need, None) == -1
+    assert L.dsa_sparse_mla(*args, ctypes.c_void_p(272), need, None) == -3
+    bad = list(args)
+    bad[0] = ODD
+    assert L.dsa_sparse_mla(*bad, P, need, None) == -3
+    bad = list(args)
+    bad[8] = 4096
+    assert L.dsa_sparse_mla(*bad, P, 1 << 40, None) == -2
+
+
+def test_forward_validation(L):
+    need = L.dsa_forward_workspace_size(2, 1, 1000, 2048)
+    # index_score (2*1000*4 -> 8192 after alignment) + indices (2*2048*4) + attention partials
+    assert need >= 8192 + 16384
+    base = [P, None, P, P, None, P, P, P, P, P, 2, 1, 1000, 1000, 2048, 1.0, 1.0, 0, P, None,
+            None]
+    assert L.dsa_forward(*base, P, need - 1, None) == -4
+    bad = list(base)
+    bad[14] = 4096
+    assert L.dsa_forward(*bad, P, need, None) == -2
+    bad = list(base)
+    bad[6] = None
+    assert L.dsa_forward(*bad, P, need, None) == -1
+
+
+def test_workspace_sizes_monotone(L):
+    a = L.dsa_dense_mla_workspace_size(8, 1, 131072)
+    b = L.dsa_dense_mla_workspace_size(8, 1, 262144)
+    assert b >= a > 0
+    assert L.dsa_topk_workspace_size(1, 1, 32768, 2048) == 0

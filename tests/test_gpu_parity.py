@@ -1,0 +1,382 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same seeded inputs.
+
+Bars:
+* top-k indices: bit-exact (integer work) - on synthetic score rows fed to both
+  sides, and end to end wherever the scores themselves are exact (integer-valued
+  indexer inputs, where every fp32 partial sum is exact);
+* indexer scores: per query row, max |I_gpu - I_ref| / max |I_ref| <= 2e-3 (bf16)
+  or 1e-2 (fp8), I_ref the oracle's score of the same stored inputs;
+* attention output: max |o_gpu - o_ref| <= 2e-2 over all elements (bf16 output);
+  lse within 1e-3 absolute.
+Large workloads are checked on sampled rows the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_indexer_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SCORE_TOL = {"bf16": 2e-3, "fp8": 1e-2}
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_amd as m
+    m.lib()
+    return m
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def np_case(case, rows_b=None):
+    """Host copies (oracle conventions); optionally only the sequences in rows_b."""
+    out = {}
+    for name in ("q", "w", "k_cache", "q_scale", "k_scale", "end_pos", "q_nope", "q_pe",
+                 "kv_cache", "pe_cache"):
+        v = getattr(case, name)
+        if v is None:
+            out[name] = None
+            continue
+        if rows_b is not None:
+            v = v[rows_b]
+        out[name] = inputs.to_numpy(v)
+    return out
+
+
+def oracle_scores(case, h, rows=None):
+    return oracle.index_scores(h["q"], h["w"], h["k_cache"], h["end_pos"], case.scale,
+                               q_scale=h["q_scale"], k_scale=h["k_scale"], rows=rows)
+
+
+def valid_mask(end_pos, T, S_max):
+    ep = np.asarray(end_pos).reshape(-1, 1, 1)
+    t = np.arange(T).reshape(1, -1, 1)
+    s = np.arange(S_max).reshape(1, 1, -1)
+    return s <= ep - T + t
+
+
+def assert_scores_close(gpu, ref, end_pos, T, tol, rows=None):
+    B, _, S = ref.shape
+    m = valid_mask(end_pos, T, S)
+    for b in range(B):
+        for t in range(T):
+            if rows is not None and b * T + t not in rows:
+                continue
+            r = ref[b, t][m[b, t]].astype(np.float64)
+            g = gpu[b, t][m[b, t]].astype(np.float64)
+            denom = max(np.abs(r).max(), 1e-30)
+            err = np.abs(g - r).max() / denom
+            assert err <= tol, f"row ({b},{t}): relative score error {err:.3e} > {tol}"
+
+
+def assert_out_close(out_gpu, lse_gpu, o_ref, lse_ref, rows=None):
+    og = out_gpu.float().cpu().numpy().astype(np.float64)
+    lg = lse_gpu.cpu().numpy().astype(np.float64)
+    B, T = og.shape[:2]
+    for b in range(B):
+        for t in range(T):
+            if rows is not None and b * T + t not in rows:
+                continue
+            err = np.abs(og[b, t] - o_ref[b, t]).max()
+            assert err <= OUT_TOL, f"row ({b},{t}): max |out error| {err:.3e}"
+            lerr = np.abs(lg[b, t] - lse_ref[b, t]).max()
+            assert lerr <= LSE_TOL, f"row ({b},{t}): max |lse error| {lerr:.3e}"
+
+
+def check_topk_invariants(idx, end_pos, T, k):
+    B = idx.shape[0]
+    for b in range(B):
+        for t in range(T):
+            n = int(end_pos[b]) - T + t + 1
+            ke = min(k, n)
+            row = idx[b, t]
+            sel = row[:ke]
+            assert np.all(row[ke:] == -1)
+            assert np.all(sel >= 0) and np.all(sel < n)
+            assert np.all(np.diff(sel) > 0)
+
+
+# --- indexer --------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["base", "dup", "equal", "short", "fp8int"])
+def test_indexer_integer_inputs_exact(variant):
+    m = dsa()
+    banner(f"indexer tiny_decode {variant}")
+    case = inputs.tiny_decode(variant).to(DEV)
+    gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
+                         q_scale=case.q_scale, k_scale=case.k_scale)
+    h = np_case(case)
+    ref = oracle_scores(case, h)
+    msk = valid_mask(h["end_pos"], case.T, case.S_max)
+    g = gpu.cpu().numpy()
+    assert np.array_equal(g[msk], ref[msk])  # -0 == +0 numerically
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_ragged_batch(dtype):
+    """Several sequences, T>1, causal rows, lengths not multiples of any tile."""
+    m = dsa()
+    banner(f"indexer ragged {dtype}")
+    case = inputs.make_case("ragged", 3, 3, [3001, 17, 2050], 3001, dtype=dtype, seed=7,
+                            device=DEV)
+    gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
+                         q_scale=case.q_scale, k_scale=case.k_scale, max_end_pos=3001)
+    h = np_case(case)
+    ref = oracle_scores(case, h)
+    assert_scores_close(gpu.cpu().numpy(), ref, h["end_pos"], case.T, SCORE_TOL[dtype])
+
+
+def test_indexer_integer_prefill_exact():
+    m = dsa()
+    banner("indexer integer prefill T=70 start_pos=200")
+    case = inputs.make_case("prefill_int", 2, 70, [270, 70], 300, index_dist="int", seed=8,
+                            device=DEV)
+    gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale)
+    h = np_case(case)
+    ref = oracle_scores(case, h)
+    msk = valid_mask(h["end_pos"], case.T, case.S_max)
+    assert np.array_equal(gpu.cpu().numpy()[msk], ref[msk])
+
+
+def test_indexer_decode_32k_full_row():
+    m = dsa()
+    banner("indexer decode_32k full row")
+    case = inputs.decode_32k(device=DEV)
+    gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale)
+    h = np_case(case)
+    ref = oracle_scores(case, h)
+    assert_scores_close(gpu.cpu().numpy(), ref, h["end_pos"], 1, SCORE_TOL["bf16"])
+
+
+def test_untouched_past_bound():
+    """Entries past each causal bound are left as they were (poisoned with NaN here)."""
+    m = dsa()
+    banner("indexer poison past bound")
+    case = inputs.make_case("poison", 2, 2, [1000, 37], 1100, seed=9, device=DEV)
+    out = torch.full((2, 2, 1100), float("nan"), device=DEV)
+    m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale, out=out)
+    msk = valid_mask(case.end_pos.cpu().numpy(), 2, 1100)
+    g = out.cpu().numpy()
+    assert not np.isnan(g[msk]).any()
+    assert np.isnan(g[~msk]).all()
+
+
+# --- top-k ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "equal", "zeros", "relu", "wide"])
+@pytest.mark.parametrize("S", [2047, 2048, 2049, 4095, 4097, 32768, 32769, 70001])
+def test_topk_exact(kind, S):
+    m = dsa()
+    banner(f"topk {kind} S={S}")
+    B, T, k = 2, 2, 2048
+    ep = np.array([S, max(2, S // 3)], np.int32)
+    scores = inputs.make_scores(B, T, S, kind=kind, seed=S % 97, device=DEV)
+    end_pos = torch.from_numpy(ep).to(DEV)
+    out = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    m.topk(scores, end_pos, k, max_end_pos=int(ep.max()), out=out)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 1000, 2048])
+def test_topk_small_k_and_causal_rows(k):
+    m = dsa()
+    banner(f"topk causal rows k={k}")
+    B, T, S = 2, 40, 3000
+    ep = np.array([3000, 1500], np.int32)
+    scores = inputs.make_scores(B, T, S, kind="ties", seed=k, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=3000)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_topk_longest_rows():
+    m = dsa()
+    banner("topk 131072-long rows")
+    B, T, S, k = 3, 1, 131072, 2048
+    ep = np.array([131072, 100000, 8192], np.int32)
+    scores = inputs.make_scores(B, T, S, kind="normal", seed=3, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+# --- attention --------------------------------------------------------------------
+
+def _mla_inputs(B, T, S, ep, seed):
+    case = inputs.make_case("mla", B, T, ep, S, seed=seed, device=DEV)
+    return case
+
+
+@pytest.mark.parametrize("fill", ["random", "first", "last"])
+def test_sparse_mla_vs_oracle(fill):
+    m = dsa()
+    banner(f"sparse_mla fill={fill}")
+    B, T, S, k = 2, 2, 5000, 2048
+    ep = [5000, 1500]  # second sequence has fewer than k valid positions
+    case = _mla_inputs(B, T, S, ep, 11)
+    idx = inputs.make_indices(B, T, ep, k, seed=5, fill=fill, device=DEV)
+    out, lse = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, idx,
+                            case.softmax_scale)
+    h = np_case(case)
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, indices=idx.cpu().numpy())
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("k", [1, 33, 100, 257])
+def test_sparse_mla_ragged_k(k):
+    m = dsa()
+    banner(f"sparse_mla k={k}")
+    B, T, S = 1, 3, 700
+    case = _mla_inputs(B, T, S, [700], 12)
+    idx = inputs.make_indices(B, T, [700], k, seed=k, device=DEV)
+    out, lse = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, idx,
+                            case.softmax_scale)
+    h = np_case(case)
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, indices=idx.cpu().numpy())
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_sparse_mla_single_row_and_empty():
+    """One kept row returns that row exactly; a row with no entry gives 0 and lse=-inf."""
+    m = dsa()
+    banner("sparse_mla single row / empty")
+    B, T, S, k = 1, 2, 300, 64
+    case = _mla_inputs(B, T, S, [300], 13)
+    idx = torch.full((B, T, k), -1, dtype=torch.int32)
+    idx[0, 0, 0] = 123
+    idx = idx.to(DEV)
+    out, lse = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, idx,
+                            case.softmax_scale)
+    row = case.kv_cache[0, 123].float()
+    assert torch.equal(out[0, 0].float(), row.expand(128, -1))
+    assert torch.equal(out[0, 1].float(), torch.zeros(128, 512, device=DEV))
+    assert torch.isinf(lse[0, 1]).all() and (lse[0, 1] < 0).all()
+
+
+@pytest.mark.parametrize("S,ep", [(3000, [3000, 1200]), (20000, [20000, 9000])])
+def test_dense_mla_vs_oracle(S, ep):
+    m = dsa()
+    banner(f"dense_mla S={S}")
+    B, T = 2, 1
+    case = _mla_inputs(B, T, S, ep, 14)
+    out, lse = m.dense_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, case.end_pos,
+                           case.softmax_scale, max_end_pos=max(ep))
+    h = np_case(case)
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+# --- whole path ----------------------------------------------------------------------
+
+def _forward_and_oracle(case, rows=None, rows_b=None):
+    """Run dsa_forward; oracle scores -> oracle top-k -> oracle attention on the same inputs."""
+    m = dsa()
+    B, T, k = case.B, case.T, case.topk
+    topk_out = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    out, lse, _ = m.forward_case(case, topk_out=topk_out)
+    torch.cuda.synchronize()
+    h = np_case(case)
+    ref_s = oracle_scores(case, h, rows=rows)
+    ref_idx = oracle.topk(np.nan_to_num(ref_s, nan=0.0), h["end_pos"], k, rows=rows)
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, indices=ref_idx, rows=rows)
+    return out, lse, topk_out.cpu().numpy(), ref_s, ref_idx, o_ref, lse_ref, h
+
+
+@pytest.mark.parametrize("variant", ["base", "dup", "equal", "short", "fp8int"])
+def test_forward_tiny_exact_indices(variant):
+    banner(f"forward tiny_decode {variant}")
+    case = inputs.tiny_decode(variant).to(DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    assert np.array_equal(idx, ref_idx)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_forward_prefill_integer_exact():
+    banner("forward integer prefill B=2 T=96")
+    case = inputs.make_case("prefill_int", 2, 96, [2500, 96], 2500, index_dist="int", seed=15,
+                            device=DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    assert np.array_equal(idx, ref_idx)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_forward_decode_32k_integer_exact():
+    """The 32K decode shape with integer-valued indexer inputs: indices exact end to end."""
+    banner("forward decode 32k integer")
+    case = inputs.make_case("d32k_int", 1, 1, [32768], 32768, index_dist="int", seed=16,
+                            device=DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    assert np.array_equal(idx, ref_idx)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_forward_decode_32k_normal():
+    """The 32K bf16 decode workload: scores within tolerance, selection valid against the
+    oracle's scores up to that tolerance, output within tolerance of the oracle's path."""
+    banner("forward decode_32k normal")
+    case = inputs.decode_32k(device=DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    check_topk_invariants(idx, h["end_pos"], 1, case.topk)
+    r = ref_s[0, 0].astype(np.float64)
+    sel = np.zeros(r.size, bool)
+    sel[idx[0, 0][idx[0, 0] >= 0]] = True
+    slack = SCORE_TOL["bf16"] * np.abs(r).max()
+    assert r[sel].min() >= r[~sel].max() - slack
+    overlap = np.intersect1d(idx[0, 0], ref_idx[0, 0]).size / case.topk
+    assert overlap >= 0.98, overlap
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_forward_b64_varlen_fp8_sampled():
+    """The batch-64 fp8 workload at full size; the oracle checks sampled sequences."""
+    banner("forward decode_b64_varlen fp8 (sampled)")
+    m = dsa()
+    case = inputs.decode_b64_varlen(device=DEV)
+    B, k = case.B, case.topk
+    topk_out = torch.full((B, 1, k), -7, dtype=torch.int32, device=DEV)
+    out, lse, _ = m.forward_case(case, topk_out=topk_out)
+    torch.cuda.synchronize()
+    idx = topk_out.cpu().numpy()
+    check_topk_invariants(idx, case.end_pos.cpu().numpy(), 1, k)
+    for b in (0, 37):
+        sub = slice(b, b + 1)
+        h = np_case(case, rows_b=sub)
+        ref_s = oracle.index_scores(h["q"], h["w"], h["k_cache"], h["end_pos"], case.scale,
+                                    q_scale=h["q_scale"], k_scale=h["k_scale"])
+        gs = m.index_scores(case.q[sub], case.w[sub], case.k_cache[sub], case.end_pos[sub],
+                            case.scale, q_scale=case.q_scale[sub], k_scale=case.k_scale[sub])
+        assert_scores_close(gs.cpu().numpy(), ref_s, h["end_pos"], 1, SCORE_TOL["fp8"])
+        ref_idx = oracle.topk(np.nan_to_num(ref_s, nan=0.0), h["end_pos"], k)
+        r = ref_s[0, 0][: int(h["end_pos"][0])].astype(np.float64)
+        sel = np.zeros(r.size, bool)
+        sel[idx[b, 0]] = True
+        assert r[sel].min() >= r[~sel].max() - SCORE_TOL["fp8"] * np.abs(r).max()
+        o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                    h["end_pos"], case.softmax_scale, indices=ref_idx)
+        assert_out_close(out[sub], lse[sub], o_ref, lse_ref)
+
+
+def test_forward_deterministic():
+    m = dsa()
+    banner("forward determinism")
+    case = inputs.make_case("det", 4, 1, [9000, 4000, 2048, 12000], 12000, dtype="fp8",
+                            seed=17, device=DEV)
+    r1 = m.forward_case(case, topk_out=torch.empty((4, 1, 2048), dtype=torch.int32, device=DEV))
+    r2 = m.forward_case(case, topk_out=torch.empty((4, 1, 2048), dtype=torch.int32, device=DEV))
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])

@@ -25,7 +25,7 @@ MUTANTS = [
      "acc = (double)w[row * H + h] * relu;"),
     ("weights_dropped", "acc += (double)w[row * H + h] * relu;", "acc += relu;"),
     ("wrong_head_of_q", "qv[h * D + d] = v;", "qv[h * D + d] = elem(q, dtype, (size_t)row * H * D + d) * qs;"),
-    ("k_scale_dropped", "(elem(k, dtype, krow * D + d) * ks)", "elem(k, dtype, krow * D + d)"),
+    ("k_scale_dropped", "kvals[d] = (elem(k, dtype, krow * D + d) * ks);", "kvals[d] = elem(k, dtype, krow * D + d);"),
     ("q_scale_dropped", "double qs = dtype == ORACLE_FP8_E4M3 ? (double)q_scale[row * H + h] : 1.0;",
      "double qs = 1.0;"),
     ("scale_dropped", "out[(size_t)row * S_max + (size_t)s] = acc32 * scale;",
