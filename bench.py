@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA decode hot path on one MI355X.
+
+A step is one dsa_forward call (lightning indexer -> top-2048 -> sparse
+absorbed MLA) over one batch of synthetic inputs already resident in HBM.
+The headline workload is batch-1 decode at 32768 cached tokens in bf16
+(64x128 indexer, 128-head 512+64 MLA).  Inputs are rotated over enough
+copies (>= 1 GiB in total) that every step reads its caches from HBM rather
+than from the 256 MB last-level cache.
+
+Printed: one JSON line with the throughput (query tokens/s), a roofline
+entry for the dominant kernel (algorithmic bytes per launch / average launch
+time, from HIP events on the launch stream), the CPU oracle timed on a
+bounded sample of the same workload, and the measured sparse-vs-dense
+break-even context of the batch-8 fp8 sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+METRIC = "sparse-attn decode query-tok/s at 32K ctx; % HBM roofline; dense break-even"
+ROTATION_BYTES = 1 << 30
+
+# Algorithmic bytes (compulsory input reads + output writes; intermediates excluded).
+def indexer_bytes(n_keys_total, rows, fp8):
+    per_key = 132 if fp8 else 256            # 128-dim key (+ fp32 scale for fp8)
+    per_row = (8192 + 256 + 256) if fp8 else (16384 + 256)  # q (+ q_scale) + weights
+    return per_key * n_keys_total + per_row * rows
+
+
+def sparse_mla_bytes(n_selected_total, rows):
+    # gathered 512+64 bf16 rows, q_nope+q_pe (147456 B), bf16 output (131072 B)
+    return 1152 * n_selected_total + (147456 + 131072) * rows
+
+
+def dense_mla_bytes(n_keys_total, rows):
+    return 1152 * n_keys_total + (147456 + 131072) * rows
+
+
+def topk_bytes(n_keys_total, rows, k):
+    return 4 * n_keys_total + 4 * k * rows
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_indexer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_file, digest):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, reps):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        s.record()
+        for i in range(reps):
+            fn(i)
+        e.record()
+        t.cuda.synchronize()
+        return s.elapsed_time(e) / reps  # ms
+
+
+def case_bytes(case):
+    tot = 0
+    for name in ("q", "w", "k_cache", "q_scale", "k_scale", "q_nope", "q_pe", "kv_cache",
+                 "pe_cache"):
+        v = getattr(case, name)
+        if v is not None:
+            tot += v.numel() * v.element_size()
+    return tot
+
+
+def clone_case(case):
+    from dataclasses import fields
+    from sparse_attention_indexer_amd.inputs import Case
+    kw = {}
+    for f in fields(case):
+        v = getattr(case, f.name)
+        kw[f.name] = v.clone() if hasattr(v, "clone") else v
+    return Case(**kw)
+
+
+def rotation(case, limit=64):
+    n = max(1, min(limit, math.ceil(ROTATION_BYTES / max(1, case_bytes(case)))))
+    return [case] + [clone_case(case) for _ in range(n - 1)]
+
+
+def bench_workload(dsa, torch, case, steps, warmup, per_kernel=True):
+    """Time dsa_forward (and, separately, each stage) over rotated input copies."""
+    copies = rotation(case)
+    B, T, S, k = case.B, case.T, case.S_max, case.topk
+    dev = case.q.device
+    mep = case.max_end_pos
+    ws = torch.empty(dsa.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, T, S), dtype=torch.float32, device=dev)
+
+    def step(i):
+        c = copies[i % len(copies)]
+        dsa.forward(c.q, c.w, c.k_cache, c.end_pos, c.q_nope, c.q_pe, c.kv_cache, c.pe_cache,
+                    c.scale, c.softmax_scale, k=k, q_scale=c.q_scale, k_scale=c.k_scale,
+                    max_end_pos=mep, out=out, lse=lse, topk_out=idx, workspace=ws)
+
+    timer = Timer(torch)
+    for i in range(warmup):
+        step(i)
+    ms = timer.time(step, steps)
+    res = {"ms_per_step": ms, "copies": len(copies)}
+    if not per_kernel:
+        return res
+
+    def st_index(i):
+        c = copies[i % len(copies)]
+        dsa.index_scores(c.q, c.w, c.k_cache, c.end_pos, c.scale, q_scale=c.q_scale,
+                         k_scale=c.k_scale, max_end_pos=mep, out=scores)
+
+    def st_topk(i):
+        dsa.topk(scores, copies[i % len(copies)].end_pos, k, max_end_pos=mep, out=idx)
+
+    mla_ws = torch.empty(max(1, dsa.lib().dsa_sparse_mla_workspace_size(B, T, k)),
+                         dtype=torch.uint8, device=dev)
+
+    def st_mla(i):
+        c = copies[i % len(copies)]
+        dsa.sparse_mla(c.q_nope, c.q_pe, c.kv_cache, c.pe_cache, idx, c.softmax_scale, out=out,
+                       lse=lse, workspace=mla_ws)
+
+    reps = max(steps, 20)
+    for fn in (st_index, st_topk, st_mla):
+        fn(0)
+    res["stage_ms"] = {"index_scores": timer.time(st_index, reps), "topk": timer.time(st_topk, reps),
+                       "sparse_mla": timer.time(st_mla, reps)}
+    return res
+
+
+def bench_dense(dsa, torch, case, steps, warmup):
+    copies = rotation(case)
+    B, T, S = case.B, case.T, case.S_max
+    dev = case.q.device
+    mep = case.max_end_pos
+    ws = torch.empty(max(1, dsa.lib().dsa_dense_mla_workspace_size(B, T, S)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
+
+    def step(i):
+        c = copies[i % len(copies)]
+        dsa.dense_mla(c.q_nope, c.q_pe, c.kv_cache, c.pe_cache, c.end_pos, c.softmax_scale,
+                      max_end_pos=mep, out=out, lse=lse, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    return Timer(torch).time(step, steps)
+
+
+def break_even(contexts, sparse_ms, dense_ms):
+    """Context where sparse and dense times cross (log-linear interpolation), or None."""
+    diff = [s - d for s, d in zip(sparse_ms, dense_ms)]
+    for i in range(1, len(contexts)):
+        if diff[i - 1] > 0 >= diff[i]:
+            x0, x1 = math.log(contexts[i - 1]), math.log(contexts[i])
+            f = diff[i - 1] / (diff[i - 1] - diff[i])
+            return round(math.exp(x0 + f * (x1 - x0)))
+    if diff and diff[0] <= 0:
+        return contexts[0]
+    return None
+
+
+def cpu_baseline(case, budget_s=15.0):
+    """The CPU oracle (as it stands) on a bounded sample: whole decode steps of the workload."""
+    import numpy as np
+
+    import oracle
+    from sparse_attention_indexer_amd import inputs
+    h = {k: (None if v is None else inputs.to_numpy(v)) for k, v in
+         [(n, getattr(case, n)) for n in ("q", "w", "k_cache", "q_scale", "k_scale", "end_pos",
+                                           "q_nope", "q_pe", "kv_cache", "pe_cache")]}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        s = oracle.index_scores(h["q"], h["w"], h["k_cache"], h["end_pos"], case.scale,
+                                q_scale=h["q_scale"], k_scale=h["k_scale"])
+        idx = oracle.topk(np.nan_to_num(s, nan=0.0), h["end_pos"], case.topk)
+        oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"], h["end_pos"],
+                   case.softmax_scale, indices=idx)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 2000:
+            break
+    q_tok = reps * case.B * case.T
+    return {"value": q_tok / el, "unit": "query-tok/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} whole decode step(s) of {case.name} (B={case.B}, T={case.T}, "
+                      f"n={case.max_end_pos}): fp64 indexer over every key, full-sort top-"
+                      f"{case.topk}, masked-softmax MLA over 128 heads; {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sparse-vs-dense sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--detail", default=None, help="also write per-config details (JSON) here")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_attention_indexer_amd as dsa
+    from sparse_attention_indexer_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dsa.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    # --- headline: batch-1 decode at 32K, bf16 ---
+    case = inputs.decode_32k(device=dev)
+    r = bench_workload(dsa, torch, case, args.steps, args.warmup)
+    B, T, n, k = case.B, case.T, case.max_end_pos, case.topk
+    ms = r["ms_per_step"]
+    value = B * T / (ms * 1e-3)
+    st = r["stage_ms"]
+    kbytes = {"index_scores": indexer_bytes(n * B, B * T, False),
+              "topk": topk_bytes(n * B, B * T, k),
+              "sparse_mla": sparse_mla_bytes(min(n, k) * B * T, B * T)}
+    dom = max(st, key=st.get)
+    achieved = kbytes[dom] / (st[dom] * 1e-3) / 1e9
+    digest_files = {"index_scores": ["indexer.hip"], "topk": ["topk.hip"],
+                    "sparse_mla": ["mla.hip"]}[dom]
+    traffic = read_traffic(f"{dom}_decode_32k_bf16.pmc.txt", source_digest(digest_files))
+    step_bytes = sum(kbytes[s] for s in ("index_scores", "sparse_mla"))
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_32k_bf16", "batch": B, "queries_per_seq": T,
+                   "context": n, "topk": k, "index_heads": 64, "index_dim": 128,
+                   "mla_heads": 128, "latent": 512, "rope": 64, "input_copies": r["copies"]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": kbytes[dom],
+                     "avg_launch_ms": round(st[dom], 5)},
+        "stage_ms": {s: round(v, 5) for s, v in st.items()},
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    detail = {"headline": r}
+
+    # --- sparse vs dense over context (batch 8, fp8 indexer) ---
+    if not args.no_sweep:
+        ctxs, sp, de = [], [], []
+        for c in inputs.SWEEP_CONTEXTS:
+            sc = inputs.sweep(c, device=dev)
+            rs = bench_workload(dsa, torch, sc, max(20, args.steps // 4), 5, per_kernel=False)
+            dm = bench_dense(dsa, torch, sc, max(20, args.steps // 4), 5)
+            ctxs.append(c)
+            sp.append(rs["ms_per_step"])
+            de.append(dm)
+            del sc
+            torch.cuda.empty_cache()
+        line["dense_break_even"] = {"context": break_even(ctxs, sp, de),
+                                    "workload": "sweep_b8_fp8", "contexts": ctxs,
+                                    "sparse_ms": [round(x, 5) for x in sp],
+                                    "dense_ms": [round(x, 5) for x in de]}
+        detail["sweep"] = line["dense_break_even"]
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case.to("cpu"), args.cpu_budget)
+
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(detail, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
