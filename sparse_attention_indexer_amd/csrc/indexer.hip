@@ -8,10 +8,11 @@
 //
 // Mapping: the 64 heads are the M dimension of 16x16 MFMA tiles (4 M-tiles),
 // 16 cached keys are the N dimension, and the 128-dim dot is the K dimension.
-// Each wave keeps its query's 64x128 fragment in registers for its whole key
-// range and streams keys straight from HBM into B-operand registers: a lane
-// reads 64 contiguous bytes (bf16) or 32 (fp8) of one key row, 4 lanes cover a
-// row, so every byte fetched is used once.  In the result tile a lane holds 4
+// A workgroup stages its query (64x128) in LDS once; each wave then keeps the
+// A fragments in registers for its whole key range and streams keys straight
+// from HBM into B-operand registers, one tile ahead of the math: a lane reads
+// 64 contiguous bytes (bf16) or 32 (fp8) of one key row, 4 lanes cover a row,
+// so every byte fetched is used once.  In the result tile a lane holds 4
 // heads of one key; ReLU, weighting and the sum over its 16 head values happen
 // in registers, and two cross-lane adds finish the sum over 64 heads.
 #include "dsa_device.h"
@@ -24,12 +25,39 @@ constexpr int kIdxDim = 128;
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTile = 16;
 
+#ifndef DSA_IDX_TARGET_BLOCKS
+#define DSA_IDX_TARGET_BLOCKS 2048
+#endif
+
+// Key fragment of one 16-key tile for this lane: 64 bytes (bf16) or 32 (fp8)
+// of key s, starting at dim 32*g.
+template <bool kFp8>
+struct KeyFrag {
+  uint4 v[kFp8 ? 2 : 4];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ KeyFrag<kFp8> load_key_frag(const uint8_t* kbase, int s, int g) {
+  KeyFrag<kFp8> f;
+  constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
+  const uint8_t* p = kbase + (size_t)s * kRowBytes + g * (kRowBytes / 4);
+#pragma unroll
+  for (int u = 0; u < (kFp8 ? 2 : 4); ++u) f.v[u] = ldg16(p + 16 * u);
+  return f;
+}
+
 template <bool kFp8>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ end_pos, int T, int S_max, float scale, int blocks_per_row,
     int tiles_per_wave, float* __restrict__ out) {
+  // The block's 64x128 query in LDS, rows padded by 16 bytes so the 16 rows a
+  // fragment read touches start on different banks.
+  constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
+  constexpr int kQPitch = kRowBytes + 16;
+  __shared__ __align__(16) uint8_t s_q[kIdxHeads * kQPitch];
+
   const int row = blockIdx.x / blocks_per_row;
   const int blk = blockIdx.x - row * blocks_per_row;
   const int b = row / T, t = row - b * T;
@@ -43,6 +71,22 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;     // lane group: which 32 of the 128 dims this lane carries
   const int r16 = lane & 15;   // head within an M-tile (A) / key within a tile (B)
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + (size_t)b * S_max * kRowBytes;
+  auto tile_start = [&](int tile) { return blk_start + (tile * kIdxWaves + wave) * kIdxTile; };
+
+  // First key tile in flight before anything else.
+  KeyFrag<kFp8> cur = load_key_frag<kFp8>(kbase, min(tile_start(0) + r16, bound), g);
+
+  // Query -> LDS: thread tid copies a quarter of head tid/4.
+  {
+    const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(q) +
+                         ((size_t)row * kIdxHeads + h) * kRowBytes + part * (kRowBytes / 4);
+    uint8_t* dst = s_q + h * kQPitch + part * (kRowBytes / 4);
+#pragma unroll
+    for (int u = 0; u < kRowBytes / 64; ++u)
+      *reinterpret_cast<uint4*>(dst + 16 * u) = ldg16(src + 16 * u);
+  }
 
   // Per-lane weights for the 16 heads whose results this lane will hold:
   // head = mt*16 + 4*g + i for M-tile mt and result element i.
@@ -56,28 +100,30 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       if constexpr (kFp8) wh *= q_scale[(size_t)row * kIdxHeads + h];
       wv[mt][i] = wh;
     }
+  __syncthreads();
+
+  // A fragments: head mt*16 + r16, bytes [g*R/4, (g+1)*R/4) of its row.
+  uint4 qa[4][kFp8 ? 2 : 4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int u = 0; u < (kFp8 ? 2 : 4); ++u)
+      qa[mt][u] = *reinterpret_cast<const uint4*>(s_q + (mt * 16 + r16) * kQPitch +
+                                                  g * (kRowBytes / 4) + 16 * u);
 
   float* orow = out + (size_t)row * S_max;
+  const float* ksrow = kFp8 ? k_scale + (size_t)b * S_max : nullptr;
 
-  if constexpr (!kFp8) {
-    // A fragments: head mt*16 + r16, dims g*32 + kk*8 .. +7 for K-step kk.
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(q) + (size_t)row * kIdxHeads * kIdxDim;
-    uint4 qa[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qa[mt][kk] = ldg16(qrow + (mt * 16 + r16) * kIdxDim + g * 32 + kk * 8);
-    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(k) + (size_t)b * S_max * kIdxDim;
+  for (int tile = 0; tile < tiles_per_wave; ++tile) {
+    const int s0 = tile_start(tile);
+    if (s0 > bound) break;
+    const int s0n = tile_start(tile + 1);
+    const bool has_next = tile + 1 < tiles_per_wave && s0n <= bound;
+    KeyFrag<kFp8> nxt;
+    if (has_next) nxt = load_key_frag<kFp8>(kbase, min(s0n + r16, bound), g);
 
-    for (int tile = 0; tile < tiles_per_wave; ++tile) {
-      const int s0 = blk_start + (tile * kIdxWaves + wave) * kIdxTile;
-      if (s0 > bound) break;
-      const int s = min(s0 + r16, bound);
-      const uint16_t* kp = kbase + (size_t)s * kIdxDim + g * 32;
-      uint4 kb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kb[kk] = ldg16(kp + kk * 8);
+    float v = 0.f;
+    if constexpr (!kFp8) {
       f32x4 acc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -85,50 +131,32 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt] = mfma_bf16_16x16x32(as_bf16x8(qa[mt][kk]), as_bf16x8(kb[kk]), acc[mt]);
-      float v = 0.f;
+          acc[mt] = mfma_bf16_16x16x32(as_bf16x8(qa[mt][kk]), as_bf16x8(cur.v[kk]), acc[mt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[mt][i], 0.f);
-      v += xor_shfl(v, 16);
-      v += xor_shfl(v, 32);
-      if (g == 0 && s0 + r16 <= bound) orow[s0 + r16] = v * scale;
-    }
-  } else {
-    // A fragments: head mt*16 + r16, the 32 bytes g*32 .. g*32+31 of its 128 codes.
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q) + (size_t)row * kIdxHeads * kIdxDim;
-    i32x8 qa[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint8_t* p = qrow + (mt * 16 + r16) * kIdxDim + g * 32;
-      const uint4 lo = ldg16(p), hi = ldg16(p + 16);
-      qa[mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + (size_t)b * S_max * kIdxDim;
-    const float* ksrow = k_scale + (size_t)b * S_max;
-
-    for (int tile = 0; tile < tiles_per_wave; ++tile) {
-      const int s0 = blk_start + (tile * kIdxWaves + wave) * kIdxTile;
-      if (s0 > bound) break;
-      const int s = min(s0 + r16, bound);
-      const uint8_t* kp = kbase + (size_t)s * kIdxDim + g * 32;
-      const uint4 lo = ldg16(kp), hi = ldg16(kp + 16);
-      const i32x8 kb = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const float ks = ksrow[s];
-      float v = 0.f;
+    } else {
+      const i32x8 kb = i32x8{(int)cur.v[0].x, (int)cur.v[0].y, (int)cur.v[0].z, (int)cur.v[0].w,
+                             (int)cur.v[1].x, (int)cur.v[1].y, (int)cur.v[1].z, (int)cur.v[1].w};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 acc = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const i32x8 a = i32x8{(int)qa[mt][0].x, (int)qa[mt][0].y, (int)qa[mt][0].z,
+                              (int)qa[mt][0].w, (int)qa[mt][1].x, (int)qa[mt][1].y,
+                              (int)qa[mt][1].z, (int)qa[mt][1].w};
+        const f32x4 acc = mfma_fp8_16x16x128(a, kb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
       }
-      v += xor_shfl(v, 16);
-      v += xor_shfl(v, 32);
-      if (g == 0 && s0 + r16 <= bound) orow[s0 + r16] = (v * ks) * scale;
     }
+    v += xor_shfl(v, 16);
+    v += xor_shfl(v, 32);
+    const int s = s0 + r16;
+    if (g == 0 && s <= bound) {
+      if constexpr (kFp8) v *= ksrow[s];
+      orow[s] = v * scale;
+    }
+    if (has_next) cur = nxt;
   }
 }
 
@@ -139,7 +167,7 @@ int launch_index_scores(const void* q, const float* q_scale, const float* w, con
   const long tiles_per_row = (max_end_pos + kIdxTile - 1) / kIdxTile;
   // Enough blocks to cover all 256 CUs several times over, but at least one
   // 16-key tile per wave and at most 16.
-  long tpw = rows * tiles_per_row / (2048L * kIdxWaves);
+  long tpw = rows * tiles_per_row / ((long)DSA_IDX_TARGET_BLOCKS * kIdxWaves);
   tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
   const int keys_per_block = (int)(kIdxWaves * tpw * kIdxTile);
   const int blocks_per_row = (max_end_pos + keys_per_block - 1) / keys_per_block;

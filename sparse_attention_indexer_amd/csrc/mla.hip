@@ -5,24 +5,36 @@
 //   z[h,j] = (q_nope[h,:] . kv[pos_j,:] + q_pe[h,:] . pe[pos_j,:]) * softmax_scale
 //   out[h,:] = sum_j softmax_j(z[h,:]) * kv[pos_j,:]
 //
-// Work item: one query row, one group of 64 heads, one split of its row list.
-// A 256-thread workgroup (4 waves, 16 heads each) walks the split 32 rows at a
-// time.  Each tile of 32 gathered rows (512 latent + 64 rope bf16 = 1152 B a
-// row) is staged in LDS once and read by all four waves twice:
-//   - scores: 16 heads x 32 rows, K = 576, on 16x16x32 bf16 MFMA, the query
-//     fragment held in registers for the whole split;
-//   - values: 16 heads x 512 latent dims, K = 32 rows, the row-major tile read
-//     back transposed with ds_read_tr16_b64 so the same LDS copy serves both.
-// The softmax is online (running max and sum per head, in base 2), the
-// probabilities go through LDS as bf16 to become the A operand of the value
-// contraction, and the 16x512 fp32 accumulator stays in registers.  The next
-// tile's global loads are issued before the current tile is computed.
-// With several splits per row, unnormalised partial outputs plus (max, sum)
-// go to the workspace and a combine kernel merges them.
+// Work item: one query row and one split of its row list, all 128 heads.  A
+// 512-thread workgroup has 8 waves of 16 heads (two waves per SIMD, so one
+// wave's LDS reads overlap the other's MFMAs); it walks its split 64 rows at a
+// time, so every gathered row is read from HBM once for all heads.
 //
-// Head groups of the same (row, split) are given block ids that fall on the
-// same XCD (ids are dealt round-robin over the 8 XCDs), so the second group
-// finds the gathered rows in that XCD's L2.
+// Gathers.  Rows are copied from HBM straight into LDS (global_load_lds, 16
+// bytes a lane, no register staging) into a 2-slot ring, so the next tile is
+// in flight while one is computed.  A 512-wide latent row (1 KiB) is one
+// instruction; the 64-wide rope part of 8 rows is another, with its 16-byte
+// chunks XOR-swizzled by row so the score reads do not collide on banks.  The
+// split's row positions are first staged in LDS.  Barriers are plain
+// s_barrier with explicit waits (vmcnt for this wave's copies, lgkmcnt for LDS
+// writes), so the copies for the next tile stay in flight across them.
+//
+// Math, transposed so that each lane owns one head.  Scores are computed as
+// S^T[row][head] = KV[row] . Q[head] (16x16x32 bf16 MFMA, rows as M, the
+// wave's 16 heads as N, K = 576): the lane holding head h gets 16 of the
+// tile's 64 rows.  The online softmax state (running max, partial sum) is
+// therefore per lane; the max over rows needs only two cross-lane swaps
+// (v_permlane32_swap / v_permlane16_swap).  The probabilities stay in
+// registers: the rows a lane holds become the B operand of the value
+// contraction O^T[c][head] += V^T[c][rows] . P[rows][head], whose A operand is
+// read from the row-major LDS tile with ds_read_tr16_b64 (the same K order,
+// rows 16s+4g..16s+4g+3 for lane group g, is used on both sides).  O^T has
+// the head in the lane too, so rescaling by exp2(m_old - m_new) is one
+// multiply per accumulator; it is done lazily, only when a tile's max exceeds
+// the running reference by more than 2^8 (probabilities stay below 256).  The
+// 16x512 fp32 accumulator lives in registers.  With several splits per row,
+// unnormalised partial outputs plus (max, sum) go to the workspace and a
+// combine kernel merges them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -31,34 +43,71 @@ namespace dsa {
 constexpr int kHeads = 128;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kDqk = kDc + kDr;
-constexpr int kHpb = 64;            // heads per workgroup
-constexpr int kRt = 32;             // gathered rows per tile
-constexpr int kKvPitch = kDqk + 8;  // bf16 per LDS row (1168 B): spreads rows over banks
-constexpr int kPPitch = kRt + 8;    // bf16 per probability row (80 B)
+constexpr int kWaves = 8;                    // 16 heads each
+constexpr int kThreads = kWaves * 64;
+constexpr int kRt = 64;                      // gathered rows per tile
+constexpr int kNbuf = 2;                     // tiles in the LDS ring
+constexpr int kKvPitch = 1040;               // bytes per latent row in LDS (+16: bank spread)
+constexpr int kTileKv = kRt * kKvPitch;      // 66560
+constexpr int kTileBytes = kTileKv + kRt * 128;  // + rope rows (128 B each)
+constexpr int kMaxSplitRows = 2048;
+constexpr int kLoadsPerTile = 9;             // per wave: 8 latent rows + 1 rope instruction
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;
 
-__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait for LDS ops, or for all but N of
+// this wave's outstanding vector-memory ops.
+constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Workgroup barrier that does not wait for in-flight global->LDS copies:
+// this wave's LDS writes are complete, then s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// max / sum over the 4 lanes l%16 + 16j that hold the same head.
+__device__ __forceinline__ float group_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
 template <bool kDense>
-__global__ __launch_bounds__(256) void mla_kernel(
+__global__ __launch_bounds__(kThreads) void mla_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int rows_per_split, int n_splits, int n_items, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
-  __shared__ __align__(16) uint16_t s_kv[kRt * kKvPitch];
-  __shared__ __align__(16) uint16_t s_p[4][16 * kPPitch];
-  __shared__ int s_valid[kRt];
+  __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
+  __shared__ int s_pos[kMaxSplitRows + kRt];
 
-  const int bid = blockIdx.x;
-  const int X = (bid >> 4) * 8 + (bid & 7);  // item = row * n_splits + split
-  const int hg = (bid >> 3) & 1;            // head group
+  const int X = blockIdx.x;  // item = row * n_splits + split
   if (X >= n_items) return;
   const int row = X / n_splits, split = X - row * n_splits;
   const int b = row / T, t = row - b * T;
@@ -72,215 +121,238 @@ __global__ __launch_bounds__(256) void mla_kernel(
   }
   const int j_begin = split * rows_per_split;
   const int j_end = min(j_begin + rows_per_split, n_list);
+  const int n_rows = max(j_end - j_begin, 0);
+  const int n_tiles = (n_rows + kRt - 1) / kRt;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;
 
-  // Query fragment (A operand): head hg*64 + wave*16 + r16; K-step kk holds dims
-  // kk*32 + 8g .. +7 of [q_nope | q_pe].
-  uint4 qa[18];
+  // Row positions of the split -> LDS (-1 = empty slot, also past the end).
+  for (int j = threadIdx.x; j < n_tiles * kRt; j += kThreads) {
+    int pos = -1;
+    if (j < n_rows) {
+      if constexpr (kDense) {
+        pos = j_begin + j;
+      } else {
+        pos = idx[(size_t)row * k + j_begin + j];
+        if (pos < 0 || pos >= S_max) pos = -1;
+      }
+    }
+    s_pos[j] = pos;
+  }
+
+  // Query fragment (B operand of S^T = KV . Q^T): head wave*16 + r16;
+  // K-step kk holds dims kk*32 + 8g .. +7 of [q_nope | q_pe].
+  const int head = wave * 16 + r16;
+  uint4 qb[18];
   {
-    const int head = hg * kHpb + wave * 16 + r16;
     const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc;
     const uint16_t* qp = q_pe + ((size_t)row * kHeads + head) * kDr;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qa[kk] = ldg16(qn + kk * 32 + g * 8);
+    for (int kk = 0; kk < 16; ++kk) qb[kk] = ldg16(qn + kk * 32 + g * 8);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) qa[16 + kk] = ldg16(qp + kk * 32 + g * 8);
+    for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = ldg16(qp + kk * 32 + g * 8);
   }
+  __syncthreads();  // s_pos visible; the query loads have completed
 
-  // Running softmax state for the 4 heads 4g+i whose results this lane holds.
-  float m_run[4], l_part[4];
+  const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
+  const uint8_t* pe_b = reinterpret_cast<const uint8_t*>(pe) + (size_t)b * S_max * kDr * 2;
+
+  // This wave copies rows 8*wave .. 8*wave+7 of tile `tile` into ring slot tile % kNbuf.
+  auto issue = [&](int tile) {
+    uint8_t* base = s_ring + (tile % kNbuf) * kTileBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_part[i] = 0.f;
-  }
-  f32x4 o[32];
+    for (int r = 0; r < 8; ++r) {
+      const int trow = 8 * wave + r;
+      const int pos = max(s_pos[tile * kRt + trow], 0);  // empty slots read row 0 (masked later)
+      __builtin_amdgcn_global_load_lds((glb_void*)(kv_b + (size_t)pos * (kDc * 2) + lane * 16),
+                                       (lds_void*)(base + trow * kKvPitch), 16, 0, 0);
+    }
+    // Rope parts of the wave's 8 rows: lane L writes chunk L%8 of row L/8, holding
+    // the row's global chunk (L%8) ^ (row & 7).
+    const int trow = 8 * wave + (lane >> 3);
+    const int pos = max(s_pos[tile * kRt + trow], 0);
+    const int chunk = (lane & 7) ^ (trow & 7);
+    __builtin_amdgcn_global_load_lds((glb_void*)(pe_b + (size_t)pos * (kDr * 2) + chunk * 16),
+                                     (lds_void*)(base + kTileKv + 8 * wave * 128), 16, 0, 0);
+  };
+
+  // Running softmax state for head `head` (base 2): reference max, and this
+  // lane's share of the sum relative to it.
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[32];  // O^T: tile ct holds latent dims ct*16 + 4g + i for this lane's head
 #pragma unroll
   for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Gather assignment: thread -> tile row lr, 1/8 of that row.
-  const int lr = threadIdx.x >> 3, lp = threadIdx.x & 7;
-  uint4 pf[9];
-  int pf_valid = 0;
-  auto issue = [&](int j0) {
-    const int j = j0 + lr;
-    int pos;
-    bool valid;
-    if constexpr (kDense) {
-      pos = j;
-      valid = j < j_end;
-    } else {
-      pos = j < j_end ? idx[(size_t)row * k + j] : -1;
-      valid = pos >= 0 && pos < S_max;
-    }
-    if (!valid) pos = 0;  // a safe address; the row is masked out below
-    const uint16_t* src = kv + ((size_t)b * S_max + pos) * kDc + lp * 64;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) pf[u] = ldg16(src + u * 8);
-    pf[8] = ldg16(pe + ((size_t)b * S_max + pos) * kDr + lp * 8);
-    pf_valid = valid ? 1 : 0;
-  };
+  for (int p = 0; p < kNbuf - 1 && p < n_tiles; ++p) issue(p);
 
-  if (j_begin < j_end) issue(j_begin);
 #pragma unroll 1
-  for (int j0 = j_begin; j0 < j_end; j0 += kRt) {
-    __syncthreads();  // every wave is done with the previous tile
-    {
-      uint16_t* dst = s_kv + lr * kKvPitch;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + lp * 64 + u * 8) = pf[u];
-      *reinterpret_cast<uint4*>(dst + kDc + lp * 8) = pf[8];
-      if (lp == 0) s_valid[lr] = pf_valid;
-    }
-    __syncthreads();
-    if (j0 + kRt < j_end) issue(j0 + kRt);  // next tile's loads overlap this tile's math
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    if (tile + kNbuf - 1 < n_tiles) issue(tile + kNbuf - 1);
+    static_assert(kNbuf == 2, "the wait below assumes one tile in flight");
+    if (tile + 1 < n_tiles)  // the next tile's copies may still be in flight
+      __builtin_amdgcn_s_waitcnt(wait_vm(kLoadsPerTile));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    lds_barrier();  // every wave's copies for this tile have landed
 
-    // ---- scores: S[head 4g+i][row nt*16 + r16] ----
-    f32x4 sc[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      sc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* brow = s_kv + (nt * 16 + r16) * kKvPitch + g * 8;
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk)
-        sc[nt] = mfma_bf16_16x16x32(as_bf16x8(qa[kk]),
-                                    as_bf16x8(*reinterpret_cast<const uint4*>(brow + kk * 32)),
-                                    sc[nt]);
-    }
+    const uint8_t* buf = s_ring + (tile % kNbuf) * kTileBytes;
 
-    // ---- online softmax (base 2) ----
-    float p[2][4], alpha[4];
-    const bool v0 = s_valid[r16] != 0, v1 = s_valid[16 + r16] != 0;
+    // ---- scores S^T[row][head], rows mt*16 + 4g + i ----
+    f32x4 sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s0 = v0 ? sc[0][i] * scale_log2 : -INFINITY;
-      const float s1 = v1 ? sc[1][i] * scale_log2 : -INFINITY;
-      float mx = fmaxf(s0, s1);
-      mx = fmaxf(mx, xor_shfl(mx, 1));
-      mx = fmaxf(mx, xor_shfl(mx, 2));
-      mx = fmaxf(mx, xor_shfl(mx, 4));
-      mx = fmaxf(mx, xor_shfl(mx, 8));
-      const float m_new = fmaxf(m_run[i], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[i] = exp2f(m_run[i] - m_use);
-      m_run[i] = m_new;
-      p[0][i] = exp2f(s0 - m_use);
-      p[1][i] = exp2f(s1 - m_use);
-      l_part[i] = l_part[i] * alpha[i] + p[0][i] + p[1][i];
+    for (int mt = 0; mt < 4; ++mt) sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int trow = mt * 16 + r16;
+        const uint8_t* a;
+        if (kk < 16) {
+          a = buf + trow * kKvPitch + (kk * 32 + 8 * g) * 2;
+        } else {
+          const int chunk = ((kk - 16) * 4 + g) ^ (trow & 7);
+          a = buf + kTileKv + trow * 128 + chunk * 16;
+        }
+        sc[mt] = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(a)),
+                                    as_bf16x8(qb[kk]), sc[mt]);
+      }
     }
 
-    // ---- probabilities: C layout -> LDS (bf16) -> A layout ----
-    uint16_t* pw = s_p[wave];
+    // ---- online softmax for this lane's head ----
+    float mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[(4 * g + i) * kPPitch + nt * 16 + r16] = f32_to_bf16_bits(p[nt][i]);
-    __syncthreads();
-    const uint4 pa = *reinterpret_cast<const uint4*>(pw + r16 * kPPitch + 8 * g);
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = s_pos[tile * kRt + mt * 16 + 4 * g + i] >= 0;
+        sc[mt][i] = valid ? sc[mt][i] * scale_log2 : -INFINITY;  // now log2-domain score
+        mx = fmaxf(mx, sc[mt][i]);
+      }
+    mx = group_max(mx);
+    // Lazy rescaling: the reference m_run moves only when this tile's max
+    // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
+    // below 2^kRescaleSlack and the accumulators are rarely touched.
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+    uint4 pb[2];  // B operands of the value contraction, one per 32-row K-step
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[h][i] = exp2f(sc[2 * ks + h][i] - m_use);
+          psum += p[h][i];
+        }
+      // K-step ks covers M-tiles 2ks and 2ks+1: rows 32ks + 4g + i, then 32ks + 16 + 4g + i.
+      pb[ks] = uint4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                     pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+    }
+    l_part += psum;
 
-    // ---- values: O[head][c] = alpha * O + P . V ----
-    const uint16_t* vbase = s_kv + (8 * g + (r16 >> 2)) * kKvPitch + 4 * (r16 & 3);
+    // ---- values: O^T[c][head] += V^T . P ----
+    // Transposed reads: lane r16 of group g gets V[32ks + 16h + 4g + j][c0 + r16]
+    // (j = 0..3) from the 8-byte rows addressed by lanes 4j + r16/4.
+    const uint8_t* vrow = buf + (4 * g + (r16 >> 2)) * kKvPitch + 8 * (r16 & 3);
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[ct][i] *= alpha[i];
-      const i16x4 lo = lds_read_tr16(vbase + ct * 16);
-      const i16x4 hi = lds_read_tr16(vbase + 4 * kKvPitch + ct * 16);
-      const uint4 vb = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                             (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                             (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                             (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-      o[ct] = mfma_bf16_16x16x32(as_bf16x8(pa), as_bf16x8(vb), o[ct]);
+      for (int ks = 0; ks < 2; ++ks) {
+        const i16x4 lo = lds_read_tr16(vrow + (32 * ks) * kKvPitch + ct * 32);
+        const i16x4 hi = lds_read_tr16(vrow + (32 * ks + 16) * kKvPitch + ct * 32);
+        const uint4 va = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        o[ct] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb[ks]), o[ct]);
+      }
     }
+    lds_barrier();  // every wave is done with this slot before it is refilled
   }
 
-  // ---- finish: sum l over the 16 lanes holding each head's columns ----
-  float l_tot[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float l = l_part[i];
-    l += xor_shfl(l, 1);
-    l += xor_shfl(l, 2);
-    l += xor_shfl(l, 4);
-    l += xor_shfl(l, 8);
-    l_tot[i] = l;
-  }
-  const int head0 = hg * kHpb + wave * 16 + 4 * g;
+  // ---- finish ----
+  const float l_tot = group_sum(l_part);
   if (n_splits == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = out + ((size_t)row * kHeads + head) * kDc + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float inv = l_tot[i] > 0.f ? 1.f / l_tot[i] : 0.f;
-      uint16_t* orow = out + ((size_t)row * kHeads + head0 + i) * kDc;
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) orow[ct * 16 + r16] = f32_to_bf16_bits(o[ct][i] * inv);
-      if (lse != nullptr && r16 == 0)
-        lse[(size_t)row * kHeads + head0 + i] =
-            l_tot[i] > 0.f ? (m_run[i] + log2f(l_tot[i])) * kLn2 : -INFINITY;
-    }
+    for (int ct = 0; ct < 32; ++ct)
+      *reinterpret_cast<uint2*>(orow + ct * 16) =
+          uint2{pack_bf16(o[ct][0] * inv, o[ct][1] * inv), pack_bf16(o[ct][2] * inv, o[ct][3] * inv)};
+    if (lse != nullptr && g == 0)
+      lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    float* prow = part_o + ((size_t)X * kHeads + head) * kDc + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* prow = part_o + ((size_t)X * kHeads + head0 + i) * kDc;
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) prow[ct * 16 + r16] = o[ct][i];
-      if (r16 == 0) part_ml[(size_t)X * kHeads + head0 + i] = float2{m_run[i], l_tot[i]};
-    }
+    for (int ct = 0; ct < 32; ++ct)
+      *reinterpret_cast<float4*>(prow + ct * 16) = float4{o[ct][0], o[ct][1], o[ct][2], o[ct][3]};
+    if (g == 0) part_ml[(size_t)X * kHeads + head] = float2{m_run, l_tot};
   }
 }
 
-// Merge the per-split partial outputs of one (row, head): 64 threads per head,
-// 8 latent dims each.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+// Merge the per-split partial outputs of one (row, head) per 128-thread block;
+// each thread owns 4 latent dims.
+__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float2* __restrict__ part_ml,
-                                                          int n_rows, int n_splits,
-                                                          uint16_t* __restrict__ out,
+                                                          int n_splits, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);  // row * 128 + head
-  if (rh >= n_rows * kHeads) return;
+  const int rh = blockIdx.x;  // row * 128 + head
   const int row = rh / kHeads, head = rh - row * kHeads;
-  const int c0 = (threadIdx.x & 63) * 8;
+  const int c0 = threadIdx.x * 4;
+  const float2* ml = part_ml + (size_t)row * n_splits * kHeads + head;
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    M = fmaxf(M, part_ml[((size_t)row * n_splits + s) * kHeads + head].x);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[(size_t)s * kHeads].x);
+  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
+    const float* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
+#pragma unroll 4
     for (int s = 0; s < n_splits; ++s) {
-      const size_t item = (size_t)row * n_splits + s;
-      const float2 ml = part_ml[item * kHeads + head];
-      if (ml.y <= 0.f) continue;
-      const float f = exp2f(ml.x - M);
-      L += ml.y * f;
-      const float* src = part_o + (item * kHeads + head) * kDc + c0;
-      const float4 a = *reinterpret_cast<const float4*>(src);
-      const float4 c = *reinterpret_cast<const float4*>(src + 4);
-      acc[0] += a.x * f; acc[1] += a.y * f; acc[2] += a.z * f; acc[3] += a.w * f;
-      acc[4] += c.x * f; acc[5] += c.y * f; acc[6] += c.z * f; acc[7] += c.w * f;
+      const float2 v = ml[(size_t)s * kHeads];
+      const float f = v.y > 0.f ? exp2f(v.x - M) : 0.f;
+      L += v.y * f;
+      const float4 a = *reinterpret_cast<const float4*>(src + (size_t)s * kHeads * kDc);
+      acc.x += a.x * f;
+      acc.y += a.y * f;
+      acc.z += a.z * f;
+      acc.w += a.w * f;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint32_t packed[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    packed[u] = (uint32_t)f32_to_bf16_bits(acc[2 * u] * inv) |
-                ((uint32_t)f32_to_bf16_bits(acc[2 * u + 1] * inv) << 16);
-  *reinterpret_cast<uint4*>(out + (size_t)rh * kDc + c0) =
-      uint4{packed[0], packed[1], packed[2], packed[3]};
-  if (lse != nullptr && (threadIdx.x & 63) == 0)
-    lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<uint2*>(out + (size_t)rh * kDc + c0) =
+      uint2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
+  if (lse != nullptr && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+#ifndef DSA_MLA_TARGET_BLOCKS
+#define DSA_MLA_TARGET_BLOCKS 256
+#endif
+#ifndef DSA_MLA_MIN_SPLIT_ROWS
+#define DSA_MLA_MIN_SPLIT_ROWS 64
+#endif
+
 MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
-  // Aim for ~512 workgroups (2 head groups each item) without splits under 128 rows.
-  long ns = 512 / (2 * rows);
-  const long max_ns = (k + 127) / 128;
+  // Aim for DSA_MLA_TARGET_BLOCKS workgroups without splits shorter than
+  // DSA_MLA_MIN_SPLIT_ROWS rows.
+  long ns = DSA_MLA_TARGET_BLOCKS / rows;
+  const long max_ns = (k + DSA_MLA_MIN_SPLIT_ROWS - 1) / DSA_MLA_MIN_SPLIT_ROWS;
   ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
-  const int rps = round_up((int)((k + ns - 1) / ns), kRt);
+  int rps = round_up((int)((k + ns - 1) / ns), kRt);
+  if (rps > kMaxSplitRows) rps = kMaxSplitRows;
   return MlaPlan{rps, (k + rps - 1) / rps};
 }
 
@@ -289,7 +361,7 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   // Rows per split depend only on the allocation sizes, so the workspace
   // computed from S_max always covers the launch.
   long rps = (long)S_max * 2 * rows / 1024;
-  rps = rps < 512 ? 512 : (rps > 8192 ? 8192 : rps);
+  rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
   const int r = round_up((int)rps, kRt);
   const int ext = max_end_pos > 0 ? max_end_pos : S_max;
   return MlaPlan{r, (ext + r - 1) / r};
@@ -314,8 +386,7 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
     part_o = reinterpret_cast<float*>(workspace);
     part_ml = reinterpret_cast<float2*>(part_o + (size_t)n_items * kHeads * kDc);
   }
-  const unsigned grid = (unsigned)(((n_items + 7) / 8) * 16);
-  hipLaunchKernelGGL(mla_kernel<kDense>, dim3(grid), dim3(256), 0, stream,
+  hipLaunchKernelGGL(mla_kernel<kDense>, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(q_nope),
                      reinterpret_cast<const uint16_t*>(q_pe), reinterpret_cast<const uint16_t*>(kv),
                      reinterpret_cast<const uint16_t*>(pe), idx, end_pos, T, S_max, k,
@@ -323,9 +394,8 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
                      reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
   if (hipGetLastError() != hipSuccess) return -5;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((rows * kHeads + 3) / 4)), dim3(256),
-                       0, stream, part_o, part_ml, rows, plan.n_splits,
-                       reinterpret_cast<uint16_t*>(out), lse);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * kHeads)), dim3(128), 0, stream,
+                       part_o, part_ml, plan.n_splits, reinterpret_cast<uint16_t*>(out), lse);
     if (hipGetLastError() != hipSuccess) return -5;
   }
   return 0;

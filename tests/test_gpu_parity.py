@@ -380,3 +380,39 @@ def test_forward_deterministic():
     r1 = m.forward_case(case, topk_out=torch.empty((4, 1, 2048), dtype=torch.int32, device=DEV))
     r2 = m.forward_case(case, topk_out=torch.empty((4, 1, 2048), dtype=torch.int32, device=DEV))
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+
+
+def test_forward_graph_replay_matches_eager():
+    """dsa_forward captured in a HIP graph: every replay, with eager work in between,
+    gives the eager result bit for bit (no memset nodes, no hidden allocation)."""
+    m = dsa()
+    banner("forward graph replay")
+    case = inputs.make_case("graph", 2, 1, [5000, 3100], 5000, seed=18, device=DEV)
+    other = inputs.make_case("graph_other", 2, 1, [5000, 4000], 5000, seed=19, device=DEV)
+    B, T, S, k = case.B, case.T, case.S_max, case.topk
+    ws = torch.empty(m.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, 128), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+
+    def run(c):
+        m.forward(c.q, c.w, c.k_cache, c.end_pos, c.q_nope, c.q_pe, c.kv_cache, c.pe_cache,
+                  c.scale, c.softmax_scale, k=k, max_end_pos=S, out=out, lse=lse, topk_out=idx,
+                  workspace=ws)
+
+    run(case)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), idx.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(case)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        run(other)  # eager work that overwrites every output and the workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(idx, ref[2]), rep
