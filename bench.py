@@ -151,7 +151,7 @@ def bench_workload(dsa, torch, case, steps, warmup, per_kernel=True):
     B, T, S, k = case.B, case.T, case.S_max, case.topk
     dev = case.q.device
     mep = case.max_end_pos
-    ws = torch.empty(dsa.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(dsa.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
     idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
@@ -176,8 +176,12 @@ def bench_workload(dsa, torch, case, steps, warmup, per_kernel=True):
         dsa.index_scores(c.q, c.w, c.k_cache, c.end_pos, c.scale, q_scale=c.q_scale,
                          k_scale=c.k_scale, max_end_pos=mep, out=scores)
 
+    topk_ws = torch.zeros(max(1, dsa.lib().dsa_topk_workspace_size(B, T, S, k)),
+                          dtype=torch.uint8, device=dev)
+
     def st_topk(i):
-        dsa.topk(scores, copies[i % len(copies)].end_pos, k, max_end_pos=mep, out=idx)
+        dsa.topk(scores, copies[i % len(copies)].end_pos, k, max_end_pos=mep, out=idx,
+                 workspace=topk_ws)
 
     mla_ws = torch.empty(max(1, dsa.lib().dsa_sparse_mla_workspace_size(B, T, k)),
                          dtype=torch.uint8, device=dev)

@@ -119,7 +119,10 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # Zero-filled: the top-k stage keeps a per-row histogram in its workspace
+        # between calls and expects zeros the first time (any other content is
+        # still correct, only slower once).
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace of {workspace.numel()} bytes < required {nbytes}")
     return workspace, workspace.numel() * workspace.element_size()

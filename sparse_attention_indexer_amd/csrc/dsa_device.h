@@ -59,8 +59,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // Order-preserving map from an fp32 score to an unsigned key: larger score,
 // larger key.  -0 is first turned into +0 so the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // x + 0 turns -0 into +0.  Negative values: all bits flipped; others: the
+  // sign bit set.  (An arithmetic shift spreads the sign over the mask.)
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -68,6 +70,22 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 template <typename T>
 __device__ __forceinline__ T xor_shfl(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
+}
+
+// s_waitcnt immediates (gfx9 encoding): wait for LDS ops, or for all but N of
+// this wave's outstanding vector-memory ops.
+constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for the
+// wave's outstanding global loads (or global->LDS copies), so they stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace dsa

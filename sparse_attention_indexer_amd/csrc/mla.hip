@@ -43,15 +43,24 @@ namespace dsa {
 constexpr int kHeads = 128;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kWaves = 8;                    // 16 heads each
-constexpr int kThreads = kWaves * 64;
-constexpr int kRt = 64;                      // gathered rows per tile
 constexpr int kNbuf = 2;                     // tiles in the LDS ring
 constexpr int kKvPitch = 1040;               // bytes per latent row in LDS (+16: bank spread)
-constexpr int kTileKv = kRt * kKvPitch;      // 66560
-constexpr int kTileBytes = kTileKv + kRt * 128;  // + rope rows (128 B each)
 constexpr int kMaxSplitRows = 2048;
 constexpr int kLoadsPerTile = 9;             // per wave: 8 latent rows + 1 rope instruction
+
+// Shape of one workgroup: kWaves waves of 16 heads; every wave copies 8 rows
+// of each tile, so a tile has 8*kWaves rows.
+template <int kWaves>
+struct MlaShape {
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kHeadsPerBlock = 16 * kWaves;
+  static constexpr int kHeadGroups = kHeads / kHeadsPerBlock;
+  static constexpr int kRt = 8 * kWaves;                  // gathered rows per tile
+  static constexpr int kMt = kRt / 16;                    // 16-row M-tiles per tile
+  static constexpr int kKs = kRt / 32;                    // 32-row K-steps of the value product
+  static constexpr int kTileKv = kRt * kKvPitch;
+  static constexpr int kTileBytes = kTileKv + kRt * 128;  // + rope rows (128 B each)
+};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;
@@ -62,20 +71,6 @@ typedef __attribute__((address_space(1))) void glb_void;
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
-
-// s_waitcnt immediates (gfx9 encoding): wait for LDS ops, or for all but N of
-// this wave's outstanding vector-memory ops.
-constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-
-// Workgroup barrier that does not wait for in-flight global->LDS copies:
-// this wave's LDS writes are complete, then s_barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // max / sum over the 4 lanes l%16 + 16j that hold the same head.
@@ -96,18 +91,33 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
 
-template <bool kDense>
-__global__ __launch_bounds__(kThreads) void mla_kernel(
+template <bool kDense, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int rows_per_split, int n_splits, int n_items, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
+  using S = MlaShape<kWaves>;
+  constexpr int kThreads = S::kThreads, kRt = S::kRt, kMt = S::kMt, kKs = S::kKs;
+  constexpr int kTileKv = S::kTileKv, kTileBytes = S::kTileBytes;
   __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
-  __shared__ int s_pos[kMaxSplitRows + kRt];
+  __shared__ int s_pos[kMaxSplitRows + 64];
 
-  const int X = blockIdx.x;  // item = row * n_splits + split
+  // Block -> (item = row * n_splits + split, head group).  The head groups of
+  // one item get ids that are 8 apart, i.e. fall on the same XCD (ids are dealt
+  // round-robin over the 8 XCDs), so later groups find the rows in its L2.
+  int X, hg;
+  if constexpr (S::kHeadGroups == 1) {
+    X = blockIdx.x;
+    hg = 0;
+  } else {
+    constexpr int G = S::kHeadGroups;
+    const int bid = blockIdx.x;
+    X = (bid / (8 * G)) * 8 + (bid & 7);
+    hg = (bid >> 3) % G;
+  }
   if (X >= n_items) return;
   const int row = X / n_splits, split = X - row * n_splits;
   const int b = row / T, t = row - b * T;
@@ -141,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
     s_pos[j] = pos;
   }
 
-  // Query fragment (B operand of S^T = KV . Q^T): head wave*16 + r16;
+  // Query fragment (B operand of S^T = KV . Q^T): head hg*16*kWaves + wave*16 + r16;
   // K-step kk holds dims kk*32 + 8g .. +7 of [q_nope | q_pe].
-  const int head = wave * 16 + r16;
+  const int head = hg * S::kHeadsPerBlock + wave * 16 + r16;
   uint4 qb[18];
   {
     const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc;
@@ -199,13 +209,13 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
     const uint8_t* buf = s_ring + (tile % kNbuf) * kTileBytes;
 
     // ---- scores S^T[row][head], rows mt*16 + 4g + i ----
-    f32x4 sc[4];
+    f32x4 sc[kMt];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < kMt; ++mt) sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < kMt; ++mt) {
         const int trow = mt * 16 + r16;
         const uint8_t* a;
         if (kk < 16) {
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
     // ---- online softmax for this lane's head ----
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < kMt; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool valid = s_pos[tile * kRt + mt * 16 + 4 * g + i] >= 0;
@@ -244,9 +254,9 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
-    uint4 pb[2];  // B operands of the value contraction, one per 32-row K-step
+    uint4 pb[kKs];  // B operands of the value contraction, one per 32-row K-step
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kKs; ++ks) {
       float p[2][4];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < kKs; ++ks) {
         const i16x4 lo = lds_read_tr16(vrow + (32 * ks) * kKvPitch + ct * 32);
         const i16x4 hi = lds_read_tr16(vrow + (32 * ks + 16) * kKvPitch + ct * 32);
         const uint4 va = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
@@ -302,37 +312,60 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(
 }
 
 // Merge the per-split partial outputs of one (row, head) per 128-thread block;
-// each thread owns 4 latent dims.
+// each thread owns 4 latent dims.  The split maxima and sums are reduced over
+// the block first (threads stride over the splits); the partial rows are then
+// read eight splits at a time so their loads overlap.
 __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float2* __restrict__ part_ml,
                                                           int n_splits, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
+  __shared__ float s_red[2][2];
   const int rh = blockIdx.x;  // row * 128 + head
   const int row = rh / kHeads, head = rh - row * kHeads;
-  const int c0 = threadIdx.x * 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float2* ml = part_ml + (size_t)row * n_splits * kHeads + head;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[(size_t)s * kHeads].x);
+
+  float m_loc = -INFINITY;
+  for (int s = tid; s < n_splits; s += 128) {
+    const float2 v = ml[(size_t)s * kHeads];
+    m_loc = fmaxf(m_loc, v.y > 0.f ? v.x : -INFINITY);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, off, 64));
+  if (lane == 0) s_red[0][wave] = m_loc;
+  __syncthreads();
+  const float M = fmaxf(s_red[0][0], s_red[0][1]);
+
+  const int c0 = tid * 4;
+  const float* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
+  const size_t stride = (size_t)kHeads * kDc;
   float4 acc = float4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    const float* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
-#pragma unroll 4
-    for (int s = 0; s < n_splits; ++s) {
-      const float2 v = ml[(size_t)s * kHeads];
-      const float f = v.y > 0.f ? exp2f(v.x - M) : 0.f;
-      L += v.y * f;
-      const float4 a = *reinterpret_cast<const float4*>(src + (size_t)s * kHeads * kDc);
-      acc.x += a.x * f;
-      acc.y += a.y * f;
-      acc.z += a.z * f;
-      acc.w += a.w * f;
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+      float4 a[8];
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(s0 + u, n_splits - 1);
+        a[u] = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
+        v[u] = ml[(size_t)s * kHeads];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = (s0 + u < n_splits && v[u].y > 0.f) ? exp2f(v[u].x - M) : 0.f;
+        L += v[u].y * w;
+        acc.x += a[u].x * w;
+        acc.y += a[u].y * w;
+        acc.z += a[u].z * w;
+        acc.w += a[u].w * w;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<uint2*>(out + (size_t)rh * kDc + c0) =
       uint2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
-  if (lse != nullptr && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (lse != nullptr && tid == 0) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -340,37 +373,68 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #ifndef DSA_MLA_TARGET_BLOCKS
 #define DSA_MLA_TARGET_BLOCKS 256
 #endif
-#ifndef DSA_MLA_MIN_SPLIT_ROWS
-#define DSA_MLA_MIN_SPLIT_ROWS 64
+#ifndef DSA_MLA_SMALL_ROWS
+#define DSA_MLA_SMALL_ROWS 16
+#endif
+#ifndef DSA_MLA_SMALL_SPLIT_MIN
+#define DSA_MLA_SMALL_SPLIT_MIN 64
 #endif
 
+// Few query rows (decode at small batch): 4-wave blocks of 64 heads and short
+// splits, so one query is spread over many CUs.  Otherwise 8-wave blocks of
+// all 128 heads (every gathered row read once) and about one block per CU.
 MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
-  // Aim for DSA_MLA_TARGET_BLOCKS workgroups without splits shorter than
-  // DSA_MLA_MIN_SPLIT_ROWS rows.
+  if (rows <= DSA_MLA_SMALL_ROWS) {
+    // Splits of k*rows/128 rows (a power of two, at least DSA_MLA_SMALL_SPLIT_MIN):
+    // about 128 items of 2 head groups each.
+    int rps = DSA_MLA_SMALL_SPLIT_MIN;
+    while (rps < kMaxSplitRows && (long)rps * 128 < (long)k * rows) rps *= 2;
+    return MlaPlan{rps, (k + rps - 1) / rps, 4};
+  }
   long ns = DSA_MLA_TARGET_BLOCKS / rows;
-  const long max_ns = (k + DSA_MLA_MIN_SPLIT_ROWS - 1) / DSA_MLA_MIN_SPLIT_ROWS;
+  const long max_ns = (k + 63) / 64;
   ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
-  int rps = round_up((int)((k + ns - 1) / ns), kRt);
+  int rps = round_up((int)((k + ns - 1) / ns), 64);
   if (rps > kMaxSplitRows) rps = kMaxSplitRows;
-  return MlaPlan{rps, (k + rps - 1) / rps};
+  return MlaPlan{rps, (k + rps - 1) / rps, 8};
 }
 
 MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   const long rows = (long)B * T;
   // Rows per split depend only on the allocation sizes, so the workspace
   // computed from S_max always covers the launch.
-  long rps = (long)S_max * 2 * rows / 1024;
+  long rps = (long)S_max * rows / DSA_MLA_TARGET_BLOCKS;
   rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
-  const int r = round_up((int)rps, kRt);
+  const int r = round_up((int)rps, 64);
   const int ext = max_end_pos > 0 ? max_end_pos : S_max;
-  return MlaPlan{r, (ext + r - 1) / r};
+  return MlaPlan{r, (ext + r - 1) / r, 8};
 }
 
 size_t mla_workspace_bytes(int B, int T, const MlaPlan& plan) {
   if (plan.n_splits <= 1) return 0;
   const size_t items = (size_t)B * T * plan.n_splits;
   return items * kHeads * kDc * sizeof(float) + items * kHeads * sizeof(float2);
+}
+
+template <bool kDense, int kWaves>
+static int launch_mla_shape(const void* q_nope, const void* q_pe, const void* kv,
+                            const void* pe, const int32_t* idx, const int32_t* end_pos, int T,
+                            int S_max, int k, const MlaPlan& plan, int rows, float softmax_scale,
+                            void* out, float* lse, float* part_o, float2* part_ml,
+                            hipStream_t stream) {
+  using S = MlaShape<kWaves>;
+  const int n_items = rows * plan.n_splits;
+  const unsigned grid = S::kHeadGroups == 1
+                            ? (unsigned)n_items
+                            : (unsigned)(((n_items + 7) / 8) * 8 * S::kHeadGroups);
+  hipLaunchKernelGGL((mla_kernel<kDense, kWaves>), dim3(grid), dim3(S::kThreads), 0, stream,
+                     reinterpret_cast<const uint16_t*>(q_nope),
+                     reinterpret_cast<const uint16_t*>(q_pe), reinterpret_cast<const uint16_t*>(kv),
+                     reinterpret_cast<const uint16_t*>(pe), idx, end_pos, T, S_max, k,
+                     plan.rows_per_split, plan.n_splits, n_items, softmax_scale * kLog2e,
+                     reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 template <bool kDense>
@@ -386,13 +450,14 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
     part_o = reinterpret_cast<float*>(workspace);
     part_ml = reinterpret_cast<float2*>(part_o + (size_t)n_items * kHeads * kDc);
   }
-  hipLaunchKernelGGL(mla_kernel<kDense>, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(q_nope),
-                     reinterpret_cast<const uint16_t*>(q_pe), reinterpret_cast<const uint16_t*>(kv),
-                     reinterpret_cast<const uint16_t*>(pe), idx, end_pos, T, S_max, k,
-                     plan.rows_per_split, plan.n_splits, n_items, softmax_scale * kLog2e,
-                     reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
-  if (hipGetLastError() != hipSuccess) return -5;
+  int st;
+  if (plan.waves == 4)
+    st = launch_mla_shape<kDense, 4>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan, rows,
+                                     softmax_scale, out, lse, part_o, part_ml, stream);
+  else
+    st = launch_mla_shape<kDense, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan, rows,
+                                     softmax_scale, out, lse, part_o, part_ml, stream);
+  if (st) return st;
   if (plan.n_splits > 1) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * kHeads)), dim3(128), 0, stream,
                        part_o, part_ml, plan.n_splits, reinterpret_cast<uint16_t*>(out), lse);

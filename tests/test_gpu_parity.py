@@ -212,6 +212,22 @@ def test_topk_longest_rows():
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+def test_topk_rows_around_bitmap_limit():
+    """Rows up to 262144 positions are selected through LDS bitmaps; longer
+    ones take the general path.  Both sides of that limit, and a row whose
+    threshold bin is too crowded for the candidate list (a narrow score
+    range), must match the oracle."""
+    m = dsa()
+    banner("topk rows of 262144 / 262145 / 300000 positions")
+    B, T, S, k = 4, 1, 300000, 2048
+    ep = np.array([262144, 262145, 300000, 50000], np.int32)
+    scores = inputs.make_scores(B, T, S, kind="normal", seed=8, device=DEV)
+    scores[3] = 1000.0 + scores[3] * 1e-3  # ~all of row 3 in one histogram bin
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 # --- attention --------------------------------------------------------------------
 
 def _mla_inputs(B, T, S, ep, seed):
@@ -390,7 +406,7 @@ def test_forward_graph_replay_matches_eager():
     case = inputs.make_case("graph", 2, 1, [5000, 3100], 5000, seed=18, device=DEV)
     other = inputs.make_case("graph_other", 2, 1, [5000, 4000], 5000, seed=19, device=DEV)
     B, T, S, k = case.B, case.T, case.S_max, case.topk
-    ws = torch.empty(m.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(m.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=DEV)
     out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, T, 128), dtype=torch.float32, device=DEV)
     idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
@@ -416,3 +432,26 @@ def test_forward_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(idx, ref[2]), rep
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x3C, "random"])
+def test_topk_any_workspace_content(fill):
+    """The top-k workspace carries a histogram between calls; whatever it holds,
+    the selection is exact (a stale or garbage histogram only costs speed)."""
+    m = dsa()
+    banner(f"topk workspace fill={fill}")
+    B, T, S, k = 3, 1, 40000, 2048
+    ep = np.array([40000, 33000, 9000], np.int32)
+    scores = inputs.make_scores(B, T, S, kind="normal", seed=21, device=DEV)
+    nbytes = m.lib().dsa_topk_workspace_size(B, T, S, k)
+    if fill == "random":
+        g = torch.Generator(device=DEV)
+        g.manual_seed(5)
+        ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
+    else:
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    end_pos = torch.from_numpy(ep).to(DEV)
+    for rep in range(3):  # the first call may take the slow path, later ones the fast path
+        out = m.topk(scores, end_pos, k, max_end_pos=S, workspace=ws)
+        assert np.array_equal(out.cpu().numpy(), ref), rep
