@@ -118,7 +118,7 @@ DSA_EXPORT int dsa_index_scores(const void* q, const float* q_scale, const float
   if (!index_score) return kErrInvalid;
   if (!aligned4(index_score)) return kErrMisaligned;
   return dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
-                                  max_end_pos, scale, dtype, index_score, stream);
+                                  max_end_pos, scale, dtype, index_score, nullptr, stream);
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k) {
@@ -134,7 +134,7 @@ DSA_EXPORT int dsa_topk(const float* index_score, const int32_t* end_pos, int32_
   st = check_workspace(workspace, workspace_bytes, dsa::topk_workspace_bytes(B, T, S_max, k));
   if (st) return st;
   return dsa::launch_topk(index_score, end_pos, B, T, S_max, max_end_pos, k, topk_indices,
-                          workspace, stream);
+                          workspace, /*counters_clear=*/false, stream);
 }
 
 DSA_EXPORT size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t T, int32_t k) {
@@ -189,11 +189,13 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   int32_t* indices =
       topk_indices_out ? topk_indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
+  // The indexer also clears the top-k's per-row counters.
+  uint32_t* topk_ctr = dsa::topk_counters(ws + L.topk_ws, B, T);
   st = dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
-                                max_end_pos, index_scale, dtype, scores, stream);
+                                max_end_pos, index_scale, dtype, scores, topk_ctr, stream);
   if (st) return st;
   st = dsa::launch_topk(scores, end_pos, B, T, S_max, max_end_pos, k, indices, ws + L.topk_ws,
-                        stream);
+                        /*counters_clear=*/topk_ctr != nullptr, stream);
   if (st) return st;
   return dsa::launch_sparse_mla(q_nope, q_pe, kv_cache, pe_cache, indices, B, T, S_max, k,
                                 softmax_scale, out, lse, ws + L.mla_ws, stream);

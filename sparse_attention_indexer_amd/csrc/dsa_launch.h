@@ -9,13 +9,21 @@
 
 namespace dsa {
 
+// With topk_ctr != nullptr the indexer also clears the top-k's per-row
+// counters (2 words per row, see topk_counters), so that launch_topk can run
+// with counters_clear = true and skip its own clearing kernel.
 int launch_index_scores(const void* q, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, const int32_t* end_pos, int B, int T, int S_max,
-                        int max_end_pos, float scale, int dtype, float* out, hipStream_t stream);
+                        int max_end_pos, float scale, int dtype, float* out, uint32_t* topk_ctr,
+                        hipStream_t stream);
 
 size_t topk_workspace_bytes(int B, int T, int S_max, int k);
+// The per-row counters at the start of the top-k workspace, or nullptr when
+// B*T rows take a path without them.
+uint32_t* topk_counters(void* workspace, int B, int T);
 int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S_max,
-                int max_end_pos, int k, int32_t* out, void* workspace, hipStream_t stream);
+                int max_end_pos, int k, int32_t* out, void* workspace, bool counters_clear,
+                hipStream_t stream);
 
 // Split plan of the attention kernel: rows per split and number of splits.
 struct MlaPlan {

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ end_pos, int T, int S_max, float scale, int blocks_per_row,
-    int tiles_per_wave, float* __restrict__ out) {
+    int tiles_per_wave, float* __restrict__ out, uint32_t* __restrict__ topk_ctr) {
   // The block's 64x128 query in LDS, rows padded by 16 bytes so the 16 rows a
   // fragment read touches start on different banks.
   constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int keys_per_block = kIdxWaves * tiles_per_wave * kIdxTile;
   const int blk_start = blk * keys_per_block;
   if (blk_start > bound) return;
+  if (topk_ctr != nullptr && blk == 0 && threadIdx.x < 2) topk_ctr[2 * row + threadIdx.x] = 0u;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 
 int launch_index_scores(const void* q, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, const int32_t* end_pos, int B, int T, int S_max,
-                        int max_end_pos, float scale, int dtype, float* out, hipStream_t stream) {
+                        int max_end_pos, float scale, int dtype, float* out, uint32_t* topk_ctr,
+                        hipStream_t stream) {
   const long rows = (long)B * T;
   const long tiles_per_row = (max_end_pos + kIdxTile - 1) / kIdxTile;
   // Enough blocks to cover all 256 CUs several times over, but at least one
@@ -174,10 +176,12 @@ int launch_index_scores(const void* q, const float* q_scale, const float* w, con
   const dim3 grid((unsigned)(rows * blocks_per_row));
   if (dtype == 0)
     hipLaunchKernelGGL(indexer_kernel<false>, grid, dim3(256), 0, stream, q, q_scale, w, k,
-                       k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out);
+                       k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out,
+                       topk_ctr);
   else
     hipLaunchKernelGGL(indexer_kernel<true>, grid, dim3(256), 0, stream, q, q_scale, w, k,
-                       k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out);
+                       k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out,
+                       topk_ctr);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -11,16 +11,17 @@
 // result is unique.
 //
 // Three ways to run it, chosen on the host:
-//  * rows of at most 32768 positions: topk_lean_kernel, one 512-thread
-//    workgroup per row holding the whole row in registers (no workspace);
-//  * longer rows, up to 1024 of them: the row is spread over many workgroups
-//    (topk_hist_kernel, topk_classify_kernel) and a last one per row
-//    finishes the selection (topk_final_kernel);
-//  * more rows than that: full_row_topk, one workgroup per row, chunk by
-//    chunk (topk_row_kernel).
+//  * up to 1024 rows: topk_split_kernel spreads each row over workgroups of
+//    4096 positions; they cut the row down to a short list of candidates and
+//    the row's last workgroup finishes the selection (one launch);
+//  * more rows, each of at most 32768 positions: topk_lean_kernel, one
+//    512-thread workgroup per row holding the whole row in registers;
+//  * otherwise: full_row_topk, one workgroup per row, chunk by chunk
+//    (topk_row_kernel).
 // The first two build bitmaps of the certain winners and of the ties and read
-// the ordered output off them; full_row_topk (also their fallback for rows
-// whose candidate set is too crowded) compacts keys held in LDS.
+// the ordered output off them; full_row_topk (also their fallback when the
+// candidate list misses or overflows) compacts keys held in LDS.  None of them
+// needs the workspace to hold anything in particular beforehand.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -33,6 +34,7 @@ constexpr int kChunk = kTkThreads * kSeg;  // 32768 positions per chunk
 constexpr int kBins = 2048;
 constexpr int kCandCap = 4096;             // candidate keys
 constexpr int kHistWords = kBins + kBins / 32;
+constexpr int kMaxK = 2048;
 
 // Histogram bins are stored with one pad word per 32 so that a lane reading
 // 32 consecutive bins (the bin search) does not collide with other lanes.
@@ -45,14 +47,29 @@ __device__ __forceinline__ int swz(int t, int j) {
   return kSeg * t + 4 * ((j >> 2) ^ (t & (kSeg / 4 - 1))) + (j & 3);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): sums
+// within rows of 16 lanes by DPP row shifts, then the row totals are carried
+// over with row broadcasts (lane 15 into row 1 and 3, lane 31 into rows 2, 3).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active), in every lane:
+// the scan pattern of wave_incl_scan with max, read back from lane 63.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Exclusive prefix sums over the block of two per-thread values, plus totals.
@@ -131,41 +148,48 @@ __device__ __forceinline__ void read_batch(const uint32_t* s_keys, int bt, uint3
 
 // One wave finds the bin holding the `remaining`-th largest counted element
 // (counting from the top bin down): returns its digit and the count of
-// elements in higher bins.  Lane l owns the 32 (or 16) bins just below the
-// bins of lane l-1.
+// elements in higher bins.  Lane l owns the kNB/64 bins just below those of
+// lane l-1 (they share one pad offset, so a lane reads them at fixed offsets
+// from one address, and consecutive lanes hit different banks).  The crossing
+// lane comes from the scan of the per-lane sums; then its bins are scanned
+// with one bin per lane.  All 64 lanes must be active.  With no crossing (an
+// inconsistent histogram) the digit is meaningless but in range.
+template <int kNB, bool kPadded>
+__device__ __forceinline__ void wave_select_bin_t(const uint32_t* hist, uint32_t remaining,
+                                                  uint32_t& digit, uint32_t& above_out) {
+  constexpr int kPer = kNB / kWave;  // 32 or 16
+  const int lane = threadIdx.x & 63;
+  auto lane_bins = [&](int l) {
+    const int low = kNB - kPer * (l + 1);  // lowest bin of lane l
+    return hist + (kPadded ? low + (low >> 5) : low);
+  };
+  const uint32_t* hb = lane_bins(lane);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) sum += hb[u];
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t excl = incl - sum;
+  const uint64_t who = __builtin_amdgcn_ballot_w64(excl < remaining && remaining <= incl);
+  const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
+  const uint32_t above_src = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+  // Lane j < kPer takes bin (top bin of lane src) - j.
+  const uint32_t v = lane_bins(src)[kPer - 1 - min(lane, kPer - 1)];
+  const uint32_t cj = lane < kPer ? v : 0u;
+  const uint32_t incl2 = wave_incl_scan(cj) + above_src;
+  const uint32_t excl2 = incl2 - cj;
+  const uint64_t who2 =
+      __builtin_amdgcn_ballot_w64(lane < kPer && excl2 < remaining && remaining <= incl2);
+  const int j = who2 ? (int)__ffsll((long long)who2) - 1 : 0;
+  digit = (uint32_t)(kNB - 1 - kPer * src - j);
+  above_out = (uint32_t)__builtin_amdgcn_readlane((int)excl2, j);
+}
+
 template <bool kPadded = true>
 __device__ __forceinline__ void wave_select_bin(const uint32_t* hist, int nbins,
                                                 uint32_t remaining, uint32_t& digit,
                                                 uint32_t& above_out) {
-  const int lane = threadIdx.x & 63;
-  const int per = nbins / kWave;  // 32 or 16
-  uint32_t c[32];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    // Unconditional (clamped) read, masked afterwards: no branch per bin.
-    const int bin = max(nbins - 1 - (lane * per + u), 0);
-    const uint32_t v = hist[kPadded ? hpad((uint32_t)bin) : bin];
-    c[u] = u < per ? v : 0u;
-    sum += c[u];
-  }
-  const uint32_t incl = wave_incl_scan(sum);
-  uint32_t above = incl - sum;
-  uint32_t my_digit = 0, my_above = 0;
-  bool found = false;
-#pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    if (u < per && above < remaining && remaining <= above + c[u]) {
-      my_digit = (uint32_t)(nbins - 1 - (lane * per + u));
-      my_above = above;
-      found = true;
-    }
-    above += c[u];
-  }
-  const uint64_t who = __ballot(found);
-  const int src = __ffsll((long long)who) - 1;
-  digit = __shfl(my_digit, src, 64);
-  above_out = __shfl(my_above, src, 64);
+  if (nbins == kBins) wave_select_bin_t<kBins, kPadded>(hist, remaining, digit, above_out);
+  else wave_select_bin_t<kBins / 2, kPadded>(hist, remaining, digit, above_out);
 }
 
 // Block-wide version: wave 0 searches, everyone receives the result.
@@ -390,68 +414,7 @@ __device__ void full_row_topk(const float* __restrict__ x, int n, int k,
 // (a candidate set holding every element >= L with at least k elements
 // contains the top k).  A zero-filled workspace gets the fast path at once.
 // ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// Few rows: the row is spread over many workgroups.
-//   1. topk_hist_kernel: a histogram of the top 11 key bits per row (blocks of
-//      2048 positions count in LDS and add their non-zero bins to the row's
-//      histogram in the workspace); it also clears the row's candidate count.
-//   2. topk_classify_kernel: every block finds the bin d0 holding the k-th
-//      largest key from that histogram, then splits its positions into sure
-//      winners (top 11 bits above d0: one ballot per 64 positions, stored as
-//      a global bitmap) and candidates (in bin d0: appended, in any order, as
-//      (key, position) pairs to the row's candidate list).
-//   3. topk_final_kernel, one workgroup per row: loads the winner bitmap and
-//      the candidates into LDS, runs rounds 2 and 3 over the candidates only,
-//      adds those above the threshold to the winner bitmap and those equal to
-//      it to a tie bitmap, and reads the ordered output off the two bitmaps
-//      (winners, plus the first need_eq ties in position order).  It leaves
-//      the histogram zeroed for the next call.
-// The histogram only steers the work: the final kernel counts the winners S
-// and candidates C itself and, unless S < k <= S + C (the k-th largest key is
-// in bin d0) and the candidates fit, selects the row from scratch with
-// full_row_topk.  Any workspace content thus gives the exact result.
-// Many rows: full_row_topk, one workgroup per row (topk_row_kernel).
-constexpr int kBlk = 2048;           // positions per histogram / classify block
-constexpr int kBlkThreads = 256;     // 8 positions per thread
-constexpr int kMultiRows = 1024;     // up to this many rows take the multi-block path
-constexpr int kSelMaxN = 262144;     // longest row the final kernel's bitmaps cover
-constexpr int kSelWords = kSelMaxN / 32;
-constexpr int kSelCap = 8192;        // candidates per row
-
-struct TopkWs {
-  uint32_t* hist;   // [rows][kBins]
-  uint32_t* ctr;    // [rows][2]: candidate count, bin d0
-  uint64_t* win;    // [rows][n_blk * 32] winner bitmap, 64 positions a word
-  uint2* cand;      // [rows][kSelCap] (key, position)
-  int n_blk;        // blocks of kBlk positions per row (covering S_max)
-};
-
-__host__ __device__ inline int topk_blocks(int S_max) { return (S_max + kBlk - 1) / kBlk; }
-
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-__host__ inline TopkWs carve_topk_ws(void* ws, int rows, int S_max) {
-  TopkWs w;
-  w.n_blk = topk_blocks(S_max);
-  char* p = reinterpret_cast<char*>(ws);
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * kBins * 4);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * 2 * 4);
-  w.win = reinterpret_cast<uint64_t*>(p);
-  p += align256((size_t)rows * w.n_blk * (kBlk / 8));
-  w.cand = reinterpret_cast<uint2*>(p);
-  return w;
-}
-
-size_t topk_workspace_bytes(int B, int T, int S_max, int) {
-  const size_t rows = (size_t)B * T;
-  // Rows that fit one workgroup's registers (max_end_pos <= S_max <= 32768),
-  // or too many rows for the histogram path, need no workspace.
-  if (S_max <= kChunk || rows > (size_t)kMultiRows) return 0;
-  return align256(rows * kBins * 4) + align256(rows * 2 * 4) +
-         align256(rows * topk_blocks(S_max) * (kBlk / 8)) + rows * kSelCap * 8;
-}
 
 __device__ __forceinline__ int row_len(const int32_t* end_pos, int row, int T, int S_max) {
   const int b = row / T, t = row - b * T;
@@ -459,133 +422,7 @@ __device__ __forceinline__ int row_len(const int32_t* end_pos, int row, int T, i
   return ep - T + t + 1;
 }
 
-__global__ __launch_bounds__(kBlkThreads) void topk_hist_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
-    int k, TopkWs ws) {
-  __shared__ uint32_t s_h[kBins];
-  const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
-  const int n = row_len(end_pos, row, T, S_max);
-  const int base = blk * kBlk;
-  if (n <= k || base >= n) return;
-  const int len = min(kBlk, n - base);
-  const float* x = scores + (size_t)row * S_max + base;
-  const int tid = threadIdx.x;
-  float v[kBlk / kBlkThreads];
-#pragma unroll
-  for (int j = 0; j < kBlk / kBlkThreads; ++j) v[j] = x[min(tid + kBlkThreads * j, len - 1)];
-  for (int i = tid; i < kBins; i += kBlkThreads) s_h[i] = 0;
-  if (blk == 0 && tid == 0) ws.ctr[2 * row] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kBlk / kBlkThreads; ++j)
-    atomicAdd(&s_h[score_key(v[j]) >> 21], tid + kBlkThreads * j < len ? 1u : 0u);
-  __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)row * kBins;
-  for (int i = tid; i < kBins; i += kBlkThreads)
-    if (s_h[i] != 0) atomicAdd(&gh[i], s_h[i]);
-}
-
-__global__ __launch_bounds__(kBlkThreads) void topk_classify_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
-    int k, TopkWs ws) {
-  __shared__ uint32_t s_wsum[kBlkThreads / kWave];
-  __shared__ uint32_t s_d0;
-  const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
-  const int n = row_len(end_pos, row, T, S_max);
-  const int base = blk * kBlk;
-  if (n <= k || base >= n) return;
-  const int len = min(kBlk, n - base);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* x = scores + (size_t)row * S_max + base;
-
-  // Positions base + tid + 256j; the loads stay in flight during the bin search.
-  constexpr int kPer = kBlk / kBlkThreads;
-  float v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) v[j] = x[min(tid + kBlkThreads * j, len - 1)];
-
-  // Bin d0: thread t owns bins 2047-8t down to 2040-8t.
-  const uint32_t* gh = ws.hist + (size_t)row * kBins;
-  const uint4 h_hi = *reinterpret_cast<const uint4*>(gh + kBins - 8 * tid - 4);
-  const uint4 h_lo = *reinterpret_cast<const uint4*>(gh + kBins - 8 * tid - 8);
-  const uint32_t c[8] = {h_hi.w, h_hi.z, h_hi.y, h_hi.x, h_lo.w, h_lo.z, h_lo.y, h_lo.x};
-  uint32_t sum = 0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) sum += c[u];
-  // No crossing (an inconsistent histogram) leaves d0 = 0 and the final kernel
-  // falls back.  With garbage counts several bins may look like the crossing:
-  // the highest one is taken, so that every block of the row, reading the same
-  // histogram, classifies against the same d0.
-  if (tid == 0) s_d0 = 0;
-  const uint32_t incl = wave_incl_scan(sum);
-  if (lane == 63) s_wsum[wave] = incl;
-  lds_barrier();
-  uint32_t above = incl - sum;
-#pragma unroll
-  for (int w = 0; w < kBlkThreads / kWave; ++w) above += w < wave ? s_wsum[w] : 0u;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (above < (uint32_t)k && (uint32_t)k <= above + c[u])
-      atomicMax(&s_d0, (uint32_t)(kBins - 1 - (8 * tid + u)));
-    above += c[u];
-  }
-  lds_barrier();
-  const uint32_t d0 = s_d0;
-  if (blk == 0 && tid == 0) ws.ctr[2 * row + 1] = d0;
-
-  // Winners (bitmap) and candidates (count) of each 64-position group.
-  uint64_t my_win = 0;
-  uint32_t n_cand = 0;
-  uint64_t cm[kPer];
-  uint32_t key[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const bool valid = tid + kBlkThreads * j < len;
-    key[j] = score_key(v[j]);
-    const uint32_t d = key[j] >> 21;
-    const uint64_t wm = __ballot(valid && d > d0);
-    cm[j] = __ballot(valid && d == d0);
-    n_cand += (uint32_t)__popcll(cm[j]);
-    my_win = lane == j ? wm : my_win;
-  }
-  // Lane j < 8 holds the mask of positions base + 256j + 64*wave .. +63.
-  uint64_t* win = ws.win + (size_t)row * ws.n_blk * (kBlk / 64) + blk * (kBlk / 64);
-  if (lane < kPer) win[kBlkThreads / 64 * lane + wave] = my_win;
-  if (n_cand == 0) return;  // wave-uniform
-  uint32_t at = 0;
-  if (lane == 0) at = atomicAdd(&ws.ctr[2 * row], n_cand);
-  at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
-  uint2* cand = ws.cand + (size_t)row * kSelCap;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cm[j] >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)cm[j], 0u));
-    if (((cm[j] >> lane) & 1u) && at + rank < (uint32_t)kSelCap)
-      cand[at + rank] = uint2{key[j], (uint32_t)(base + tid + kBlkThreads * j)};
-    at += (uint32_t)__popcll(cm[j]);
-  }
-}
-
-struct SelShared {
-  uint32_t sure[kSelWords];  // bit p: position p is selected for certain
-  uint32_t eq[kSelWords];    // bit p: the key of p equals the threshold
-  uint32_t ck[kSelCap];      // candidate keys
-  uint32_t cp[kSelCap];      // candidate positions
-  uint32_t hist[kHistWords];
-  uint32_t wave[2 * kTkWaves];
-  uint32_t sel[2];
-  uint32_t small[kWave];     // the few keys left after round 2
-  uint32_t nsmall;
-};
-
-union TopkLds {
-  TopkShared full;
-  SelShared sel;
-};
-
-static_assert(kSelMaxN % kBlk == 0, "the bitmaps cover whole classify blocks");
-
-// select_bin with LDS-only barriers.
+// select_bin with LDS-only barriers (global loads in flight stay in flight).
 template <bool kPadded = true>
 __device__ __forceinline__ uint32_t sel_select_bin(const uint32_t* hist, int nbins,
                                                    uint32_t& remaining, uint32_t* s_sel) {
@@ -604,170 +441,339 @@ __device__ __forceinline__ uint32_t sel_select_bin(const uint32_t* hist, int nbi
   return digit;
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_final_kernel(
+// The few keys (at most 64) left after round 2, gathered in s_small: one wave
+// ranks them and publishes the `remaining`-th largest (thr) and how many keys
+// equal to it are kept (need_eq).
+__device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
+                                           uint32_t remaining, uint32_t* s_sel) {
+  const int lane = threadIdx.x & 63;
+  const bool valid = lane < (int)m;
+  const uint32_t mine = s_small[min(lane, (int)m - 1)];
+  uint32_t gt = 0, ge = 0;
+  for (int j = 0; j < (int)m; ++j) {
+    const uint32_t other = s_small[j];
+    gt += other > mine ? 1u : 0u;
+    ge += other >= mine ? 1u : 0u;
+  }
+  // Fewer than `remaining` keys above it, at least `remaining` at or above it.
+  const bool hit = valid && gt < remaining && remaining <= ge;
+  const uint64_t who = __builtin_amdgcn_ballot_w64(hit);
+  const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
+  const uint32_t t_key = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+  const uint32_t t_gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+  if (lane == 0) {
+    s_sel[0] = t_key;
+    s_sel[1] = remaining - t_gt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Up to 1024 rows: each row is spread over workgroups of 4096 positions in a
+// single launch (topk_split_kernel), and the last workgroup of the row to
+// finish its part completes the row.
+//   1. Every workgroup derives the same cut L from the same 2048 sampled
+//      positions of the row (floor(j n / 2048)): the 22-bit key prefix of the
+//      sample's T_s-th largest key, T_s being the sample's expected count of
+//      keys above the k-th largest plus four standard deviations (and 16).
+//   2. It appends its keys >= L with their positions to the row's list in the
+//      workspace (one device-scope atomic per wave reserves the slots),
+//      fences, and counts itself in the row's arrival counter.
+//   3. The workgroup that arrives last (no waiting: it is simply the one that
+//      sees the final count) loads the list into registers, runs three radix
+//      rounds over it (the last one a direct rank when at most 64 keys are
+//      left), marks the keys above the threshold in a winner bitmap and those
+//      equal to it in a tie bitmap, and writes the ordered output.
+// If the list holds fewer than k keys (the sample misjudged the row), more
+// than it can hold, or the row is longer than the bitmaps, the last workgroup
+// selects the row from scratch (full_row_topk).  The two counters per row must
+// be zero when the launch starts: the indexer clears them in the fused call,
+// a small kernel otherwise.
+constexpr int kMultiRows = 1024;
+constexpr int kSpBlk = 4096;                          // positions per workgroup
+constexpr int kSpPer = kSpBlk / kTkThreads;           // 8 per thread
+constexpr int kSpSample = 2048;                       // sampled positions per row
+constexpr int kSpSamplePer = kSpSample / kTkThreads;  // 4 per thread
+constexpr int kSpCap = 8192;                          // list entries per row
+constexpr int kSpListPer = kSpCap / kTkThreads;       // 16 per thread
+constexpr int kSpMaxN = 131072;                       // longest row the bitmaps cover
+
+struct SplitWs {
+  uint32_t* ctr;  // [rows][2]: arrived workgroups, list length
+  uint2* list;    // [rows][kSpCap]: (key, position) of the keys >= L
+  int n_blk;      // workgroups per row
+};
+
+__host__ inline SplitWs carve_split_ws(void* ws, int rows, int max_end_pos) {
+  SplitWs w;
+  char* p = reinterpret_cast<char*>(ws);
+  w.ctr = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 2 * 4);
+  w.list = reinterpret_cast<uint2*>(p);
+  w.n_blk = max(1, (max_end_pos + kSpBlk - 1) / kSpBlk);
+  return w;
+}
+
+size_t topk_workspace_bytes(int B, int T, int, int) {
+  const size_t rows = (size_t)B * T;
+  if (rows > (size_t)kMultiRows) return 0;
+  return align256(rows * 2 * 4) + rows * kSpCap * 8;
+}
+
+uint32_t* topk_counters(void* workspace, int B, int T) {
+  return B * T > kMultiRows ? nullptr : reinterpret_cast<uint32_t*>(workspace);
+}
+
+struct SplitShared {
+  uint32_t hist[kHistWords];
+  uint32_t hist2[kHistWords];
+  uint32_t sure[kSpMaxN / 32];
+  uint32_t eq[kSpMaxN / 32];
+  int32_t outs[kMaxK];
+  uint32_t wave[2 * kTkWaves];
+  uint32_t sel[2];
+  uint32_t small[kWave];
+  uint32_t nsmall;
+  uint32_t last;
+};
+
+union SplitLds {
+  TopkShared full;
+  SplitShared sp;
+};
+
+// Step 3 for the row's last workgroup: exact selection over the list.
+__device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t* __restrict__ o,
+                             const uint32_t* count, const uint2* __restrict__ list, uint32_t L,
+                             SplitLds& lds) {
+  SplitShared& sh = lds.sp;
+  const int tid = threadIdx.x;
+  const uint32_t M = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool ok = M >= (uint32_t)k && M <= (uint32_t)kSpCap && n <= kSpMaxN;
+  if (!ok) {
+    full_row_topk(x, n, k, o, lds.full);
+    return;
+  }
+  uint32_t ek[kSpListPer], ep[kSpListPer];
+#pragma unroll
+  for (int u = 0; u < kSpListPer; ++u) {
+    const uint2 e = list[min(tid + kTkThreads * u, (int)M - 1)];
+    ek[u] = e.x;
+    ep[u] = min(e.y, (uint32_t)(n - 1));  // a position outside the row cannot occur
+  }
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < kHistWords; i += kTkThreads) {
+    sh.hist[i] = 0;
+    sh.hist2[i] = 0;
+  }
+  for (int i = tid; i < nwords; i += kTkThreads) {
+    sh.sure[i] = 0;
+    sh.eq[i] = 0;
+  }
+  if (tid == 0) sh.nsmall = 0;
+  lds_barrier();
+  // Every list key is >= L; the rounds work on D = key - L, whose range is
+  // known from the largest key, so the first digit spreads the list over
+  // the histogram instead of piling it into the few top-bit bins it shares.
+  uint32_t mx = 0;
+#pragma unroll
+  for (int u = 0; u < kSpListPer; ++u) {
+    ek[u] -= L;
+    if (tid + kTkThreads * u < (int)M) mx = max(mx, ek[u]);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) sh.wave[tid >> 6] = mx;
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) mx = max(mx, sh.wave[w]);
+  const int bits = 32 - __clz((int)mx);           // D < 2^bits
+  const int s1 = bits > 11 ? bits - 11 : 0;       // round 1: D >> s1 (< 2048)
+  const int s2 = s1 > 11 ? s1 - 11 : 0;           // round 2: bits s2.. of D
+  // Round 1.
+#pragma unroll
+  for (int u = 0; u < kSpListPer; ++u)
+    if (tid + kTkThreads * u < (int)M) atomicAdd(&sh.hist[hpad(ek[u] >> s1)], 1u);
+  uint32_t remaining = (uint32_t)k;
+  const uint32_t d1 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
+  const uint32_t m1 = sh.hist[hpad(d1)];  // keys left in the running
+  uint32_t thr, need_eq;                  // threshold as a D value
+  // The keys whose D >> shift equals pre are gathered and ranked directly.
+  auto rank_direct = [&](int shift, uint32_t pre, uint32_t m) {
+#pragma unroll
+    for (int u = 0; u < kSpListPer; ++u)
+      if (tid + kTkThreads * u < (int)M && (ek[u] >> shift) == pre)
+        sh.small[atomicAdd(&sh.nsmall, 1u)] = ek[u];
+    lds_barrier();
+    if (tid < kWave) rank_small(sh.small, m, remaining, sh.sel);
+    lds_barrier();
+    thr = sh.sel[0];
+    need_eq = sh.sel[1];
+  };
+  if (s1 == 0) {
+    thr = d1;
+    need_eq = remaining;
+  } else if (m1 <= (uint32_t)kWave) {
+    rank_direct(s1, d1, m1);
+  } else {
+    // Round 2: bits s2 .. s1-1 of D (with the constant bits above when the
+    // span is shorter than 11).
+#pragma unroll
+    for (int u = 0; u < kSpListPer; ++u)
+      if (tid + kTkThreads * u < (int)M && (ek[u] >> s1) == d1)
+        atomicAdd(&sh.hist2[hpad((ek[u] >> s2) & (kBins - 1))], 1u);
+    const uint32_t d2 = sel_select_bin(sh.hist2, kBins, remaining, sh.sel);
+    const uint32_t m2 = sh.hist2[hpad(d2)];
+    const uint32_t low = (1u << (s1 - s2)) - 1u;
+    const uint32_t p2 = (d1 << (s1 - s2)) | (d2 & low);  // D >> s2 of the survivors
+    if (s2 == 0) {
+      thr = p2;
+      need_eq = remaining;
+    } else if (m2 <= (uint32_t)kWave) {
+      rank_direct(s2, p2, m2);
+    } else {
+      // Round 3: the last s2 (<= 10) bits.
+      for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;
+      lds_barrier();
+#pragma unroll
+      for (int u = 0; u < kSpListPer; ++u)
+        if (tid + kTkThreads * u < (int)M && (ek[u] >> s2) == p2)
+          atomicAdd(&sh.hist[hpad(ek[u] & ((1u << s2) - 1u))], 1u);
+      const uint32_t d3 = sel_select_bin(sh.hist, 1024, remaining, sh.sel);
+      thr = (p2 << s2) | d3;
+      need_eq = remaining;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSpListPer; ++u) {
+    if (tid + kTkThreads * u < (int)M) {
+      const uint32_t p = ep[u];
+      if (ek[u] > thr) atomicOr(&sh.sure[p >> 5], 1u << (p & 31));
+      else if (ek[u] == thr) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
+    }
+  }
+  lds_barrier();
+  // Ordered output: thread t owns bitmap words [w0, w1).
+  const int wpt = (nwords + kTkThreads - 1) / kTkThreads;
+  const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int w = w0; w < w1; ++w) {
+    n_gt += (uint32_t)__popc(sh.sure[w]);
+    n_eq += (uint32_t)__popc(sh.eq[w]);
+  }
+  uint32_t gt, eqb, tot_gt, tot_eq;
+  block_exclusive_scan2(n_gt, n_eq, sh.wave, gt, eqb, tot_gt, tot_eq);
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t sw = sh.sure[w], ew = sh.eq[w];
+    uint32_t bits = sw | ew;
+    while (bits != 0u) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int32_t p = 32 * w + b;
+      if ((sw >> b) & 1u) {
+        const uint32_t at = gt + min(eqb, need_eq);
+        if (at < (uint32_t)k) sh.outs[at] = p;
+        ++gt;
+      } else {
+        if (eqb < need_eq && gt + eqb < (uint32_t)k) sh.outs[gt + eqb] = p;
+        ++eqb;
+      }
+    }
+  }
+  lds_barrier();
+  for (int i = tid; i < k; i += kTkThreads) o[i] = sh.outs[i];
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
-    int k, int32_t* __restrict__ out, TopkWs ws) {
-  __shared__ __align__(16) TopkLds lds;
-  SelShared& sh = lds.sel;
-  const int row = blockIdx.x;
+    int k, int32_t* __restrict__ out, SplitWs ws) {
+  __shared__ __align__(16) SplitLds lds;
+  SplitShared& sh = lds.sp;
+  const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
   const int n = row_len(end_pos, row, T, S_max);
   const float* x = scores + (size_t)row * S_max;
   int32_t* o = out + (size_t)row * k;
-  uint4* gh = reinterpret_cast<uint4*>(ws.hist + (size_t)row * kBins) + threadIdx.x;
-  const int tid = threadIdx.x;
-
+  const int tid = threadIdx.x, lane = tid & 63;
   if (n <= k) {  // every valid position is kept
-    for (int i = tid; i < k; i += kTkThreads) o[i] = i < n ? i : -1;
-    *gh = uint4{0u, 0u, 0u, 0u};
+    if (blk == 0)
+      for (int i = tid; i < k; i += kTkThreads) o[i] = i < n ? i : -1;
     return;
   }
-  bool ok = n <= kSelMaxN;
-  if (ok) {
-    // Everything the selection reads goes out at once: the counters, the
-    // winner bitmap (16-byte pieces, at most 4 per thread) and the first 2048
-    // candidate slots (4 per thread; the count then says which are real).
-    // Loads are clamped; only the stores are conditional.
-    const int nwords = (n + 31) >> 5;
-    const int n16 = (nwords + 3) >> 2;
-    const uint4* wsrc =
-        reinterpret_cast<const uint4*>(ws.win + (size_t)row * ws.n_blk * (kBlk / 64));
-    const uint2* cs = ws.cand + (size_t)row * kSelCap;
-    const uint32_t C = ws.ctr[2 * row], d0 = ws.ctr[2 * row + 1];
-    uint4 q[4];
-    uint2 e[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) q[u] = wsrc[min(tid + kTkThreads * u, n16 - 1)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) e[u] = cs[tid + kTkThreads * u];
-    for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;  // round 2
-    if (tid == 0) sh.nsmall = 0;
-    uint32_t n_win = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + kTkThreads * u;
-      if (i < n16) {
-        reinterpret_cast<uint4*>(sh.sure)[i] = q[u];
-        reinterpret_cast<uint4*>(sh.eq)[i] = uint4{0u, 0u, 0u, 0u};
-        n_win += (uint32_t)(__popc(q[u].x) + __popc(q[u].y) + __popc(q[u].z) + __popc(q[u].w));
-      }
-    }
-    const int nc = (int)min(C, (uint32_t)kSelCap);
-    // A position outside the row can only come from a corrupted list.
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + kTkThreads * u;
-      if (i < nc) {
-        sh.ck[i] = e[u].x;
-        sh.cp[i] = min(e[u].y, (uint32_t)(n - 1));
-      }
-    }
-#pragma unroll 1
-    for (int b0 = 4 * kTkThreads; b0 < nc; b0 += 4 * kTkThreads) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = cs[min(b0 + tid + kTkThreads * u, nc - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = b0 + tid + kTkThreads * u;
-        if (i < nc) {
-          sh.ck[i] = e[u].x;
-          sh.cp[i] = min(e[u].y, (uint32_t)(n - 1));
-        }
-      }
-    }
-    uint32_t S, dummy_ex, dummy_ex2, dummy_tot;
-    block_exclusive_scan2(n_win, 0u, sh.wave, dummy_ex, dummy_ex2, S, dummy_tot);
-    ok = S < (uint32_t)k && (uint32_t)k <= S + C && C <= (uint32_t)kSelCap;
-    if (ok) {
-      // Round 2 over the candidates (their top 11 bits are d0): bits 10..20.
-      uint32_t remaining = (uint32_t)k - S;
-      for (int i = tid; i < nc; i += kTkThreads)
-        atomicAdd(&sh.hist[hpad((sh.ck[i] >> 10) & (kBins - 1))], 1u);
-      const uint32_t d1 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
-      const uint32_t pre = (d0 << 11) | d1;
-      const uint32_t m = sh.hist[hpad(d1)];  // keys left in the running
-      uint32_t thr, need_eq;
-      if (m <= (uint32_t)kWave) {
-        // Few keys left: gather them and let one wave rank them directly.
-        for (int i = tid; i < nc; i += kTkThreads) {
-          const uint32_t key = sh.ck[i];
-          if ((key >> 10) == pre) sh.small[atomicAdd(&sh.nsmall, 1u)] = key;
-        }
-        lds_barrier();
-        if (tid < kWave) {
-          const bool valid = tid < (int)m;
-          const uint32_t mine = sh.small[min(tid, (int)m - 1)];
-          uint32_t gt = 0, ge = 0;
-          for (int j2 = 0; j2 < (int)m; ++j2) {
-            const uint32_t other = sh.small[j2];
-            gt += other > mine ? 1u : 0u;
-            ge += other >= mine ? 1u : 0u;
-          }
-          // The remaining-th largest key: fewer than `remaining` keys above it,
-          // at least `remaining` at or above it.
-          const bool hit = valid && gt < remaining && remaining <= ge;
-          const uint64_t who = __ballot(hit);
-          const int src = (int)__ffsll((long long)who) - 1;
-          const uint32_t t_key = (uint32_t)__builtin_amdgcn_readlane((int)mine, src < 0 ? 0 : src);
-          const uint32_t t_gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, src < 0 ? 0 : src);
-          if (tid == 0) {
-            sh.sel[0] = t_key;
-            sh.sel[1] = remaining - t_gt;
-          }
-        }
-        lds_barrier();
-        thr = sh.sel[0];
-        need_eq = sh.sel[1];
-      } else {
-        // Round 3: the last 10 bits.
-        for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;
-        lds_barrier();
-        for (int i = tid; i < nc; i += kTkThreads) {
-          const uint32_t key = sh.ck[i];
-          atomicAdd(&sh.hist[hpad(key & 1023u)], (key >> 10) == pre ? 1u : 0u);
-        }
-        const uint32_t d2 = sel_select_bin(sh.hist, 1024, remaining, sh.sel);
-        thr = (pre << 10) | d2;
-        need_eq = remaining;
-      }
-      for (int i = tid; i < nc; i += kTkThreads) {
-        const uint32_t key = sh.ck[i], p = sh.cp[i];
-        if (key > thr) atomicOr(&sh.sure[p >> 5], 1u << (p & 31));
-        else if (key == thr) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
-      }
-      lds_barrier();
-      // Ordered output: thread t owns bitmap words [w0, w1).
-      const int wpt = (nwords + kTkThreads - 1) / kTkThreads;
-      const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
-      uint32_t n_gt = 0, n_eq = 0;
-      for (int w = w0; w < w1; ++w) {
-        n_gt += (uint32_t)__popc(sh.sure[w]);
-        n_eq += (uint32_t)__popc(sh.eq[w]);
-      }
-      uint32_t gt, eqb, tot_gt, tot_eq;
-      block_exclusive_scan2(n_gt, n_eq, sh.wave, gt, eqb, tot_gt, tot_eq);
-      for (int w = w0; w < w1; ++w) {
-        const uint32_t s = sh.sure[w], e = sh.eq[w];
-        uint32_t bits = s | e;
-        while (bits != 0u) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1u;
-          const int32_t p = 32 * w + b;
-          if ((s >> b) & 1u) {
-            const uint32_t at = gt + min(eqb, need_eq);
-            if (at < (uint32_t)k) o[at] = p;
-            ++gt;
-          } else {
-            if (eqb < need_eq && gt + eqb < (uint32_t)k) o[gt + eqb] = p;
-            ++eqb;
-          }
-        }
-      }
-    }
+  if (n > ws.n_blk * kSpBlk) {  // longer than max_end_pos promised: not split
+    if (blk == 0) full_row_topk(x, n, k, o, lds.full);
+    return;
   }
-  // A fallback starts after the scan's last barrier: no wave reads the
-  // selection's LDS any more.
-  if (!ok) full_row_topk(x, n, k, o, lds.full);
-  *gh = uint4{0u, 0u, 0u, 0u};  // leave the row's histogram zeroed for the next call
+  const int base = blk * kSpBlk;
+  if (base >= n) return;
+  const int nb = (n + kSpBlk - 1) / kSpBlk;  // workgroups that take part for this row
+
+  // This workgroup's positions base + tid + 512u, and the row's sample.
+  uint32_t kv[kSpPer], ks[kSpSamplePer];
+#pragma unroll
+  for (int u = 0; u < kSpPer; ++u)
+    kv[u] = __float_as_uint(x[min(base + tid + kTkThreads * u, n - 1)]);
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u)
+    ks[u] = __float_as_uint(
+        x[(int)(((uint64_t)(tid + kTkThreads * u) * (uint64_t)n) / (uint64_t)kSpSample)]);
+  for (int i = tid; i < kHistWords; i += kTkThreads) {
+    sh.hist[i] = 0;
+    sh.hist2[i] = 0;
+  }
+  lds_barrier();
+
+  // 1. The cut L.
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u) {
+    ks[u] = score_key(__uint_as_float(ks[u]));
+    atomicAdd(&sh.hist[hpad(ks[u] >> 21)], 1u);
+  }
+  const float mean = (float)k * (float)kSpSample / (float)n;
+  uint32_t rem = min((uint32_t)kSpSample, (uint32_t)(mean + 4.0f * sqrtf(mean) + 16.0f));
+  const uint32_t s0 = sel_select_bin(sh.hist, kBins, rem, sh.sel);
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u)
+    if ((ks[u] >> 21) == s0) atomicAdd(&sh.hist2[hpad((ks[u] >> 10) & (kBins - 1))], 1u);
+  const uint32_t s1 = sel_select_bin(sh.hist2, kBins, rem, sh.sel);
+  const uint32_t L = (s0 << 21) | (s1 << 10);
+
+  // 2. Keys >= L -> the row's list.
+  bool ge[kSpPer];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kSpPer; ++u) {
+    kv[u] = score_key(__uint_as_float(kv[u]));
+    ge[u] = base + tid + kTkThreads * u < n && kv[u] >= L;
+    cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(ge[u]));
+  }
+  uint32_t at = 0;
+  if (lane == 0 && cnt != 0) at = atomicAdd(&ws.ctr[2 * row + 1], cnt);
+  at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
+  uint2* list = ws.list + (size_t)row * kSpCap;
+#pragma unroll
+  for (int u = 0; u < kSpPer; ++u) {
+    const uint64_t mk = __builtin_amdgcn_ballot_w64(ge[u]);
+    const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    if (ge[u] && at + r < (uint32_t)kSpCap)
+      list[at + r] = uint2{kv[u], (uint32_t)(base + tid + kTkThreads * u)};
+    at += (uint32_t)__popcll(mk);
+  }
+
+  // Arrive: the list entries are made visible device-wide first (release).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) sh.last = atomicAdd(&ws.ctr[2 * row], 1u) == (uint32_t)(nb - 1) ? 1u : 0u;
+  __syncthreads();
+  const bool last = sh.last != 0u;
+  __syncthreads();  // read by every wave before the LDS is reused
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other workgroups' entries
+  // 3. This is the row's last workgroup.
+  split_finish(x, n, k, o, ws.ctr + 2 * row + 1, list, L, lds);
+}
+
+__global__ __launch_bounds__(256) void topk_reset_kernel(uint32_t* __restrict__ ctr, int words) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < words) ctr[i] = 0u;
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __restrict__ scores,
@@ -788,29 +794,37 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
 // ---------------------------------------------------------------------------
 // Rows of up to 32768 positions: one workgroup per row with the whole row in
 // registers (64 keys per thread), no workspace.  Wave w takes the 64-position
-// groups w, w+8, w+16, ... (one coalesced 256-byte load each), so a run of
-// high scores is spread over all waves.
-//   1. Keys of all positions; LDS histogram of the top 11 bits; bin d0.
-//   2. One pass over the registers: per group, a ballot of the winners (top
-//      bits above d0) goes to the winner bitmap and the candidates (in bin
-//      d0) are appended to the wave's own region of the candidate list.
-//   3. Round 2 over the candidates, then either a direct rank of the few keys
-//      left (one wave) or round 3; candidates above the threshold join the
-//      winner bitmap, those equal to it go to the tie bitmap.
-//   4. Ordered output from the two bitmaps.
-// If a wave's region overflows (more than 1024 candidates in its groups) the
-// row is redone by full_row_topk.
-constexpr int kLeanMaxN = kChunk;               // 32768
+// groups w, w+8, w+16, ... (one coalesced 256-byte load each).
+//   1. A cut L below the k-th largest key: a histogram of the top 11 key bits
+//      over every position (rows up to 8192) or over every 4th group of each
+//      wave (longer rows, a quarter of the row in blocks of 512), and the bin
+//      where the count from the top reaches k (scaled to the sample, plus a
+//      margin of four standard deviations) gives L.
+//   2. One pass over the registers appends every key >= L with its position
+//      to the wave's own region of an LDS list (typically 1.2-2 k entries).
+//   3. If the list holds at least k keys, the k-th largest is among them: three
+//      radix rounds over the list (the last one a direct rank when few keys
+//      are left) give the threshold and need_eq; list entries above it go to a
+//      winner bitmap, those equal to it to a tie bitmap.
+//   4. Ordered output from the two bitmaps, staged in LDS and stored with
+//      coalesced writes.
+// Too short a list (the sample misjudged the row) or an overflowing region
+// sends the row to full_row_topk.
+constexpr int kLeanMaxN = kChunk;                          // 32768
 constexpr int kLeanGroups = kLeanMaxN / kWave / kTkWaves;  // 64 groups per wave
-constexpr int kLeanRegion = kSelCap / kTkWaves;  // 1024 candidates per wave
+constexpr int kLeanCap = 16384;                            // keys >= L per row
+constexpr int kLeanRegion = kLeanCap / kTkWaves;           // 2048 per wave
+constexpr int kLeanExactN = 8192;                          // histogram every position up to here
+constexpr int kLeanSample = 4;                             // else every 4th group
 
 struct LeanShared {
-  uint32_t hist[kHistWords];   // round 1 (and round 3)
+  uint32_t hist[kHistWords];   // round 0 (the sample), then round 1, then round 3
   uint32_t hist2[kHistWords];  // round 2
+  uint32_t ck[kLeanCap];       // keys >= L; wave w's at [2048 w, 2048 w + ncw[w])
+  uint16_t cp[kLeanCap];       // their positions
   uint32_t sure[kLeanMaxN / 32];
   uint32_t eq[kLeanMaxN / 32];
-  uint32_t ck[kSelCap];        // wave w's candidates at [1024 w, 1024 w + ncw[w])
-  uint32_t cp[kSelCap];
+  int32_t outs[kMaxK];         // the output row, staged
   uint32_t ncw[kTkWaves];
   uint32_t wave[2 * kTkWaves];
   uint32_t sel[2];
@@ -841,7 +855,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
   }
   bool ok = n <= kLeanMaxN;
   if (ok) {
-    // Position of group i of this wave, lane l: 64 (8 i + wave) + l.
+    // Group i of this wave holds positions 64 (8 i + wave) + lane.
     uint32_t key[kLeanGroups];
 #pragma unroll
     for (int i = 0; i < kLeanGroups; ++i)
@@ -850,55 +864,99 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
       sh.hist[i] = 0;
       sh.hist2[i] = 0;
     }
-    for (int i = tid; i < kLeanMaxN / 32; i += kTkThreads) sh.eq[i] = 0;
+    for (int i = tid; i < kLeanMaxN / 32; i += kTkThreads) {
+      sh.sure[i] = 0;
+      sh.eq[i] = 0;
+    }
     if (tid == 0) sh.nsmall = 0;
     lds_barrier();
-    // 1. Round 1 (unpadded histogram).  Every lane counts; the lanes past the
-    // row end loaded position n-1 again, and thread 0 takes those 32768 - n
-    // extra counts back out of that key's bin.
+
+    // 1. Histogram of all positions, or of the sample, and the cut L.
+    const bool exact = n <= kLeanExactN;
 #pragma unroll
     for (int i = 0; i < kLeanGroups; ++i) {
       key[i] = score_key(__uint_as_float(key[i]));
-      atomicAdd(&sh.hist[key[i] >> 21], 1u);
+      const int base = kWave * (kTkWaves * i + wave);
+      if (base < n && (exact || i % kLeanSample == 0))
+        atomicAdd(&sh.hist[hpad(key[i] >> 21)], lane < n - base ? 1u : 0u);
     }
-    if (tid == 0)
-      atomicSub(&sh.hist[score_key(x[n - 1]) >> 21], (uint32_t)(kLeanMaxN - n));
-    uint32_t remaining = (uint32_t)k;
-    const uint32_t d0 = sel_select_bin<false>(sh.hist, kBins, remaining, sh.sel);
-    // 2. Winners and candidates.
-    uint32_t win_lo = 0, win_hi = 0, nc = 0;
+    lds_barrier();
+    if (wave == 0) {
+      // Lane l sums bins 2047-32l down to 2016-32l; the scan gives the count
+      // above each of them.
+      uint32_t c[32], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        c[u] = sh.hist[hpad((uint32_t)(kBins - 1 - (32 * lane + u)))];
+        sum += c[u];
+      }
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t ns = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);  // counted keys
+      uint32_t target = (uint32_t)k;
+      if (!exact) {
+        const float mean = (float)k * (float)ns / (float)n;
+        target = min(ns, (uint32_t)(mean + 4.0f * sqrtf(mean) + 16.0f));
+      }
+      uint32_t above = incl - sum, bin = 0;
+      bool found = false;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (!found && above + c[u] >= target) {
+          bin = (uint32_t)(kBins - 1 - (32 * lane + u));
+          found = true;
+        }
+        above += c[u];
+      }
+      // The highest bin where the count from the top reaches the target.
+      const uint64_t who = __builtin_amdgcn_ballot_w64(found);
+      const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
+      bin = who ? (uint32_t)__builtin_amdgcn_readlane((int)bin, src) : 0u;
+      if (lane == 0) sh.sel[0] = bin << 21;
+    }
+    lds_barrier();
+    const uint32_t L = sh.sel[0];
+    for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;  // round 1
+
+    // 2. Keys >= L -> the wave's region.
+    uint32_t nc = 0;
     const int region = wave * kLeanRegion;
 #pragma unroll
     for (int i = 0; i < kLeanGroups; ++i) {
       const int base = kWave * (kTkWaves * i + wave);
-      const bool in_row = lane < n - base;
-      const uint32_t d = key[i] >> 21;
-      const bool c = in_row && d == d0;
-      const uint64_t wm = __builtin_amdgcn_ballot_w64(in_row && d > d0);
-      const uint64_t cm = __builtin_amdgcn_ballot_w64(c);
-      win_lo = lane == i ? (uint32_t)wm : win_lo;
-      win_hi = lane == i ? (uint32_t)(wm >> 32) : win_hi;
-      const uint32_t at = nc + __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
-      if (c && at < (uint32_t)kLeanRegion) {
-        sh.ck[region + at] = key[i];
-        sh.cp[region + at] = (uint32_t)(base + lane);
+      if (base < n) {
+        const bool ge = lane < n - base && key[i] >= L;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(ge);
+        const uint32_t at = nc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (ge && at < (uint32_t)kLeanRegion) {
+          sh.ck[region + at] = key[i];
+          sh.cp[region + at] = (uint16_t)(base + lane);
+        }
+        nc += (uint32_t)__popcll(m);
       }
-      nc += (uint32_t)__popcll(cm);
     }
-    // Lane i holds the winner mask of group 8 i + wave.
-    reinterpret_cast<uint2*>(sh.sure)[kTkWaves * lane + wave] = uint2{win_lo, win_hi};
     if (lane == 0) sh.ncw[wave] = nc;
     lds_barrier();
-    uint32_t over = 0;
+    uint32_t M = 0, over = 0;
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) over |= sh.ncw[w] > (uint32_t)kLeanRegion ? 1u : 0u;
-    ok = over == 0;
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t c = sh.ncw[w];
+      M += c;
+      over |= c > (uint32_t)kLeanRegion ? 1u : 0u;
+    }
+    ok = over == 0 && M >= (uint32_t)k;
     if (ok) {
-      // 3. Round 2 over each wave's own candidates: bits 10..20.
+      // 3. Exact selection over the list.  Round 1: bits 21..31.
       const int my_nc = (int)nc;
       for (int j = lane; j < my_nc; j += kWave)
-        atomicAdd(&sh.hist2[hpad((sh.ck[region + j] >> 10) & (kBins - 1))], 1u);
+        atomicAdd(&sh.hist[hpad(sh.ck[region + j] >> 21)], 1u);
+      uint32_t remaining = (uint32_t)k;
+      const uint32_t d0 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
+      // Round 2: bits 10..20 of the keys in bin d0.
+      for (int j = lane; j < my_nc; j += kWave) {
+        const uint32_t kk = sh.ck[region + j];
+        if ((kk >> 21) == d0) atomicAdd(&sh.hist2[hpad((kk >> 10) & (kBins - 1))], 1u);
+      }
       const uint32_t d1 = sel_select_bin(sh.hist2, kBins, remaining, sh.sel);
       const uint32_t pre = (d0 << 11) | d1;
       const uint32_t m = sh.hist2[hpad(d1)];  // keys left in the running
@@ -919,7 +977,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
             ge += other >= mine ? 1u : 0u;
           }
           const bool hit = valid && gt < remaining && remaining <= ge;
-          const uint64_t who = __ballot(hit);
+          const uint64_t who = __builtin_amdgcn_ballot_w64(hit);
           const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
           const uint32_t t_key = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
           const uint32_t t_gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
@@ -932,11 +990,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
         thr = sh.sel[0];
         need_eq = sh.sel[1];
       } else {
+        // Round 3: the last 10 bits.
         for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;
         lds_barrier();
         for (int j = lane; j < my_nc; j += kWave) {
           const uint32_t kk = sh.ck[region + j];
-          atomicAdd(&sh.hist[hpad(kk & 1023u)], (kk >> 10) == pre ? 1u : 0u);
+          if ((kk >> 10) == pre) atomicAdd(&sh.hist[hpad(kk & 1023u)], 1u);
         }
         const uint32_t d2 = sel_select_bin(sh.hist, 1024, remaining, sh.sel);
         thr = (pre << 10) | d2;
@@ -967,18 +1026,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
           const int32_t p = 32 * w + b;
           if ((sw >> b) & 1u) {
             const uint32_t at = gt + min(eqb, need_eq);
-            if (at < (uint32_t)k) o[at] = p;
+            if (at < (uint32_t)k) sh.outs[at] = p;
             ++gt;
           } else {
-            if (eqb < need_eq && gt + eqb < (uint32_t)k) o[gt + eqb] = p;
+            if (eqb < need_eq && gt + eqb < (uint32_t)k) sh.outs[gt + eqb] = p;
             ++eqb;
           }
         }
       }
+      lds_barrier();
+      for (int i = tid; i < k; i += kTkThreads) o[i] = sh.outs[i];
     }
   }
   if (!ok) {
-    __syncthreads();  // the overflow check's reads are done before the LDS is reused
+    __syncthreads();  // the list checks' reads are done before the LDS is reused
     full_row_topk(x, n, k, o, lds.full);
   }
 }
@@ -989,28 +1050,27 @@ static_assert(kTkThreads * 2 * 32 == kLeanMaxN, "two bitmap words per thread");
 static_assert(kTkThreads * 4 == kBins, "one 16-byte histogram piece per thread");
 
 int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S_max,
-                int max_end_pos, int k, int32_t* out, void* workspace, hipStream_t stream) {
+                int max_end_pos, int k, int32_t* out, void* workspace, bool counters_clear,
+                hipStream_t stream) {
   const int rows = B * T;
+  if (rows <= kMultiRows) {
+    const SplitWs ws = carve_split_ws(workspace, rows, max_end_pos);
+    if (!counters_clear) {
+      hipLaunchKernelGGL(topk_reset_kernel, dim3((unsigned)((2 * rows + 255) / 256)), dim3(256),
+                         0, stream, ws.ctr, 2 * rows);
+      if (hipGetLastError() != hipSuccess) return -5;
+    }
+    hipLaunchKernelGGL(topk_split_kernel, dim3((unsigned)((long)rows * ws.n_blk)),
+                       dim3(kTkThreads), 0, stream, scores, end_pos, T, S_max, k, out, ws);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   if (max_end_pos <= kLeanMaxN) {
     hipLaunchKernelGGL(topk_lean_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream,
                        scores, end_pos, T, S_max, k, out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
-  if (rows > kMultiRows) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream,
-                       scores, end_pos, T, S_max, k, out);
-    return hipGetLastError() == hipSuccess ? 0 : -5;
-  }
-  const TopkWs ws = carve_topk_ws(workspace, rows, S_max);
-  const dim3 blk_grid((unsigned)((long)rows * ws.n_blk));
-  hipLaunchKernelGGL(topk_hist_kernel, blk_grid, dim3(kBlkThreads), 0, stream, scores, end_pos,
-                     T, S_max, k, ws);
-  if (hipGetLastError() != hipSuccess) return -5;
-  hipLaunchKernelGGL(topk_classify_kernel, blk_grid, dim3(kBlkThreads), 0, stream, scores,
-                     end_pos, T, S_max, k, ws);
-  if (hipGetLastError() != hipSuccess) return -5;
-  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream,
-                     scores, end_pos, T, S_max, k, out, ws);
+  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, scores,
+                     end_pos, T, S_max, k, out);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

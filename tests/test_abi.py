@@ -102,16 +102,14 @@ def test_workspace_sizes_monotone(L):
     a = L.dsa_dense_mla_workspace_size(8, 1, 131072)
     b = L.dsa_dense_mla_workspace_size(8, 1, 262144)
     assert b >= a > 0
-    # rows of up to 32768 positions are selected in one workgroup: no workspace
-    assert L.dsa_topk_workspace_size(64, 1, 32768, 2048) == 0
-    # longer rows: per row a 2048-bin histogram (8 KiB), a bitmap and candidates
-    assert L.dsa_topk_workspace_size(1, 1, 65536, 2048) >= 8192 + 65536 // 8
-    assert L.dsa_topk_workspace_size(4, 2, 65536, 2048) >= 8 * (8192 + 65536 // 8)
-    # too many rows for the histogram path: no workspace either
+    # up to 1024 rows: two counters and a list of 8192 (key, position) pairs per row
+    assert L.dsa_topk_workspace_size(1, 1, 32768, 2048) >= 8192 * 8
+    assert L.dsa_topk_workspace_size(64, 1, 131072, 2048) >= 64 * 8192 * 8
+    # more rows: one workgroup per row, no workspace
     assert L.dsa_topk_workspace_size(2048, 1, 65536, 2048) == 0
+    assert L.dsa_topk_workspace_size(8, 1024, 8192, 2048) == 0
     S = 40000
     assert L.dsa_topk(P, P, 1, 1, S, S, 64, P, None, 1 << 20, None) == -1  # null workspace
     need = L.dsa_topk_workspace_size(1, 1, S, 64)
     assert L.dsa_topk(P, P, 1, 1, S, S, 64, P, P, need - 1, None) == -4
     assert L.dsa_topk(P, P, 1, 1, S, S, 64, P, ctypes.c_void_p(272), need, None) == -3
-    assert L.dsa_topk_workspace_size(1, 1, 100, 64) == 0

@@ -212,6 +212,20 @@ def test_topk_longest_rows():
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("B,T,S,kind", [(1, 1100, 3000, "ties"), (2, 520, 33000, "normal")])
+def test_topk_many_rows(B, T, S, kind):
+    """More than 1024 query rows: one workgroup per row (rows of up to 32768
+    positions held in registers, longer ones chunk by chunk)."""
+    m = dsa()
+    banner(f"topk many rows B={B} T={T} S={S}")
+    k = 2048
+    ep = np.array([S] + [S - 7] * (B - 1), np.int32)
+    scores = inputs.make_scores(B, T, S, kind=kind, seed=T, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_topk_rows_around_bitmap_limit():
     """Rows up to 262144 positions are selected through LDS bitmaps; longer
     ones take the general path.  Both sides of that limit, and a row whose
