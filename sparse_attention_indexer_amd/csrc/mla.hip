@@ -46,16 +46,17 @@ constexpr int kDr = 64;
 constexpr int kNbuf = 2;                     // tiles in the LDS ring
 constexpr int kKvPitch = 1040;               // bytes per latent row in LDS (+16: bank spread)
 constexpr int kMaxSplitRows = 2048;
-constexpr int kLoadsPerTile = 9;             // per wave: 8 latent rows + 1 rope instruction
 
-// Shape of one workgroup: kWaves waves of 16 heads; every wave copies 8 rows
-// of each tile, so a tile has 8*kWaves rows.
-template <int kWaves>
+// Shape of one workgroup: kWaves waves of 16 heads; every wave copies kRw
+// rows of each tile (one instruction per latent row, one per 8 rope rows),
+// so a tile has kRw*kWaves rows.
+template <int kWaves, int kRw>
 struct MlaShape {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kHeadsPerBlock = 16 * kWaves;
   static constexpr int kHeadGroups = kHeads / kHeadsPerBlock;
-  static constexpr int kRt = 8 * kWaves;                  // gathered rows per tile
+  static constexpr int kRt = kRw * kWaves;                // gathered rows per tile
+  static constexpr int kLoadsPerTile = kRw + kRw / 8;     // per wave
   static constexpr int kMt = kRt / 16;                    // 16-row M-tiles per tile
   static constexpr int kKs = kRt / 32;                    // 32-row K-steps of the value product
   static constexpr int kTileKv = kRt * kKvPitch;
@@ -90,16 +91,21 @@ __device__ __forceinline__ float group_sum(float v) {
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
+__device__ __forceinline__ uint32_t pack_half(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
 
-template <bool kDense, int kWaves>
+template <bool kDense, int kWaves, int kRw>
 __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int rows_per_split, int n_splits, int n_items, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
-  using S = MlaShape<kWaves>;
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float4* __restrict__ part_ml) {
+  using S = MlaShape<kWaves, kRw>;
+  constexpr int kLoadsPerTile = S::kLoadsPerTile;
   constexpr int kThreads = S::kThreads, kRt = S::kRt, kMt = S::kMt, kKs = S::kKs;
   constexpr int kTileKv = S::kTileKv, kTileBytes = S::kTileBytes;
   __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
@@ -137,8 +143,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;
 
-  // Row positions of the split -> LDS (-1 = empty slot, also past the end).
-  for (int j = threadIdx.x; j < n_tiles * kRt; j += kThreads) {
+  // Position of split entry j (-1 = empty slot, also past the end).
+  auto entry_pos = [&](int j) {
     int pos = -1;
     if (j < n_rows) {
       if constexpr (kDense) {
@@ -148,8 +154,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
         if (pos < 0 || pos >= S_max) pos = -1;
       }
     }
-    s_pos[j] = pos;
-  }
+    return pos;
+  };
 
   // Query fragment (B operand of S^T = KV . Q^T): head hg*16*kWaves + wave*16 + r16;
   // K-step kk holds dims kk*32 + 8g .. +7 of [q_nope | q_pe].
@@ -163,28 +169,38 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = ldg16(qp + kk * 32 + g * 8);
   }
-  __syncthreads();  // s_pos visible; the query loads have completed
 
   const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
   const uint8_t* pe_b = reinterpret_cast<const uint8_t*>(pe) + (size_t)b * S_max * kDr * 2;
 
-  // This wave copies rows 8*wave .. 8*wave+7 of tile `tile` into ring slot tile % kNbuf.
+  // This wave copies rows kRw*wave .. kRw*wave+kRw-1 of tile `tile` into ring
+  // slot tile % kNbuf.  Empty slots copy row 0 (masked in the softmax).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int tile) {
     uint8_t* base = s_ring + (tile % kNbuf) * kTileBytes;
+    int rpos[kRw];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int trow = 8 * wave + r;
-      const int pos = max(s_pos[tile * kRt + trow], 0);  // empty slots read row 0 (masked later)
-      __builtin_amdgcn_global_load_lds((glb_void*)(kv_b + (size_t)pos * (kDc * 2) + lane * 16),
+    for (int r = 0; r < kRw; ++r) rpos[r] = max(entry_pos(tile * kRt + kRw * wv + r), 0);
+#pragma unroll
+    for (int r = 0; r < kRw; ++r) {
+      const int trow = kRw * wv + r;
+      __builtin_amdgcn_global_load_lds((glb_void*)(kv_b + (size_t)rpos[r] * (kDc * 2) + lane * 16),
                                        (lds_void*)(base + trow * kKvPitch), 16, 0, 0);
     }
-    // Rope parts of the wave's 8 rows: lane L writes chunk L%8 of row L/8, holding
-    // the row's global chunk (L%8) ^ (row & 7).
-    const int trow = 8 * wave + (lane >> 3);
-    const int pos = max(s_pos[tile * kRt + trow], 0);
-    const int chunk = (lane & 7) ^ (trow & 7);
-    __builtin_amdgcn_global_load_lds((glb_void*)(pe_b + (size_t)pos * (kDr * 2) + chunk * 16),
-                                     (lds_void*)(base + kTileKv + 8 * wave * 128), 16, 0, 0);
+    // Rope parts, 8 rows per instruction: lane L writes chunk L%8 of row L/8,
+    // holding the row's global chunk (L%8) ^ (row & 7).
+#pragma unroll
+    for (int q8 = 0; q8 < kRw / 8; ++q8) {
+      const int r = 8 * q8 + (lane >> 3);
+      int pos = rpos[0];
+#pragma unroll
+      for (int rr = 1; rr < kRw; ++rr) pos = r == rr ? rpos[rr] : pos;
+      const int trow = kRw * wv + r;
+      const int chunk = (lane & 7) ^ (trow & 7);
+      __builtin_amdgcn_global_load_lds((glb_void*)(pe_b + (size_t)pos * (kDr * 2) + chunk * 16),
+                                       (lds_void*)(base + kTileKv + (kRw * wv + 8 * q8) * 128),
+                                       16, 0, 0);
+    }
   };
 
   // Running softmax state for head `head` (base 2): reference max, and this
@@ -195,6 +211,10 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < kNbuf - 1 && p < n_tiles; ++p) issue(p);
+  // Row positions of the split -> LDS, for the softmax's validity test (the
+  // copies read their wave-uniform positions straight from memory, so this
+  // overlaps the first gathers; the barrier after the first wait publishes it).
+  for (int j = threadIdx.x; j < n_tiles * kRt; j += kThreads) s_pos[j] = entry_pos(j);
 
 #pragma unroll 1
   for (int tile = 0; tile < n_tiles; ++tile) {
@@ -303,63 +323,91 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     if (lse != nullptr && g == 0)
       lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    float* prow = part_o + ((size_t)X * kHeads + head) * kDc + 4 * g;
+    // Partial output o/l in fp16, scaled by a power of two that puts its
+    // largest element in [2^14, 2^15) (fp16 keeps 11 significant bits at any
+    // magnitude of the cache values), plus (max, sum, 1/scale) in fp32.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float amax = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct)
-      *reinterpret_cast<float4*>(prow + ct * 16) = float4{o[ct][0], o[ct][1], o[ct][2], o[ct][3]};
-    if (g == 0) part_ml[(size_t)X * kHeads + head] = float2{m_run, l_tot};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[ct][i]));
+    amax = group_max(amax) * inv;
+    int e;
+    frexpf(amax, &e);  // amax < 2^e
+    e = min(max(e, -100), 100);
+    const float sc = ldexpf(inv, 15 - e);
+    uint16_t* prow = part_o + ((size_t)X * kHeads + head) * kDc + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct)
+      *reinterpret_cast<uint2*>(prow + ct * 16) =
+          uint2{pack_half(o[ct][0] * sc, o[ct][1] * sc), pack_half(o[ct][2] * sc, o[ct][3] * sc)};
+    if (g == 0) part_ml[(size_t)X * kHeads + head] = float4{m_run, l_tot, ldexpf(1.f, e - 15), 0.f};
   }
 }
 
+__device__ __forceinline__ float half_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
 // Merge the per-split partial outputs of one (row, head) per 128-thread block;
-// each thread owns 4 latent dims.  The split maxima and sums are reduced over
-// the block first (threads stride over the splits); the partial rows are then
-// read eight splits at a time so their loads overlap.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
-                                                          const float2* __restrict__ part_ml,
+// each thread owns 4 latent dims.  The splits are read 32 at a time (their
+// loads all in flight together), with an online maximum across batches, so a
+// decode row with up to 32 splits costs one round trip to memory.
+__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                          const float4* __restrict__ part_ml,
                                                           int n_splits, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  __shared__ float s_red[2][2];
+  constexpr int kBatch = 32;
   const int rh = blockIdx.x;  // row * 128 + head
   const int row = rh / kHeads, head = rh - row * kHeads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float2* ml = part_ml + (size_t)row * n_splits * kHeads + head;
-
-  float m_loc = -INFINITY;
-  for (int s = tid; s < n_splits; s += 128) {
-    const float2 v = ml[(size_t)s * kHeads];
-    m_loc = fmaxf(m_loc, v.y > 0.f ? v.x : -INFINITY);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, off, 64));
-  if (lane == 0) s_red[0][wave] = m_loc;
-  __syncthreads();
-  const float M = fmaxf(s_red[0][0], s_red[0][1]);
-
+  const int tid = threadIdx.x;
+  const float4* ml = part_ml + (size_t)row * n_splits * kHeads + head;
   const int c0 = tid * 4;
-  const float* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
+  const uint16_t* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
   const size_t stride = (size_t)kHeads * kDc;
   float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n_splits; s0 += 8) {
-      float4 a[8];
-      float2 v[8];
+  float L = 0.f, M = -INFINITY;
+  __shared__ float4 s_ml[kBatch];
+  for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+    // The batch's partials and its (max, sum, 1/scale) triples, all in
+    // flight at once; the triples go through LDS to every thread.
+    uint2 a[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = min(s0 + u, n_splits - 1);
-        a[u] = *reinterpret_cast<const float4*>(src + (size_t)s * stride);
-        v[u] = ml[(size_t)s * kHeads];
-      }
+    for (int u = 0; u < kBatch; ++u)
+      a[u] = *reinterpret_cast<const uint2*>(src + (size_t)min(s0 + u, n_splits - 1) * stride);
+    if (tid < kBatch) s_ml[tid] = ml[(size_t)min(s0 + tid, n_splits - 1) * kHeads];
+    __syncthreads();
+    float4 v[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = (s0 + u < n_splits && v[u].y > 0.f) ? exp2f(v[u].x - M) : 0.f;
-        L += v[u].y * w;
-        acc.x += a[u].x * w;
-        acc.y += a[u].y * w;
-        acc.z += a[u].z * w;
-        acc.w += a[u].w * w;
-      }
+    for (int u = 0; u < kBatch; ++u) v[u] = s_ml[u];
+    __syncthreads();  // s_ml is refilled by the next batch
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < n_splits && v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
+    if (mb == -INFINITY) continue;  // nothing kept so far
+    const float alpha = M == -INFINITY ? 0.f : exp2f(M - mb);
+    M = mb;
+    L *= alpha;
+    acc.x *= alpha;
+    acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      // Split weight: its sum times 2^(its max - M); the stored partial is
+      // o/sum times a power-of-two scale whose inverse is v.z.
+      const float w = (s0 + u < n_splits && v[u].y > 0.f) ? v[u].y * exp2f(v[u].x - M) : 0.f;
+      const float ws = w * v[u].z;
+      L += w;
+      acc.x += half_lo(a[u].x) * ws;
+      acc.y += half_hi(a[u].x) * ws;
+      acc.z += half_lo(a[u].y) * ws;
+      acc.w += half_hi(a[u].y) * ws;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -380,9 +428,10 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #define DSA_MLA_SMALL_SPLIT_MIN 64
 #endif
 
-// Few query rows (decode at small batch): 4-wave blocks of 64 heads and short
-// splits, so one query is spread over many CUs.  Otherwise 8-wave blocks of
-// all 128 heads (every gathered row read once) and about one block per CU.
+// Few query rows (decode at small batch): 2-wave blocks of 32 heads (16 rows
+// per wave per tile) and short splits, so one query is spread over many CUs.
+// Otherwise 8-wave blocks of all 128 heads (every gathered row read once) and
+// about one block per CU.
 MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
   if (rows <= DSA_MLA_SMALL_ROWS) {
@@ -390,7 +439,7 @@ MlaPlan sparse_mla_plan(int B, int T, int k) {
     // about 128 items of 2 head groups each.
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)k * rows) rps *= 2;
-    return MlaPlan{rps, (k + rps - 1) / rps, 4};
+    return MlaPlan{rps, (k + rps - 1) / rps, 2};
   }
   long ns = DSA_MLA_TARGET_BLOCKS / rows;
   const long max_ns = (k + 63) / 64;
@@ -414,21 +463,21 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
 size_t mla_workspace_bytes(int B, int T, const MlaPlan& plan) {
   if (plan.n_splits <= 1) return 0;
   const size_t items = (size_t)B * T * plan.n_splits;
-  return items * kHeads * kDc * sizeof(float) + items * kHeads * sizeof(float2);
+  return items * kHeads * kDc * sizeof(uint16_t) + items * kHeads * sizeof(float4);
 }
 
-template <bool kDense, int kWaves>
+template <bool kDense, int kWaves, int kRw>
 static int launch_mla_shape(const void* q_nope, const void* q_pe, const void* kv,
                             const void* pe, const int32_t* idx, const int32_t* end_pos, int T,
                             int S_max, int k, const MlaPlan& plan, int rows, float softmax_scale,
-                            void* out, float* lse, float* part_o, float2* part_ml,
+                            void* out, float* lse, uint16_t* part_o, float4* part_ml,
                             hipStream_t stream) {
-  using S = MlaShape<kWaves>;
+  using S = MlaShape<kWaves, kRw>;
   const int n_items = rows * plan.n_splits;
   const unsigned grid = S::kHeadGroups == 1
                             ? (unsigned)n_items
                             : (unsigned)(((n_items + 7) / 8) * 8 * S::kHeadGroups);
-  hipLaunchKernelGGL((mla_kernel<kDense, kWaves>), dim3(grid), dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL((mla_kernel<kDense, kWaves, kRw>), dim3(grid), dim3(S::kThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(q_nope),
                      reinterpret_cast<const uint16_t*>(q_pe), reinterpret_cast<const uint16_t*>(kv),
                      reinterpret_cast<const uint16_t*>(pe), idx, end_pos, T, S_max, k,
@@ -444,19 +493,19 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
                       void* workspace, hipStream_t stream) {
   const int rows = B * T;
   const int n_items = rows * plan.n_splits;
-  float* part_o = nullptr;
-  float2* part_ml = nullptr;
+  uint16_t* part_o = nullptr;
+  float4* part_ml = nullptr;
   if (plan.n_splits > 1) {
-    part_o = reinterpret_cast<float*>(workspace);
-    part_ml = reinterpret_cast<float2*>(part_o + (size_t)n_items * kHeads * kDc);
+    part_o = reinterpret_cast<uint16_t*>(workspace);
+    part_ml = reinterpret_cast<float4*>(part_o + (size_t)n_items * kHeads * kDc);
   }
   int st;
-  if (plan.waves == 4)
-    st = launch_mla_shape<kDense, 4>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan, rows,
-                                     softmax_scale, out, lse, part_o, part_ml, stream);
+  if (plan.waves == 2)
+    st = launch_mla_shape<kDense, 2, 16>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
+                                         rows, softmax_scale, out, lse, part_o, part_ml, stream);
   else
-    st = launch_mla_shape<kDense, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan, rows,
-                                     softmax_scale, out, lse, part_o, part_ml, stream);
+    st = launch_mla_shape<kDense, 8, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
+                                        rows, softmax_scale, out, lse, part_o, part_ml, stream);
   if (st) return st;
   if (plan.n_splits > 1) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * kHeads)), dim3(128), 0, stream,
