@@ -10,7 +10,7 @@
 namespace dsa {
 
 // With topk_ctr != nullptr the indexer also clears the top-k's per-row
-// counters (2 words per row, see topk_counters), so that launch_topk can run
+// counters (the first 2 of 4 words per row, see topk_counters), so that launch_topk can run
 // with counters_clear = true and skip its own clearing kernel.
 int launch_index_scores(const void* q, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, const int32_t* end_pos, int B, int T, int S_max,

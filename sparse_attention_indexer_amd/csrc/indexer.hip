@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int keys_per_block = kIdxWaves * tiles_per_wave * kIdxTile;
   const int blk_start = blk * keys_per_block;
   if (blk_start > bound) return;
-  if (topk_ctr != nullptr && blk == 0 && threadIdx.x < 2) topk_ctr[2 * row + threadIdx.x] = 0u;
+  if (topk_ctr != nullptr && blk == 0 && threadIdx.x < 2) topk_ctr[4 * row + threadIdx.x] = 0u;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   constexpr int kThreads = S::kThreads, kRt = S::kRt, kMt = S::kMt, kKs = S::kKs;
   constexpr int kTileKv = S::kTileKv, kTileBytes = S::kTileBytes;
   __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
-  __shared__ int s_pos[kMaxSplitRows + 64];
+  __shared__ int s_pos[kNbuf][kRt];  // positions of the tiles in the ring (-1 = empty)
 
   // Block -> (item = row * n_splits + split, head group).  The head groups of
   // one item get ids that are 8 apart, i.e. fall on the same XCD (ids are dealt
@@ -180,7 +180,17 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     uint8_t* base = s_ring + (tile % kNbuf) * kTileBytes;
     int rpos[kRw];
 #pragma unroll
-    for (int r = 0; r < kRw; ++r) rpos[r] = max(entry_pos(tile * kRt + kRw * wv + r), 0);
+    for (int r = 0; r < kRw; ++r) rpos[r] = entry_pos(tile * kRt + kRw * wv + r);
+    // The tile's positions for the softmax's validity test (published by the
+    // barrier that follows the wait for this tile).
+    {
+      int mine = rpos[0];
+#pragma unroll
+      for (int r = 1; r < kRw; ++r) mine = lane == r ? rpos[r] : mine;
+      if (lane < kRw) s_pos[tile % kNbuf][kRw * wv + lane] = mine;
+    }
+#pragma unroll
+    for (int r = 0; r < kRw; ++r) rpos[r] = max(rpos[r], 0);
 #pragma unroll
     for (int r = 0; r < kRw; ++r) {
       const int trow = kRw * wv + r;
@@ -211,10 +221,6 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < kNbuf - 1 && p < n_tiles; ++p) issue(p);
-  // Row positions of the split -> LDS, for the softmax's validity test (the
-  // copies read their wave-uniform positions straight from memory, so this
-  // overlaps the first gathers; the barrier after the first wait publishes it).
-  for (int j = threadIdx.x; j < n_tiles * kRt; j += kThreads) s_pos[j] = entry_pos(j);
 
 #pragma unroll 1
   for (int tile = 0; tile < n_tiles; ++tile) {
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     for (int mt = 0; mt < kMt; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool valid = s_pos[tile * kRt + mt * 16 + 4 * g + i] >= 0;
+        const bool valid = s_pos[tile % kNbuf][mt * 16 + 4 * g + i] >= 0;
         sc[mt][i] = valid ? sc[mt][i] * scale_log2 : -INFINITY;  // now log2-domain score
         mx = fmaxf(mx, sc[mt][i]);
       }
@@ -427,6 +433,9 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #ifndef DSA_MLA_SMALL_SPLIT_MIN
 #define DSA_MLA_SMALL_SPLIT_MIN 64
 #endif
+#ifndef DSA_MLA_DENSE_SMALL_WORK
+#define DSA_MLA_DENSE_SMALL_WORK 65536
+#endif
 
 // Few query rows (decode at small batch): 2-wave blocks of 32 heads (16 rows
 // per wave per tile) and short splits, so one query is spread over many CUs.
@@ -451,12 +460,19 @@ MlaPlan sparse_mla_plan(int B, int T, int k) {
 
 MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   const long rows = (long)B * T;
+  const int ext = max_end_pos > 0 ? max_end_pos : S_max;
   // Rows per split depend only on the allocation sizes, so the workspace
   // computed from S_max always covers the launch.
+  // Few rows over a short context: the small-batch shape, as on the sparse
+  // path; otherwise 8-wave blocks, which gather every row once for all heads.
+  if (rows <= DSA_MLA_SMALL_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK) {
+    int rps = DSA_MLA_SMALL_SPLIT_MIN;
+    while (rps < kMaxSplitRows && (long)rps * 128 < (long)S_max * rows) rps *= 2;
+    return MlaPlan{rps, (ext + rps - 1) / rps, 2};
+  }
   long rps = (long)S_max * rows / DSA_MLA_TARGET_BLOCKS;
   rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
   const int r = round_up((int)rps, 64);
-  const int ext = max_end_pos > 0 ? max_end_pos : S_max;
   return MlaPlan{r, (ext + r - 1) / r, 8};
 }
 

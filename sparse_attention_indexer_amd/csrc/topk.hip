@@ -468,55 +468,63 @@ __device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
 }
 
 // ---------------------------------------------------------------------------
-// Up to 1024 rows: each row is spread over workgroups of 4096 positions in a
-// single launch (topk_split_kernel), and the last workgroup of the row to
-// finish its part completes the row.
+// Up to 1024 rows: each row is spread over workgroups of 512 * kSpPer
+// positions (topk_split_kernel), and a second launch with one workgroup per
+// row finishes it (topk_finish_kernel).
 //   1. Every workgroup derives the same cut L from the same 2048 sampled
 //      positions of the row (floor(j n / 2048)): the 22-bit key prefix of the
 //      sample's T_s-th largest key, T_s being the sample's expected count of
 //      keys above the k-th largest plus four standard deviations (and 16).
 //   2. It appends its keys >= L with their positions to the row's list in the
-//      workspace (one device-scope atomic per wave reserves the slots),
-//      fences, and counts itself in the row's arrival counter.
-//   3. The workgroup that arrives last (no waiting: it is simply the one that
-//      sees the final count) loads the list into registers, runs three radix
-//      rounds over it (the last one a direct rank when at most 64 keys are
-//      left), marks the keys above the threshold in a winner bitmap and those
-//      equal to it in a tie bitmap, and writes the ordered output.
+//      workspace (one device-scope atomic per wave reserves the slots).
+//   3. The finishing workgroup loads the list into registers, runs up to
+//      three radix rounds over it (the last one a direct rank when at most 64
+//      keys are left), marks the keys above the threshold in a winner bitmap
+//      and those equal to it in a tie bitmap, and writes the ordered output.
+// The launch boundary makes the lists visible to the finishing workgroups
+// (one release for the whole grid; fences in every workgroup cost more).  A
+// row that fits one workgroup is selected by it directly from its registers.
 // If the list holds fewer than k keys (the sample misjudged the row), more
-// than it can hold, or the row is longer than the bitmaps, the last workgroup
-// selects the row from scratch (full_row_topk).  The two counters per row must
-// be zero when the launch starts: the indexer clears them in the fused call,
-// a small kernel otherwise.
+// than it can hold, or the row is longer than the bitmaps, the finishing
+// workgroup selects the row from scratch (full_row_topk).  The list counter
+// of each row must be zero when the first launch starts: the indexer clears
+// it in the fused call, a small kernel otherwise.
 constexpr int kMultiRows = 1024;
-constexpr int kSpBlk = 4096;                          // positions per workgroup
-constexpr int kSpPer = kSpBlk / kTkThreads;           // 8 per thread
+constexpr int kSpPerShort = 8;                        // positions per thread, rows <= 32768
+constexpr int kSpPerLong = 32;                        // longer rows (fewer workgroups per row)
 constexpr int kSpSample = 2048;                       // sampled positions per row
 constexpr int kSpSamplePer = kSpSample / kTkThreads;  // 4 per thread
 constexpr int kSpCap = 8192;                          // list entries per row
 constexpr int kSpListPer = kSpCap / kTkThreads;       // 16 per thread
 constexpr int kSpMaxN = 131072;                       // longest row the bitmaps cover
 
+constexpr int kCtrWords = 4;  // per row: unused, list length, cut L, unused
+
 struct SplitWs {
-  uint32_t* ctr;  // [rows][2]: arrived workgroups, list length
+  uint32_t* ctr;  // [rows][kCtrWords]
   uint2* list;    // [rows][kSpCap]: (key, position) of the keys >= L
   int n_blk;      // workgroups per row
 };
+
+__host__ inline int split_per_thread(int max_end_pos) {
+  return max_end_pos <= kChunk ? kSpPerShort : kSpPerLong;
+}
 
 __host__ inline SplitWs carve_split_ws(void* ws, int rows, int max_end_pos) {
   SplitWs w;
   char* p = reinterpret_cast<char*>(ws);
   w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * 2 * 4);
+  p += align256((size_t)rows * kCtrWords * 4);
   w.list = reinterpret_cast<uint2*>(p);
-  w.n_blk = max(1, (max_end_pos + kSpBlk - 1) / kSpBlk);
+  const int blk = kTkThreads * split_per_thread(max_end_pos);
+  w.n_blk = max(1, (max_end_pos + blk - 1) / blk);
   return w;
 }
 
 size_t topk_workspace_bytes(int B, int T, int, int) {
   const size_t rows = (size_t)B * T;
   if (rows > (size_t)kMultiRows) return 0;
-  return align256(rows * 2 * 4) + rows * kSpCap * 8;
+  return align256(rows * kCtrWords * 4) + rows * kSpCap * 8;
 }
 
 uint32_t* topk_counters(void* workspace, int B, int T) {
@@ -533,7 +541,6 @@ struct SplitShared {
   uint32_t sel[2];
   uint32_t small[kWave];
   uint32_t nsmall;
-  uint32_t last;
 };
 
 union SplitLds {
@@ -541,25 +548,13 @@ union SplitLds {
   SplitShared sp;
 };
 
-// Step 3 for the row's last workgroup: exact selection over the list.
-__device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t* __restrict__ o,
-                             const uint32_t* count, const uint2* __restrict__ list, uint32_t L,
-                             SplitLds& lds) {
-  SplitShared& sh = lds.sp;
+// Exact selection of the k largest among M >= k keys, all >= L, held in
+// registers: entry tid + 512u of the set is (ek[u], ep[u]) for every
+// tid + 512u < M.  Writes the row's ordered output.
+template <int kEnt>
+__device__ void split_select(uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt], int M, int n,
+                             int k, int32_t* __restrict__ o, uint32_t L, SplitShared& sh) {
   const int tid = threadIdx.x;
-  const uint32_t M = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool ok = M >= (uint32_t)k && M <= (uint32_t)kSpCap && n <= kSpMaxN;
-  if (!ok) {
-    full_row_topk(x, n, k, o, lds.full);
-    return;
-  }
-  uint32_t ek[kSpListPer], ep[kSpListPer];
-#pragma unroll
-  for (int u = 0; u < kSpListPer; ++u) {
-    const uint2 e = list[min(tid + kTkThreads * u, (int)M - 1)];
-    ek[u] = e.x;
-    ep[u] = min(e.y, (uint32_t)(n - 1));  // a position outside the row cannot occur
-  }
   const int nwords = (n + 31) >> 5;
   for (int i = tid; i < kHistWords; i += kTkThreads) {
     sh.hist[i] = 0;
@@ -571,12 +566,12 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
   }
   if (tid == 0) sh.nsmall = 0;
   lds_barrier();
-  // Every list key is >= L; the rounds work on D = key - L, whose range is
-  // known from the largest key, so the first digit spreads the list over
-  // the histogram instead of piling it into the few top-bit bins it shares.
+  // Every key is >= L; the rounds work on D = key - L, whose range is known
+  // from the largest key, so the first digit spreads the keys over the
+  // histogram instead of piling them into the few top-bit bins they share.
   uint32_t mx = 0;
 #pragma unroll
-  for (int u = 0; u < kSpListPer; ++u) {
+  for (int u = 0; u < kEnt; ++u) {
     ek[u] -= L;
     if (tid + kTkThreads * u < (int)M) mx = max(mx, ek[u]);
   }
@@ -590,7 +585,7 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
   const int s2 = s1 > 11 ? s1 - 11 : 0;           // round 2: bits s2.. of D
   // Round 1.
 #pragma unroll
-  for (int u = 0; u < kSpListPer; ++u)
+  for (int u = 0; u < kEnt; ++u)
     if (tid + kTkThreads * u < (int)M) atomicAdd(&sh.hist[hpad(ek[u] >> s1)], 1u);
   uint32_t remaining = (uint32_t)k;
   const uint32_t d1 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
@@ -599,7 +594,7 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
   // The keys whose D >> shift equals pre are gathered and ranked directly.
   auto rank_direct = [&](int shift, uint32_t pre, uint32_t m) {
 #pragma unroll
-    for (int u = 0; u < kSpListPer; ++u)
+    for (int u = 0; u < kEnt; ++u)
       if (tid + kTkThreads * u < (int)M && (ek[u] >> shift) == pre)
         sh.small[atomicAdd(&sh.nsmall, 1u)] = ek[u];
     lds_barrier();
@@ -617,7 +612,7 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
     // Round 2: bits s2 .. s1-1 of D (with the constant bits above when the
     // span is shorter than 11).
 #pragma unroll
-    for (int u = 0; u < kSpListPer; ++u)
+    for (int u = 0; u < kEnt; ++u)
       if (tid + kTkThreads * u < (int)M && (ek[u] >> s1) == d1)
         atomicAdd(&sh.hist2[hpad((ek[u] >> s2) & (kBins - 1))], 1u);
     const uint32_t d2 = sel_select_bin(sh.hist2, kBins, remaining, sh.sel);
@@ -634,7 +629,7 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
       for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;
       lds_barrier();
 #pragma unroll
-      for (int u = 0; u < kSpListPer; ++u)
+      for (int u = 0; u < kEnt; ++u)
         if (tid + kTkThreads * u < (int)M && (ek[u] >> s2) == p2)
           atomicAdd(&sh.hist[hpad(ek[u] & ((1u << s2) - 1u))], 1u);
       const uint32_t d3 = sel_select_bin(sh.hist, 1024, remaining, sh.sel);
@@ -643,7 +638,7 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
     }
   }
 #pragma unroll
-  for (int u = 0; u < kSpListPer; ++u) {
+  for (int u = 0; u < kEnt; ++u) {
     if (tid + kTkThreads * u < (int)M) {
       const uint32_t p = ep[u];
       if (ek[u] > thr) atomicOr(&sh.sure[p >> 5], 1u << (p & 31));
@@ -682,9 +677,32 @@ __device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t*
   for (int i = tid; i < k; i += kTkThreads) o[i] = sh.outs[i];
 }
 
+// Step 3 for the row's last workgroup: the list -> registers -> selection.
+__device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t* __restrict__ o,
+                             const uint32_t* count, const uint2* __restrict__ list, uint32_t L,
+                             SplitLds& lds) {
+  const int tid = threadIdx.x;
+  const uint32_t M = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool ok = M >= (uint32_t)k && M <= (uint32_t)kSpCap && n <= kSpMaxN;
+  if (!ok) {
+    full_row_topk(x, n, k, o, lds.full);
+    return;
+  }
+  uint32_t ek[kSpListPer], ep[kSpListPer];
+#pragma unroll
+  for (int u = 0; u < kSpListPer; ++u) {
+    const uint2 e = list[min(tid + kTkThreads * u, (int)M - 1)];
+    ek[u] = e.x;
+    ep[u] = min(e.y, (uint32_t)(n - 1));  // a position outside the row cannot occur
+  }
+  split_select<kSpListPer>(ek, ep, (int)M, n, k, o, L, lds.sp);
+}
+
+template <int kSpPer>
 __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int32_t* __restrict__ out, SplitWs ws) {
+  constexpr int kSpBlk = kTkThreads * kSpPer;  // positions per workgroup
   __shared__ __align__(16) SplitLds lds;
   SplitShared& sh = lds.sp;
   const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
@@ -714,6 +732,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
   for (int u = 0; u < kSpSamplePer; ++u)
     ks[u] = __float_as_uint(
         x[(int)(((uint64_t)(tid + kTkThreads * u) * (uint64_t)n) / (uint64_t)kSpSample)]);
+  if (nb == 1) {
+    // The whole row is in this workgroup's registers: select over it directly.
+    uint32_t pv[kSpPer];
+#pragma unroll
+    for (int u = 0; u < kSpPer; ++u) {
+      kv[u] = score_key(__uint_as_float(kv[u]));
+      pv[u] = (uint32_t)(tid + kTkThreads * u);
+    }
+    split_select<kSpPer>(kv, pv, n, n, k, o, 0u, sh);
+    return;
+  }
   for (int i = tid; i < kHistWords; i += kTkThreads) {
     sh.hist[i] = 0;
     sh.hist2[i] = 0;
@@ -745,7 +774,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
     cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(ge[u]));
   }
   uint32_t at = 0;
-  if (lane == 0 && cnt != 0) at = atomicAdd(&ws.ctr[2 * row + 1], cnt);
+  if (lane == 0 && cnt != 0) at = atomicAdd(&ws.ctr[kCtrWords * row + 1], cnt);
+  if (blk == 0 && tid == 0) ws.ctr[kCtrWords * row + 2] = L;
   at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
   uint2* list = ws.list + (size_t)row * kSpCap;
 #pragma unroll
@@ -757,18 +787,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
       list[at + r] = uint2{kv[u], (uint32_t)(base + tid + kTkThreads * u)};
     at += (uint32_t)__popcll(mk);
   }
+}
 
-  // Arrive: the list entries are made visible device-wide first (release).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) sh.last = atomicAdd(&ws.ctr[2 * row], 1u) == (uint32_t)(nb - 1) ? 1u : 0u;
-  __syncthreads();
-  const bool last = sh.last != 0u;
-  __syncthreads();  // read by every wave before the LDS is reused
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other workgroups' entries
-  // 3. This is the row's last workgroup.
-  split_finish(x, n, k, o, ws.ctr + 2 * row + 1, list, L, lds);
+// Second launch: one workgroup per row finishes the rows that the first
+// launch spread over several workgroups.
+template <int kSpPer>
+__global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
+    int k, int32_t* __restrict__ out, SplitWs ws) {
+  constexpr int kSpBlk = kTkThreads * kSpPer;
+  __shared__ __align__(16) SplitLds lds;
+  const int row = blockIdx.x;
+  const int n = row_len(end_pos, row, T, S_max);
+  if (n <= k || n <= kSpBlk || n > ws.n_blk * kSpBlk) return;  // done by the first launch
+  const float* x = scores + (size_t)row * S_max;
+  split_finish(x, n, k, out + (size_t)row * k, ws.ctr + kCtrWords * row + 1,
+               ws.list + (size_t)row * kSpCap, ws.ctr[kCtrWords * row + 2], lds);
 }
 
 __global__ __launch_bounds__(256) void topk_reset_kernel(uint32_t* __restrict__ ctr, int words) {
@@ -1056,12 +1090,24 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
   if (rows <= kMultiRows) {
     const SplitWs ws = carve_split_ws(workspace, rows, max_end_pos);
     if (!counters_clear) {
-      hipLaunchKernelGGL(topk_reset_kernel, dim3((unsigned)((2 * rows + 255) / 256)), dim3(256),
-                         0, stream, ws.ctr, 2 * rows);
+      hipLaunchKernelGGL(topk_reset_kernel, dim3((unsigned)((kCtrWords * rows + 255) / 256)),
+                         dim3(256), 0, stream, ws.ctr, kCtrWords * rows);
       if (hipGetLastError() != hipSuccess) return -5;
     }
-    hipLaunchKernelGGL(topk_split_kernel, dim3((unsigned)((long)rows * ws.n_blk)),
-                       dim3(kTkThreads), 0, stream, scores, end_pos, T, S_max, k, out, ws);
+    const dim3 grid((unsigned)((long)rows * ws.n_blk));
+    if (split_per_thread(max_end_pos) == kSpPerShort) {
+      hipLaunchKernelGGL(topk_split_kernel<kSpPerShort>, grid, dim3(kTkThreads), 0, stream,
+                         scores, end_pos, T, S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL(topk_finish_kernel<kSpPerShort>, dim3((unsigned)rows), dim3(kTkThreads),
+                         0, stream, scores, end_pos, T, S_max, k, out, ws);
+    } else {
+      hipLaunchKernelGGL(topk_split_kernel<kSpPerLong>, grid, dim3(kTkThreads), 0, stream,
+                         scores, end_pos, T, S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL(topk_finish_kernel<kSpPerLong>, dim3((unsigned)rows), dim3(kTkThreads),
+                         0, stream, scores, end_pos, T, S_max, k, out, ws);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   if (max_end_pos <= kLeanMaxN) {
