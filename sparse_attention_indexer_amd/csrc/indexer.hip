@@ -161,11 +161,204 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill form (many queries per sequence): the same products as one GEMM of
+// the queries' [T*64, 128] against the keys' [S, 128]^T.  A 512-thread
+// workgroup takes 16 consecutive queries (two per wave, their 64 heads held
+// as A fragments in registers) and a chunk of up to 1024 keys of the causal
+// range.  Key tiles of 64 rows are copied into LDS (global_load_lds, 16
+// bytes a lane, two tiles in flight) with their 16-byte chunks XOR-swizzled
+// by row so the B-fragment reads hit distinct banks; every B fragment feeds
+// eight MFMAs (2 queries x 4 head tiles).  The ReLU, head weights and the sum
+// over heads stay in registers as in the decode form.
+constexpr int kPfWaves = 8;
+constexpr int kPfQ = 2 * kPfWaves;      // queries per workgroup
+constexpr int kPfTile = 64;             // keys per LDS tile
+constexpr int kPfChunk = 1024;          // keys per workgroup
+
+// Position of 16-byte chunk c of key row r inside the row's LDS copy.
+template <bool kFp8>
+__device__ __forceinline__ int pf_swz(int r, int c) {
+  return kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+}
+
+__device__ __forceinline__ float quad_sum(float v) {  // over lanes l%16 + 16j
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <bool kFp8>
+__global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ end_pos, int T, int S_max, float scale, int n_qblk,
+    int n_chunks, float* __restrict__ out, uint32_t* __restrict__ topk_ctr) {
+  constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
+  constexpr int kChunks = kRowBytes / 16;                  // 16-byte chunks per key row
+  constexpr int kTileBytes = kPfTile * kRowBytes;
+  constexpr int kCopies = kTileBytes / 1024 / kPfWaves;    // 1 KiB copies per wave per tile
+  constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  __shared__ __align__(16) uint8_t s_k[2][kTileBytes];
+
+  const int bid = blockIdx.x;
+  const int chunk = bid % n_chunks, rest = bid / n_chunks;
+  const int qblk = rest % n_qblk, b = rest / n_qblk;
+  const int t0 = qblk * kPfQ;
+  const int ep = min(max(end_pos[b], T), S_max);
+  const int t_last = min(t0 + kPfQ - 1, T - 1);
+  const int bound_max = ep - T + t_last;  // last key any query of the block may see
+  const int s_begin = chunk * kPfChunk;
+  if (s_begin > bound_max) return;
+  const int n_keys = min(kPfChunk, bound_max + 1 - s_begin);
+  const int n_tiles = (n_keys + kPfTile - 1) / kPfTile;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  if (topk_ctr != nullptr && chunk == 0 && tid < 2 * kPfQ && t0 + tid / 2 < T)
+    topk_ctr[4 * ((size_t)b * T + t0 + tid / 2) + (tid & 1)] = 0u;
+
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k) + (size_t)b * S_max * kRowBytes;
+  // Wave w copies rows [kRowsPerCopy*(kCopies*w + j), +kRowsPerCopy) of a tile.
+  auto issue = [&](int tile) {
+    uint8_t* dst = s_k[tile & 1];
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      const int r = kRowsPerCopy * (kCopies * wave + j) + lane / kChunks;
+      const int p = lane % kChunks;
+      const int s = min(s_begin + tile * kPfTile + r, S_max - 1);
+      __builtin_amdgcn_global_load_lds(
+          (glb_void_t*)(kb + (size_t)s * kRowBytes + pf_swz<kFp8>(r, p) * 16),
+          (lds_void_t*)(dst + kRowsPerCopy * (kCopies * wave + j) * kRowBytes), 16, 0, 0);
+    }
+  };
+  issue(0);
+  if (n_tiles > 1) issue(1);
+
+  // A fragments of the wave's two queries: head mt*16 + r16, dims of K-step kk.
+  int tq[2];
+  uint4 qa[2][4][kFp8 ? 2 : 4];
+  float wv[2][4][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    tq[qq] = t0 + 2 * wave + qq;
+    const int tt = min(tq[qq], T - 1);
+    const size_t qrow = (size_t)b * T + tt;
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(q) + qrow * kIdxHeads * kRowBytes;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int u = 0; u < (kFp8 ? 2 : 4); ++u)
+        qa[qq][mt][u] = ldg16(qbase + (mt * 16 + r16) * kRowBytes + g * (kRowBytes / 4) + 16 * u);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = mt * 16 + 4 * g + i;
+        float wh = w[qrow * kIdxHeads + h];
+        if constexpr (kFp8) wh *= q_scale[qrow * kIdxHeads + h];
+        wv[qq][mt][i] = tq[qq] < T ? wh : 0.f;
+      }
+  }
+  const int bound0 = ep - T + tq[0], bound1 = ep - T + tq[1];
+  float* orow0 = out + ((size_t)b * T + min(tq[0], T - 1)) * S_max;
+  float* orow1 = out + ((size_t)b * T + min(tq[1], T - 1)) * S_max;
+  const float* ksrow = kFp8 ? k_scale + (size_t)b * S_max : nullptr;
+
+#pragma unroll 1
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    if (tile + 1 < n_tiles)
+      __builtin_amdgcn_s_waitcnt(wait_vm(kCopies));  // the next tile may stay in flight
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    lds_barrier();
+    const uint8_t* buf = s_k[tile & 1];
+#pragma unroll
+    for (int nt = 0; nt < kPfTile / 16; ++nt) {
+      const int r = nt * 16 + r16;  // key row of this lane's B fragment
+      f32x4 acc[2][4];
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[qq][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!kFp8) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          // Same K order as the A fragments: lane group g, step kk holds dims
+          // 32g + 8kk .. +7, i.e. chunk 4g + kk of the key row.
+          const uint4 bv =
+              *reinterpret_cast<const uint4*>(buf + r * kRowBytes + pf_swz<false>(r, 4 * g + kk) * 16);
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[qq][mt] = mfma_bf16_16x16x32(as_bf16x8(qa[qq][mt][kk]), as_bf16x8(bv), acc[qq][mt]);
+        }
+      } else {
+        const uint4 b0 =
+            *reinterpret_cast<const uint4*>(buf + r * kRowBytes + pf_swz<true>(r, 2 * g) * 16);
+        const uint4 b1 =
+            *reinterpret_cast<const uint4*>(buf + r * kRowBytes + pf_swz<true>(r, 2 * g + 1) * 16);
+        const i32x8 bb = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                               (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const i32x8 a = i32x8{(int)qa[qq][mt][0].x, (int)qa[qq][mt][0].y,
+                                  (int)qa[qq][mt][0].z, (int)qa[qq][mt][0].w,
+                                  (int)qa[qq][mt][1].x, (int)qa[qq][mt][1].y,
+                                  (int)qa[qq][mt][1].z, (int)qa[qq][mt][1].w};
+            acc[qq][mt] = mfma_fp8_16x16x128(a, bb, acc[qq][mt]);
+          }
+      }
+      // Epilogue: ReLU, head weights, sum over the 64 heads.
+      float v[2];
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        float x = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x += wv[qq][mt][i] * fmaxf(acc[qq][mt][i], 0.f);
+        v[qq] = quad_sum(x);
+      }
+      const int s = s_begin + tile * kPfTile + nt * 16 + r16;
+      if (g == 0) {
+        const float ks = kFp8 ? ksrow[min(s, S_max - 1)] : 1.f;
+        if (s <= bound0 && tq[0] < T) orow0[s] = v[0] * ks * scale;
+        if (s <= bound1 && tq[1] < T) orow1[s] = v[1] * ks * scale;
+      }
+    }
+    lds_barrier();  // every wave is done with this buffer before it is refilled
+    if (tile + 2 < n_tiles) issue(tile + 2);
+  }
+}
+
 int launch_index_scores(const void* q, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, const int32_t* end_pos, int B, int T, int S_max,
                         int max_end_pos, float scale, int dtype, float* out, uint32_t* topk_ctr,
                         hipStream_t stream) {
   const long rows = (long)B * T;
+  if (T >= kPfQ) {  // prefill form
+    const int n_qblk = (T + kPfQ - 1) / kPfQ;
+    const int n_chunks = (max_end_pos + kPfChunk - 1) / kPfChunk;
+    const dim3 grid((unsigned)((long)B * n_qblk * n_chunks));
+    if (dtype == 0)
+      hipLaunchKernelGGL(indexer_prefill_kernel<false>, grid, dim3(kPfWaves * 64), 0, stream, q,
+                         q_scale, w, k, k_scale, end_pos, T, S_max, scale, n_qblk, n_chunks, out,
+                         topk_ctr);
+    else
+      hipLaunchKernelGGL(indexer_prefill_kernel<true>, grid, dim3(kPfWaves * 64), 0, stream, q,
+                         q_scale, w, k, k_scale, end_pos, T, S_max, scale, n_qblk, n_chunks, out,
+                         topk_ctr);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   const long tiles_per_row = (max_end_pos + kIdxTile - 1) / kIdxTile;
   // Enough blocks to cover all 256 CUs several times over, but at least one
   // 16-key tile per wave and at most 16.

@@ -149,6 +149,34 @@ def test_indexer_integer_prefill_exact():
     assert np.array_equal(gpu.cpu().numpy()[msk], ref[msk])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_prefill_ragged(dtype):
+    """The prefill form (16 queries per workgroup, 64-key LDS tiles, 1024-key
+    chunks): T not a multiple of 16, a sequence whose queries start deep in
+    its cache, and one starting at position 0."""
+    m = dsa()
+    banner(f"indexer prefill ragged {dtype}")
+    case = inputs.make_case("prefill_ragged", 2, 37, [2300, 37], 2300, dtype=dtype, seed=11,
+                            device=DEV)
+    gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
+                         q_scale=case.q_scale, k_scale=case.k_scale, max_end_pos=2300)
+    h = np_case(case)
+    ref = oracle_scores(case, h)
+    assert_scores_close(gpu.cpu().numpy(), ref, h["end_pos"], case.T, SCORE_TOL[dtype])
+
+
+def test_indexer_prefill_untouched_past_bound():
+    m = dsa()
+    banner("indexer prefill poison past bound")
+    case = inputs.make_case("poison_pf", 1, 40, [1500], 1600, seed=12, device=DEV)
+    out = torch.full((1, 40, 1600), float("nan"), device=DEV)
+    m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale, out=out)
+    msk = valid_mask(case.end_pos.cpu().numpy(), 40, 1600)
+    g = out.cpu().numpy()
+    assert not np.isnan(g[msk]).any()
+    assert np.isnan(g[~msk]).all()
+
+
 def test_indexer_decode_32k_full_row():
     m = dsa()
     banner("indexer decode_32k full row")
@@ -469,3 +497,40 @@ def test_topk_any_workspace_content(fill):
     for rep in range(3):  # the first call may take the slow path, later ones the fast path
         out = m.topk(scores, end_pos, k, max_end_pos=S, workspace=ws)
         assert np.array_equal(out.cpu().numpy(), ref), rep
+
+
+def test_prefill_8192_sampled():
+    """The T=8192 causal prefill at full size, checked on sampled query rows
+    (each recomputed by the oracle as a one-query decode with end_pos = t+1,
+    which has the same causal bound): indexer scores within tolerance, top-k
+    bit-exact on the GPU's own scores, attention within tolerance given the
+    GPU's indices."""
+    m = dsa()
+    banner("prefill T=8192 sampled rows")
+    case = inputs.prefill(8192, device=DEV)
+    T, k = case.T, case.topk
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    out, _, _ = m.forward(case.q, case.w, case.k_cache, case.end_pos, case.q_nope, case.q_pe,
+                       case.kv_cache, case.pe_cache, case.scale, case.softmax_scale, k=k,
+                       max_end_pos=T, topk_out=idx)
+    scores = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
+                            max_end_pos=T)
+    torch.cuda.synchronize()
+    kc = inputs.to_numpy(case.k_cache)
+    kv = inputs.to_numpy(case.kv_cache)
+    pe = inputs.to_numpy(case.pe_cache)
+    for t in (0, 15, 16, 2047, 2048, 5001, 8191):
+        ep = np.array([t + 1], np.int32)
+        qt = inputs.to_numpy(case.q[:, t:t + 1])
+        wt = case.w[:, t:t + 1].cpu().numpy()
+        ref_s = oracle.index_scores(qt, wt, kc, ep, case.scale)[0, 0, :t + 1]
+        g_s = scores[0, t, :t + 1].cpu().numpy()
+        err = np.abs(g_s.astype(np.float64) - ref_s).max() / max(np.abs(ref_s).max(), 1e-30)
+        assert err <= SCORE_TOL["bf16"], (t, float(err))
+        ref_i = oracle.topk(g_s.reshape(1, 1, -1), ep, k)
+        assert np.array_equal(idx[0, t].cpu().numpy(), ref_i[0, 0]), t
+        o_ref, _ = oracle.mla(inputs.to_numpy(case.q_nope[:, t:t + 1]),
+                              inputs.to_numpy(case.q_pe[:, t:t + 1]), kv, pe, ep,
+                              case.softmax_scale, indices=ref_i)
+        o_gpu = out[0, t].float().cpu().numpy()
+        assert np.abs(o_gpu - o_ref[0, 0]).max() < OUT_TOL, t
