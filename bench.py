@@ -51,6 +51,15 @@ def topk_bytes(n_keys_total, rows, k):
     return 4 * n_keys_total + 4 * k * rows
 
 
+# The HIP kernels behind each stage of the decode step (a stage's time is the
+# sum of its kernels' launch durations plus the gaps between them).
+STAGE_KERNELS = {
+    "index_scores": ["indexer_kernel"],
+    "topk": ["topk_reset_kernel", "topk_split_kernel", "topk_finish_kernel"],
+    "sparse_mla": ["mla_kernel", "mla_combine_kernel"],
+}
+
+
 def source_digest(names):
     h = hashlib.sha256()
     for n in names:
@@ -312,7 +321,8 @@ def main(argv=None):
         "config": {"workload": "decode_32k_bf16", "batch": B, "queries_per_seq": T,
                    "context": n, "topk": k, "index_heads": 64, "index_dim": 128,
                    "mla_heads": 128, "latent": 512, "rope": 64, "input_copies": r["copies"]},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "kernels": STAGE_KERNELS[dom],
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kbytes[dom],
                      "avg_launch_ms": round(st[dom], 5)},
