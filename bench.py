@@ -229,6 +229,29 @@ def bench_dense(dsa, torch, case, steps, warmup):
     return Timer(torch).time(step, steps)
 
 
+def bench_projections(dsa, torch, B, T, steps, dev):
+    """Query absorption and output up-projection at B x T query rows: time per
+    call and the HBM roofline of their 16.8 MB per-call weight stream."""
+    from sparse_attention_indexer_amd import inputs
+    qn, wkv, x = inputs.make_proj(B, T, seed=1, device=dev)
+    n = max(1, min(64, math.ceil(ROTATION_BYTES / (wkv.numel() * 2))))
+    w = [wkv] + [wkv.clone() for _ in range(n - 1)]  # rotate the weights through HBM
+    qa = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+    res = {}
+    R = B * T
+    for name, fn, act in (("q_absorb", lambda i: dsa.q_absorb(qn, w[i % n], out=qa), 128 + 512),
+                          ("out_proj", lambda i: dsa.out_proj(x, w[i % n], out=y), 512 + 128)):
+        fn(0)
+        ms = timer.time(fn, steps)
+        nbytes = 128 * 128 * 512 * 2 + R * 128 * act * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"rows": R, "us": round(ms * 1e3, 2), "bytes": nbytes,
+                     "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def break_even(contexts, sparse_ms, dense_ms):
     """Context where sparse and dense times cross (log-linear interpolation), or None."""
     diff = [s - d for s, d in zip(sparse_ms, dense_ms)]
@@ -330,6 +353,8 @@ def main(argv=None):
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
     detail = {"headline": r}
+    # The per-head products on either side of the attention (decode, one row).
+    line["projections"] = bench_projections(dsa, torch, B, T, max(20, args.steps // 4), dev)
 
     # --- sparse vs dense over context (batch 8, fp8 indexer) ---
     if not args.no_sweep:

@@ -175,6 +175,23 @@ int dsa_dense_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
                   int32_t S_max, int32_t max_end_pos, float softmax_scale, void* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Query absorption and output up-projection: the two per-head products on
+ * either side of (c) in the MQA decode branch of "DeepSeek-V3.2-Exp - Apply
+ * sparse mask", with the key/value up-projection wkv_b viewed as
+ * [128 heads, 128 + 128, 512] (its first 128 rows per head act on the query's
+ * non-rope part, its last 128 = v_head_dim rows produce the head's output):
+ *   dsa_q_absorb:  q_abs[b,t,h,c] = sum_{d<128} q_nope[b,t,h,d] * wkv_b[h,d,c]
+ *   dsa_out_proj:  y[b,t,h,d]     = sum_{c<512} x[b,t,h,c] * wkv_b[h,128+d,c]
+ *   q_nope [B,T,128,128] bf16   wkv_b [128,256,512] bf16 (dequantised weight)
+ *   q_abs  [B,T,128,512] bf16   x [B,T,128,512] bf16 (the latent output of (c))
+ *   y      [B,T,128,128] bf16
+ * Arithmetic: bf16 MFMA with fp32 accumulation, rounded to nearest even.
+ * No workspace; 1 <= B*T <= 2^24; pointers 16-byte aligned. */
+int dsa_q_absorb(const void* q_nope, const void* wkv_b, int32_t B, int32_t T, void* q_abs,
+                 hipStream_t stream);
+int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t T, void* y,
+                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,9 +5,11 @@ TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 (``sparse_attention_indexer_amd``) never imports this package, and this
 package never imports the product.
 
-The arithmetic lives in ``dsa_oracle.c`` (plain C, fp64 sums, OpenMP over
-query rows), built with gcc into ``liboracle.so``.  This module only
-marshals numpy arrays.  Conventions for array arguments:
+The arithmetic of the three decode stages lives in ``dsa_oracle.c`` (plain
+C, fp64 sums, OpenMP over query rows), built with gcc into ``liboracle.so``;
+for them this module only marshals numpy arrays.  The two per-head products
+around the attention (``q_absorb``, ``out_proj``) are written out below as
+fp64 numpy contractions.  Conventions for array arguments:
 
 * bf16 tensors are ``np.uint16`` arrays of raw bfloat16 bits;
 * fp8 tensors are ``np.uint8`` arrays of OCP e4m3fn codes;
@@ -169,3 +171,41 @@ def mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, softmax_scale, indices=None, 
                         Dr, k, float(softmax_scale), _ptr(r), nr, _ptr(out), _ptr(lse))
     _check(st, "mla")
     return out, lse
+
+
+# --- query absorption and output up-projection ------------------------------
+# MQA decode branch of "DeepSeek-V3.2-Exp - Apply sparse mask": wkv_b viewed
+# as [heads, qk_nope_head_dim + v_head_dim, kv_lora_rank] = [128, 128+128, 512].
+
+QK_NOPE = 128
+V_HEAD = 128
+
+
+def bf16_to_f64(bits):
+    """bfloat16 bits (uint16) -> float64 (exact: bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _as_f64(a):
+    """bf16 bits (uint16) are decoded; float arrays are taken as they are."""
+    a = np.asarray(a)
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def q_absorb(q_nope, wkv_b):
+    """q_abs[b,t,h,c] = sum_d q_nope[b,t,h,d] * wkv_b[h,d,c] over the first 128 rows of
+    each head's slice (the query absorption).  q_nope [B,T,128,128] and wkv_b
+    [128,256,512] as bf16 bits (or float arrays); returns float64 [B,T,128,512]."""
+    q = _as_f64(q_nope)
+    w = _as_f64(wkv_b)[:, :QK_NOPE, :]
+    return np.einsum("bthd,hdc->bthc", q, w)
+
+
+def out_proj(x, wkv_b):
+    """y[b,t,h,d] = sum_c x[b,t,h,c] * wkv_b[h,128+d,c] over the last v_head_dim rows of
+    each head's slice (the output up-projection).  x [B,T,128,512] and wkv_b as bf16
+    bits (or float arrays); returns float64 [B,T,128,128]."""
+    xx = _as_f64(x)
+    w = _as_f64(wkv_b)[:, -V_HEAD:, :]
+    return np.einsum("bthc,hdc->bthd", xx, w)

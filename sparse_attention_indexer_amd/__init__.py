@@ -66,6 +66,8 @@ def _bind(L):
         "dsa_dense_mla_workspace_size": ([i32, i32, i32], sz),
         "dsa_dense_mla": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp],
                           ctypes.c_int),
+        "dsa_q_absorb": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+        "dsa_out_proj": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -221,6 +223,34 @@ def dense_mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, softmax_scale, max_end_
                              _stream(stream))
     _check(st, "dsa_dense_mla")
     return out, lse
+
+
+def q_absorb(q_nope, wkv_b, out=None, stream=None):
+    """q_abs[b,t,h,:] = q_nope[b,t,h,:] @ wkv_b[h,:128,:]  ([B,T,128,128] -> [B,T,128,512])."""
+    B, T = q_nope.shape[:2]
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.bfloat16, (B, T, 128, 128), dev)
+    _need(wkv_b, "wkv_b", torch.bfloat16, (128, 256, 512), dev)
+    if out is None:
+        out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, 128, 512), dev)
+    _check(lib().dsa_q_absorb(_ptr(q_nope), _ptr(wkv_b), B, T, _ptr(out), _stream(stream)),
+           "dsa_q_absorb")
+    return out
+
+
+def out_proj(x, wkv_b, out=None, stream=None):
+    """y[b,t,h,:] = x[b,t,h,:] @ wkv_b[h,128:,:]^T  ([B,T,128,512] -> [B,T,128,128])."""
+    B, T = x.shape[:2]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (B, T, 128, 512), dev)
+    _need(wkv_b, "wkv_b", torch.bfloat16, (128, 256, 512), dev)
+    if out is None:
+        out = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, 128, 128), dev)
+    _check(lib().dsa_out_proj(_ptr(x), _ptr(wkv_b), B, T, _ptr(out), _stream(stream)),
+           "dsa_out_proj")
+    return out
 
 
 def forward_workspace_size(B, T, S_max, k=MAX_TOPK) -> int:

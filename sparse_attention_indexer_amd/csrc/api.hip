@@ -223,3 +223,19 @@ DSA_EXPORT int dsa_dense_mla(const void* q_nope, const void* q_pe, const void* k
   return dsa::launch_dense_mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, B, T, S_max,
                                max_end_pos, softmax_scale, out, lse, workspace, stream);
 }
+
+DSA_EXPORT int dsa_q_absorb(const void* q_nope, const void* wkv_b, int32_t B, int32_t T,
+                            void* q_abs, hipStream_t stream) {
+  if (!q_nope || !wkv_b || !q_abs) return kErrInvalid;
+  if (B < 1 || T < 1 || (long)B * T > (1L << 24)) return kErrInvalid;
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_abs)) return kErrMisaligned;
+  return dsa::launch_q_absorb(q_nope, wkv_b, B * T, q_abs, stream);
+}
+
+DSA_EXPORT int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t T, void* y,
+                            hipStream_t stream) {
+  if (!x || !wkv_b || !y) return kErrInvalid;
+  if (B < 1 || T < 1 || (long)B * T > (1L << 24)) return kErrInvalid;
+  if (!aligned16(x) || !aligned16(wkv_b) || !aligned16(y)) return kErrMisaligned;
+  return dsa::launch_out_proj(x, wkv_b, B * T, y, stream);
+}

@@ -43,4 +43,9 @@ int launch_dense_mla(const void* q_nope, const void* q_pe, const void* kv, const
                      float softmax_scale, void* out, float* lse, void* workspace,
                      hipStream_t stream);
 
+// Head-batched products around the absorbed attention (rows = B*T).
+int launch_q_absorb(const void* q_nope, const void* wkv_b, int rows, void* q_abs,
+                    hipStream_t stream);
+int launch_out_proj(const void* x, const void* wkv_b, int rows, void* y, hipStream_t stream);
+
 }  // namespace dsa

@@ -249,6 +249,22 @@ def sweep(n: int, seed: int = 5, device="cpu", B: int = 8) -> Case:
 SWEEP_CONTEXTS = (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
 
 
+# --- the products around the attention ----------------------------------------
+
+def make_proj(B: int, T: int, seed: int = 0, device="cpu"):
+    """Inputs of the query absorption and output up-projection: q_nope
+    [B,T,128,128] ~N(0,1), a synthetic wkv_b [128,256,512] ~N(0,1)/sqrt(fan-in)
+    (128 for the key rows, 512 for the value rows, so outputs are O(1)), and a
+    latent attention output x [B,T,128,512] ~N(0,1); all bf16."""
+    g = _gen(seed, device)
+    qn = _normal((B, T, N_HEADS, 128), g, device)
+    wk = _normal((N_HEADS, 128, D_LATENT), g, device) / math.sqrt(128)
+    wv = _normal((N_HEADS, 128, D_LATENT), g, device) / math.sqrt(D_LATENT)
+    x = _normal((B, T, N_HEADS, D_LATENT), g, device)
+    bf = torch.bfloat16
+    return qn.to(bf), torch.cat([wk, wv], 1).to(bf), x.to(bf)
+
+
 # --- standalone inputs for the selection and attention stages ----------------
 
 def make_scores(B: int, T: int, S_max: int, kind: str = "normal", seed: int = 0,

@@ -11,7 +11,9 @@ test_oracle_mutants.py).  What each pin compares against:
 * brute force over every subset of tiny rows (top-k);
 * exact algebraic invariants on integer inputs (sum over heads, linearity in
   the weights, head permutation) and closed forms (one kept row returns that
-  row, a zero query returns the mean of the kept rows).
+  row, a zero query returns the mean of the kept rows);
+* for the absorption and up-projection: selector weights, and the identity
+  between the pages' two attention forms (absorbed decode vs MHA prefill).
 """
 from __future__ import annotations
 
@@ -346,9 +348,62 @@ def check_mla_closed_forms(lib):
     assert np.array_equal(os_, oa) and np.array_equal(ls_, la)
 
 
+# --- query absorption and output up-projection -------------------------------
+
+def check_proj_identity(lib):
+    """Selector weights: the absorption's first 128 rows per head as the identity
+    (q_abs = [q_nope, 0]); the up-projection's rows picking latent dims 256..383."""
+    rng = np.random.default_rng(51)
+    H = 3
+    w = np.zeros((H, 256, 512), np.float32)
+    for d in range(128):
+        w[:, d, d] = 1.0
+        w[:, 128 + d, 256 + d] = 1.0
+    wb = bf16(w)
+    qn = bf16(rng.standard_normal((2, 1, H, 128)))
+    x = bf16(rng.standard_normal((2, 1, H, 512)))
+    qa = oracle.q_absorb(qn, wb)
+    assert np.array_equal(qa[..., :128], bf16_val(qn)) and not qa[..., 128:].any()
+    assert np.array_equal(oracle.out_proj(x, wb), bf16_val(x)[..., 256:384])
+
+
+def check_absorbed_equals_mha(lib):
+    """The decode branch's absorbed form (query absorbed into the latent space,
+    attention over the latent cache, output up-projected) against the prefill
+    branch's MHA form (keys and values up-projected from the latent first, then
+    attention): "DeepSeek-V3.2-Exp - Apply sparse mask" and "Keep top-k positions".
+    Integer query and key-part weights keep the absorbed query exact in bf16, so
+    the two associations agree to fp64 rounding; the MHA side is torch SDPA."""
+    rng = np.random.default_rng(53)
+    H, Dr, n = 4, 8, 12
+    scale = float(np.float32(0.05))  # the oracle takes the scale as an fp32
+    qn = bf16(rng.integers(-2, 3, (1, 1, H, 128)))
+    wk = rng.integers(-1, 2, (H, 128, 512)) * (rng.random((H, 128, 512)) < 0.5)
+    wv = rng.standard_normal((H, 128, 512)) * 0.05
+    wb = bf16(np.concatenate([wk, wv], axis=1))
+    qp = bf16(rng.standard_normal((1, 1, H, Dr)))
+    kv = bf16(rng.standard_normal((1, n, 512)))
+    pe = bf16(rng.standard_normal((1, n, Dr)))
+    # Absorbed: oracle.q_absorb -> oracle.mla over all n rows -> oracle.out_proj.
+    qa = oracle.q_absorb(qn, wb)
+    assert np.abs(qa).max() <= 256 and np.array_equal(qa, np.round(qa))  # exact in bf16
+    x, _ = oracle.mla(bf16(qa), qp, kv, pe, np.array([n], np.int32), scale, lib=lib)
+    y = oracle.out_proj(x, wb)[0, 0]
+    # MHA: per-head keys [k_nope, k_pe] and values from the latent rows.
+    W = torch.from_numpy(bf16_val(wb))                       # [H, 256, 512]
+    C = torch.from_numpy(bf16_val(kv[0]))                    # [n, 512]
+    k_nope = torch.einsum("hdc,tc->htd", W[:, :128], C)      # [H, n, 128]
+    v = torch.einsum("hdc,tc->htd", W[:, 128:], C)           # [H, n, 128]
+    k_pe = torch.from_numpy(bf16_val(pe[0]))[None].expand(H, -1, -1)
+    q = torch.cat([torch.from_numpy(bf16_val(qn[0, 0])), torch.from_numpy(bf16_val(qp[0, 0]))], -1)
+    k = torch.cat([k_nope, k_pe], -1)
+    o = torch.nn.functional.scaled_dot_product_attention(q[:, None], k, v, scale=scale)[:, 0]
+    assert np.allclose(y, o.numpy(), rtol=1e-10, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_indexer_golden, check_fp8_decoding, check_bf16_decoding, check_single_head_matmul,
     check_fp8_single_head_matmul, check_head_sum_and_linearity, check_topk_bruteforce,
     check_topk_stable_sort, check_topk_special_cases, check_mla_golden, check_mla_sdpa,
-    check_mla_closed_forms,
+    check_mla_closed_forms, check_proj_identity, check_absorbed_equals_mha,
 ]

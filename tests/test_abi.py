@@ -113,3 +113,16 @@ def test_workspace_sizes_monotone(L):
     need = L.dsa_topk_workspace_size(1, 1, S, 64)
     assert L.dsa_topk(P, P, 1, 1, S, S, 64, P, P, need - 1, None) == -4
     assert L.dsa_topk(P, P, 1, 1, S, S, 64, P, ctypes.c_void_p(272), need, None) == -3
+
+
+def test_projection_validation(L):
+    """Absorption / up-projection: null, empty and misaligned arguments are
+    rejected on the host."""
+    for fn in (L.dsa_q_absorb, L.dsa_out_proj):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_void_p, ctypes.c_void_p]
+        assert fn(None, P, 1, 1, P, None) == -1
+        assert fn(P, P, 0, 1, P, None) == -1
+        assert fn(P, P, 1, 0, P, None) == -1
+        assert fn(P, ctypes.c_void_p(P.value + 8), 1, 1, P, None) == -3

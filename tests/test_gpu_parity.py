@@ -534,3 +534,22 @@ def test_prefill_8192_sampled():
                               case.softmax_scale, indices=ref_i)
         o_gpu = out[0, t].float().cpu().numpy()
         assert np.abs(o_gpu - o_ref[0, 0]).max() < OUT_TOL, t
+
+
+# --- query absorption and output up-projection --------------------------------------
+
+@pytest.mark.parametrize("B,T", [(1, 1), (3, 37), (1, 300)])
+def test_q_absorb_and_out_proj(B, T):
+    """Both head-batched products against the oracle: one decode row, a ragged
+    batch (two 64-row workgroups, the second partial), and 300 rows."""
+    m = dsa()
+    banner(f"absorb / up-projection B={B} T={T}")
+    qn, wkv, x = inputs.make_proj(B, T, seed=B * 100 + T, device=DEV)
+    qa = m.q_absorb(qn, wkv)
+    y = m.out_proj(x, wkv)
+    ref_qa = oracle.q_absorb(inputs.to_numpy(qn), inputs.to_numpy(wkv))
+    ref_y = oracle.out_proj(inputs.to_numpy(x), inputs.to_numpy(wkv))
+    # bf16 outputs of fp32 sums: within two bf16 half-ulps of the largest value
+    for g, r in ((qa, ref_qa), (y, ref_y)):
+        g = g.float().cpu().numpy().astype(np.float64)
+        assert np.abs(g - r).max() <= 2.0 ** -8 * np.abs(r).max()
