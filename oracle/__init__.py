@@ -9,7 +9,9 @@ The arithmetic of the three decode stages lives in ``dsa_oracle.c`` (plain
 C, fp64 sums, OpenMP over query rows), built with gcc into ``liboracle.so``;
 for them this module only marshals numpy arrays.  The two per-head products
 around the attention (``q_absorb``, ``out_proj``) are written out below as
-fp64 numpy contractions.  Conventions for array arguments:
+fp64 numpy contractions, and so is the weight-free indexer input preparation
+(``indexer_prep``: RoPE, Hadamard rotation, fp8 block quantisation; its code
+decisions are taken in fp32, the precision of the quantiser on the GPU).  Conventions for array arguments:
 
 * bf16 tensors are ``np.uint16`` arrays of raw bfloat16 bits;
 * fp8 tensors are ``np.uint8`` arrays of OCP e4m3fn codes;
@@ -209,3 +211,110 @@ def out_proj(x, wkv_b):
     xx = _as_f64(x)
     w = _as_f64(wkv_b)[:, -V_HEAD:, :]
     return np.einsum("bthc,hdc->bthd", xx, w)
+
+
+# --- indexer input preparation (weight-free part) -----------------------------
+# The Indexer.forward excerpt on "DeepSeek-V3.2-Exp - Keep top-k positions":
+# RoPE on the first 64 dims ("not interleaved"), those dims first, then
+# rotate_activation, then act_quant with 128-element blocks, and the key
+# written to k_cache / k_scale_cache at its position.  The pages name these
+# steps but do not spell them out; the readings taken here:
+#   * RoPE "not interleaved": dim i pairs with dim i + 32 of the 64 rope dims,
+#     (x_i + j x_{i+32}) times (cos_i + j sin_i) for the token's position;
+#   * rotate_activation: the orthonormal Walsh-Hadamard transform of the
+#     128-dim vector (Sylvester order, scaled by 128^-1/2);
+#   * act_quant(x, 128): scale = max|x| / 448 (fp32), codes = x / scale
+#     rounded to the nearest e4m3 value (ties to even), saturating at 448.
+
+ROPE_DIM = 64
+E4M3_MAX = 448.0
+
+
+def rope_halves(x, cos, sin):
+    """x [..., 64] rotated pairwise: (x_i, x_{i+32}) -> (x_i c - x_{i+32} s, x_i s + x_{i+32} c)."""
+    x1, x2 = x[..., :ROPE_DIM // 2], x[..., ROPE_DIM // 2:ROPE_DIM]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], -1)
+
+
+def hadamard128(x, scaled=True):
+    """Walsh-Hadamard transform over the last axis (128), Sylvester order, built from the
+    recursion H_2n = [[H_n, H_n], [H_n, -H_n]] one doubling at a time; times 128^-1/2
+    when ``scaled``."""
+    y = np.array(x, dtype=np.float64)
+    lead = y.shape[:-1]
+    h = 1
+    while h < 128:
+        y = y.reshape(lead + (128 // (2 * h), 2, h))
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2)
+        h *= 2
+    y = y.reshape(lead + (128,))
+    return y / np.sqrt(128.0) if scaled else y
+
+
+def _e4m3_table():
+    """The 127 non-negative finite e4m3fn values, indexed by code 0..126."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+_E4M3 = _e4m3_table()
+
+
+def e4m3_encode(x):
+    """Nearest e4m3fn code (ties to the even code), saturating at +-448; the sign bit
+    follows the sign of x (so -0 and small negatives give 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_E4M3, a, side="left")          # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a >= _E4M3[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    neg = np.signbit(x)
+    return (code | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def act_quant_128(u, post_scale):
+    """Block-128 quantisation of u [..., 128] (u = the rotation before its 128^-1/2
+    factor, post_scale = that factor): the code decision is taken in fp32 --
+    scale_u = fp32(max|u| / 448), codes = e4m3(fp32(u / scale_u)) -- and the
+    returned scale is fp32(scale_u * post_scale), the scale of u * post_scale.
+    An all-zero block gets scale 0 and zero codes."""
+    u32 = np.asarray(u, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(u32), axis=-1)
+    scale_u = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale_u > 0, scale_u, np.float32(1.0))
+    q = (u32 / safe[..., None]).astype(np.float32)
+    codes = e4m3_encode(q)
+    codes = np.where((scale_u > 0)[..., None], codes, np.uint8(0))
+    return codes, (scale_u * np.float32(post_scale)).astype(np.float32)
+
+
+def indexer_prep(q_in, k_in, rope_cos, rope_sin, end_pos, fp8=True):
+    """Weight-free indexer input preparation for B sequences of T new tokens.
+
+    q_in [B,T,64,128] and k_in [B,T,128] as bf16 bits; rope_cos / rope_sin
+    [S_max,32] float32 tables by absolute position; token t of sequence b sits at
+    position end_pos[b] - T + t.  Returns (q, q_scale, k, k_scale, pos): with fp8,
+    q [B,T,64,128] / k [B,T,128] are uint8 e4m3 codes and the scales float32
+    [B,T,64] / [B,T]; otherwise q and k are the rotated values in float64 (no
+    scales).  pos [B,T] are the cache rows the keys go to."""
+    q = _as_f64(q_in).copy()
+    k = _as_f64(k_in).copy()
+    B, T = q.shape[:2]
+    pos = np.asarray(end_pos, np.int64)[:, None] - T + np.arange(T)[None, :]
+    c = np.asarray(rope_cos, np.float32).astype(np.float64)[pos]    # [B,T,32]
+    s = np.asarray(rope_sin, np.float32).astype(np.float64)[pos]
+    q[..., :ROPE_DIM] = rope_halves(q[..., :ROPE_DIM], c[:, :, None, :], s[:, :, None, :])
+    k[..., :ROPE_DIM] = rope_halves(k[..., :ROPE_DIM], c, s)
+    post = float(np.float32(1.0 / np.sqrt(128.0)))
+    if not fp8:
+        return hadamard128(q), None, hadamard128(k), None, pos
+    qc, qs = act_quant_128(hadamard128(q, scaled=False), post)
+    kc, ks = act_quant_128(hadamard128(k, scaled=False), post)
+    return qc, qs, kc, ks, pos

@@ -13,7 +13,11 @@ test_oracle_mutants.py).  What each pin compares against:
   the weights, head permutation) and closed forms (one kept row returns that
   row, a zero query returns the mean of the kept rows);
 * for the absorption and up-projection: selector weights, and the identity
-  between the pages' two attention forms (absorbed decode vs MHA prefill).
+  between the pages' two attention forms (absorbed decode vs MHA prefill);
+* for the indexer input preparation: torch's complex multiply (RoPE), scipy's
+  Hadamard matrix (rotation), torch's float8_e4m3fn cast (encoder), RoPE's
+  relative-position property, the position convention of the k_cache write,
+  and e4m3's half-step error bound (block quantisation).
 """
 from __future__ import annotations
 
@@ -401,9 +405,169 @@ def check_absorbed_equals_mha(lib):
     assert np.allclose(y, o.numpy(), rtol=1e-10, atol=1e-12)
 
 
+# --- indexer input preparation (rope, rotation, fp8 block quantisation) -------
+# These checks take the oracle module as ``mod`` so that planted mistakes in a
+# patched copy of its Python source can be run against them.
+
+def _rope_table(S, rng):
+    """cos/sin tables [S, 32] of angles theta_i * p with random per-dim frequencies."""
+    theta = rng.uniform(0.01, 1.5, 32)
+    ang = np.arange(S)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def check_prep_rope_complex(lib, mod=oracle):
+    """RoPE in the indexer's non-interleaved ("concatenated") layout as a complex
+    multiply: dims i and i+32 of the 64 rope dims are the real and imaginary parts
+    of one complex number, turned by that dim's angle (MaxText PR #2933, "What
+    this PR does", the indexer RoPE note; Indexer.forward excerpt on "Keep top-k
+    positions").  The product is torch's complex multiply by torch.polar."""
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((5, 64))
+    th = rng.uniform(-np.pi, np.pi, (5, 32))
+    z = torch.complex(torch.from_numpy(x[:, :32]), torch.from_numpy(x[:, 32:]))
+    z = z * torch.polar(torch.ones(5, 32, dtype=torch.float64), torch.from_numpy(th))
+    want = torch.cat([z.real, z.imag], -1).numpy()
+    got = mod.rope_halves(x, np.cos(th), np.sin(th))
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+def check_prep_hadamard(lib, mod=oracle):
+    """rotate_activation as the orthonormal Walsh-Hadamard transform: scipy's
+    Sylvester-ordered hadamard(128) over 128**0.5; the unscaled form on the
+    identity is that integer matrix; the scaled transform is its own inverse."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((3, 4, 128))
+    assert np.allclose(mod.hadamard128(x), x @ H.T / np.sqrt(128.0), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(mod.hadamard128(np.eye(128), scaled=False), H.T)
+    assert np.allclose(mod.hadamard128(mod.hadamard128(x)), x, rtol=1e-12, atol=1e-12)
+
+
+def check_prep_e4m3_encoding(lib, mod=oracle):
+    """The e4m3 encoder against torch's float32 -> float8_e4m3fn cast: random values
+    across the whole range, exact ties between neighbouring codes (which go to the
+    even code), subnormals, signed zeros and values past 448 (which saturate)."""
+    rng = np.random.default_rng(63)
+    vals = [rng.uniform(-460, 460, 20000), rng.uniform(-2.0 ** -5, 2.0 ** -5, 20000),
+            rng.standard_normal(20000) * 10]
+    grid = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    grid = np.unique(grid[np.isfinite(grid)])
+    vals.append((grid[1:] + grid[:-1]) / 2)                  # midpoints: ties
+    vals.append(grid)
+    vals.append([448.0, 449.0, 464.0, -464.0, 0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -11])
+    x = np.concatenate([np.asarray(v, np.float64) for v in vals]).astype(np.float32)
+    x = x[np.abs(x) <= 464]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mod.e4m3_encode(x), want)
+    # Past 464 torch's cast gives NaN; the quantiser never sees such values (its
+    # scale puts the block maximum at 448) and the encoder saturates them instead.
+    big = np.array([464.5, 1e6, -479.9, -1e30], np.float32)
+    assert mod.e4m3_encode(big).tolist() == [0x7E, 0x7E, 0xFE, 0xFE]
+
+
+def check_prep_act_quant(lib, mod=oracle):
+    """Block-128 quantisation: the scale is the block's max |u| over 448 (times the
+    post factor), the largest element maps to the top code, every element comes back
+    within half an e4m3 step (2^-4 relative for normal codes, 2^-10 absolute below),
+    signs are kept, and an all-zero block has scale 0 and zero codes."""
+    rng = np.random.default_rng(64)
+    u = (rng.standard_normal((6, 128)) * rng.uniform(0.01, 100, (6, 1))).astype(np.float32)
+    u[1, 7] = -50 * np.abs(u[1]).max()                       # a block led by a negative value
+    u[2, :] = 0.0
+    u[3, :] = np.float32(3.0)
+    codes, scale = mod.act_quant_128(u, 0.25)
+    amax = np.abs(u).max(-1)
+    su = (amax / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(scale, (su * np.float32(0.25)).astype(np.float32))
+    assert scale[2] == 0 and not codes[2].any()
+    dq = pinlib_fp8_values(codes)
+    nz = su > 0
+    x = u[nz] / su[nz, None].astype(np.float64)
+    err = np.abs(dq[nz] - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6))
+    assert np.all(np.abs(dq[nz]).max(-1) == 448.0)
+    assert np.all((codes[nz] >= 0x80) == (u[nz] < 0) | ((u[nz] == 0) & np.signbit(u[nz])))
+
+
+def pinlib_fp8_values(codes):
+    """e4m3fn codes decoded by torch."""
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(
+        torch.float8_e4m3fn).double().numpy()
+
+
+def check_prep_positions(lib, mod=oracle):
+    """The T new tokens of a sequence take positions start_pos..end_pos-1 with
+    end_pos = start_pos + T (the k_cache slice write and end_pos of the
+    Indexer.forward excerpt): with cos = p, sin = 0 the inverse rotation of the
+    prepared vectors gives back the rope dims times the token's position and the
+    other 64 dims untouched."""
+    rng = np.random.default_rng(65)
+    S, T = 8, 2
+    cos = np.repeat(np.arange(S, dtype=np.float32)[:, None], 32, 1)
+    sin = np.zeros((S, 32), np.float32)
+    qb = bf16(rng.standard_normal((1, T, 2, 128)))
+    kb = bf16(rng.standard_normal((1, T, 128)))
+    q, _, k, _, pos = mod.indexer_prep(qb, kb, cos, sin, np.array([5], np.int32), fp8=False)
+    assert pos.tolist() == [[3, 4]]
+    q0, k0 = bf16_val(qb), bf16_val(kb)
+    qi, ki = mod.hadamard128(q), mod.hadamard128(k)
+    for t, p in enumerate((3, 4)):
+        assert np.allclose(qi[0, t, :, :64], q0[0, t, :, :64] * p, atol=1e-12)
+        assert np.allclose(qi[0, t, :, 64:], q0[0, t, :, 64:], atol=1e-12)
+        assert np.allclose(ki[0, t, :64], k0[0, t, :64] * p, atol=1e-12)
+        assert np.allclose(ki[0, t, 64:], k0[0, t, 64:], atol=1e-12)
+
+
+def check_prep_relative_position(lib, mod=oracle):
+    """With tables of angles theta_i * p, the prepared query of a token at position
+    p1 dotted with the prepared key of a token at p2 depends on p1 - p2 only (RoPE's
+    relative-position property; the rotation is orthonormal so it keeps dot
+    products), and both the query and the key are rotated."""
+    rng = np.random.default_rng(66)
+    cos, sin = _rope_table(300, rng)
+    qb = bf16(rng.standard_normal((1, 1, 3, 128)))
+    kb = bf16(rng.standard_normal((1, 1, 128)))
+
+    def dot(p1, p2):
+        q, _, _, _, _ = mod.indexer_prep(qb, kb, cos, sin, np.array([p1 + 1], np.int32), fp8=False)
+        _, _, k, _, _ = mod.indexer_prep(qb, kb, cos, sin, np.array([p2 + 1], np.int32), fp8=False)
+        return q[0, 0] @ k[0, 0]
+
+    # the tables are fp32, so equality holds to their rounding only
+    a, b, c = dot(10, 3), dot(207, 200), dot(3, 10)
+    assert np.allclose(a, b, rtol=1e-5, atol=1e-5) and not np.allclose(a, c, rtol=1e-3)
+    assert np.allclose(dot(0, 0), bf16_val(qb)[0, 0] @ bf16_val(kb)[0, 0], rtol=1e-12)
+
+
+def check_prep_quantised_pipeline(lib, mod=oracle):
+    """End to end with the identity rotation of RoPE (cos 1, sin 0): the prepared
+    fp8 codes times their scales give scipy's hadamard(128) @ x / 128**0.5 within
+    half an e4m3 step of the block scale, for the query heads and the key."""
+    import scipy.linalg
+    rng = np.random.default_rng(67)
+    H = scipy.linalg.hadamard(128).astype(np.float64) / np.sqrt(128.0)
+    cos, sin = np.ones((4, 32), np.float32), np.zeros((4, 32), np.float32)
+    qb = bf16(rng.standard_normal((2, 1, 5, 128)))
+    kb = bf16(rng.standard_normal((2, 1, 128)))
+    qc, qs, kc, ks, _ = mod.indexer_prep(qb, kb, cos, sin, np.array([1, 4], np.int32))
+    for codes, sc, x in ((qc, qs, bf16_val(qb)), (kc, ks, bf16_val(kb))):
+        want = x @ H.T
+        got = pinlib_fp8_values(codes) * sc[..., None].astype(np.float64)
+        step = np.abs(want).max(-1, keepdims=True) * 2.0 ** -4
+        assert np.all(np.abs(got - want) <= step * (1 + 1e-5))
+        assert np.allclose(sc, np.abs(want).max(-1) / 448.0, rtol=1e-6)
+
+
 ALL_CHECKS = [
     check_indexer_golden, check_fp8_decoding, check_bf16_decoding, check_single_head_matmul,
     check_fp8_single_head_matmul, check_head_sum_and_linearity, check_topk_bruteforce,
     check_topk_stable_sort, check_topk_special_cases, check_mla_golden, check_mla_sdpa,
     check_mla_closed_forms, check_proj_identity, check_absorbed_equals_mha,
 ]
+PREP_CHECKS = [
+    check_prep_rope_complex, check_prep_hadamard, check_prep_e4m3_encoding, check_prep_act_quant,
+    check_prep_positions, check_prep_relative_position, check_prep_quantised_pipeline,
+]
+ALL_CHECKS += PREP_CHECKS

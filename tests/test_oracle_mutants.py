@@ -71,3 +71,44 @@ def test_mutant_is_caught(name, old, new, tmp_path):
         except (AssertionError, ValueError) as e:
             failures.append(check.__name__)
     assert failures, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the Python part of the oracle (indexer input preparation):
+# (name, text in oracle/__init__.py, replacement).  Each patched copy is loaded as
+# a module of its own and run against the preparation pins.
+PY_SRC = os.path.join(pinlib.ROOT, "oracle", "__init__.py")
+PY_MUTANTS = [
+    ("rope_sign", "x1 * cos - x2 * sin", "x1 * cos + x2 * sin"),
+    ("rope_interleaved", "x1, x2 = x[..., :ROPE_DIM // 2], x[..., ROPE_DIM // 2:ROPE_DIM]",
+     "x1, x2 = x[..., 0:ROPE_DIM:2], x[..., 1:ROPE_DIM:2]"),
+    ("rope_on_last_dims", "q[..., :ROPE_DIM] = rope_halves(q[..., :ROPE_DIM],",
+     "q[..., -ROPE_DIM:] = rope_halves(q[..., -ROPE_DIM:],"),
+    ("key_not_roped", "    k[..., :ROPE_DIM] = rope_halves(k[..., :ROPE_DIM], c, s)\n", ""),
+    ("position_off_by_one", "- T + np.arange(T)[None, :]", "- T + 1 + np.arange(T)[None, :]"),
+    ("hadamard_unscaled", "return y / np.sqrt(128.0) if scaled else y", "return y"),
+    ("hadamard_sign", "np.stack([a + b, a - b], axis=-2)", "np.stack([a + b, b - a], axis=-2)"),
+    ("e4m3_ties_to_odd", "(hi % 2 == 0)", "(hi % 2 == 1)"),
+    ("e4m3_max_240", "E4M3_MAX = 448.0", "E4M3_MAX = 240.0"),
+    ("e4m3_subnormal_step", "m * 2.0 ** -9 if e == 0", "m * 2.0 ** -10 if e == 0"),
+    ("amax_signed", "np.max(np.abs(u32), axis=-1)", "np.max(u32, axis=-1)"),
+    ("post_scale_dropped", "(scale_u * np.float32(post_scale))", "(scale_u)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(name, old, new, tmp_path):
+    import importlib.util
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"oracle_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"oracle_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    failures = []
+    for check in pinlib.PREP_CHECKS:
+        try:
+            check(None, mod=mod)
+        except (AssertionError, ValueError, IndexError) as e:
+            failures.append(check.__name__)
+    assert failures, f"mutant {name} passed every pin"
