@@ -252,6 +252,49 @@ def bench_projections(dsa, torch, B, T, steps, dev):
     return res
 
 
+def prep_bytes(tokens, fp8=True):
+    """Algorithmic HBM bytes of the indexer input preparation for `tokens` new
+    tokens: per token 64 query heads + 1 key of 128 bf16 in, one 128-byte cos and
+    sin table row in, and 65 rotated vectors out (fp8 codes + one fp32 scale
+    each, or bf16)."""
+    out = 65 * (128 + 4) if fp8 else 65 * 256
+    return tokens * (65 * 256 + 2 * 128 + out)
+
+
+def bench_prep(dsa, torch, steps, dev, shapes=((1, 1), (64, 1), (1, 8192))):
+    """Indexer input preparation (fp8 cache) at decode batch 1, decode batch 64
+    and one 8192-token prefill chunk: time per call and its HBM roofline."""
+    from sparse_attention_indexer_amd import inputs
+    timer = Timer(torch)
+    res = {}
+    for B, T in shapes:
+        S_max = max(T, 4096)
+        per = prep_bytes(B * T)
+        n = max(2, min(16, math.ceil(ROTATION_BYTES / 2 / per)))   # copies rotated through HBM
+        sets = []
+        for i in range(n):
+            q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, [S_max] * B, S_max, seed=90 + i,
+                                                        device=dev)
+            kc = torch.zeros((B, S_max, 128), dtype=torch.float8_e4m3fn, device=dev)
+            ks = torch.zeros((B, S_max), dtype=torch.float32, device=dev)
+            qo = torch.empty((B, T, 64, 128), dtype=torch.float8_e4m3fn, device=dev)
+            qs = torch.empty((B, T, 64), dtype=torch.float32, device=dev)
+            sets.append((q_in, k_in, cos, sin, ep, kc, ks, qo, qs))
+
+        def fn(i):
+            q_in, k_in, cos, sin, ep, kc, ks, qo, qs = sets[i % n]
+            dsa.indexer_prep(q_in, k_in, cos, sin, ep, kc, ks, q_out=qo, q_scale=qs)
+        fn(0)
+        ms = timer.time(fn, steps)
+        gbs = per / (ms * 1e-3) / 1e9
+        res[f"b{B}_t{T}"] = {"tokens": B * T, "us": round(ms * 1e3, 2), "bytes": per,
+                             "achieved_gbs": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def break_even(contexts, sparse_ms, dense_ms):
     """Context where sparse and dense times cross (log-linear interpolation), or None."""
     diff = [s - d for s, d in zip(sparse_ms, dense_ms)]
@@ -355,6 +398,8 @@ def main(argv=None):
     detail = {"headline": r}
     # The per-head products on either side of the attention (decode, one row).
     line["projections"] = bench_projections(dsa, torch, B, T, max(20, args.steps // 4), dev)
+    # The weight-free indexer input preparation (RoPE, rotation, fp8 quantisation).
+    line["indexer_prep"] = bench_prep(dsa, torch, max(20, args.steps // 4), dev)
 
     # --- sparse vs dense over context (batch 8, fp8 indexer) ---
     if not args.no_sweep:

@@ -192,6 +192,36 @@ int dsa_q_absorb(const void* q_nope, const void* wkv_b, int32_t B, int32_t T, vo
 int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t T, void* y,
                  hipStream_t stream);
 
+/* Indexer input preparation - the weight-free steps of the Indexer.forward
+ * excerpt on "DeepSeek-V3.2-Exp - Keep top-k positions" between the
+ * projections (wq_b, wk + k_norm) and fp8_index: RoPE on the first 64 dims of
+ * every query head and of the key, in the concatenated layout that "MaxText
+ * PR #2933" gives for the indexer (dim i and dim i+32, i < 32, are the two
+ * parts of one pair turned by the angle of frequency i); the rotation
+ * rotate_activation, read as the orthonormal Walsh-Hadamard transform
+ * (Sylvester order, 128^-1/2); then, for fp8, act_quant with 128-element
+ * blocks (scale = max|x| / 448, codes = nearest e4m3 of x / scale, ties to
+ * even) and, for either dtype, the key written at its position.
+ *   q_in  [B,T,64,128] bf16 (rope dims first)   k_in [B,T,128] bf16
+ *   rope_cos, rope_sin [S_max,32] fp32: cos and sin of the pair angles at each
+ *         absolute position; token t of sequence b uses row end_pos[b]-T+t
+ *   end_pos [B] int32 (device), T <= end_pos[b] <= S_max
+ *   dtype DSA_FP8_E4M3: q_out [B,T,64,128] fp8 codes, q_scale [B,T,64] fp32,
+ *         k_cache [B,S_max,128] fp8 and k_scale [B,S_max] fp32 get row
+ *         end_pos[b]-T+t of each token -- the inputs of dsa_index_scores.
+ *   dtype DSA_BF16: q_out / k_cache get the rotated values rounded to bf16;
+ *         q_scale and k_scale are ignored (may be NULL).
+ * Other cache rows are not touched.  Arithmetic in fp32 (the rotation's sums
+ * unscaled, the 128^-1/2 folded into the scale), IEEE divisions for the
+ * scale and the codes; an all-zero block gets scale 0 and zero codes.  A
+ * token whose position falls outside [0, S_max) (end_pos out of contract)
+ * writes no key.  No workspace; 1 <= B*T <= 2^24; tensors 16-byte aligned,
+ * scales 4-byte aligned. */
+int dsa_indexer_prep(const void* q_in, const void* k_in, const float* rope_cos,
+                     const float* rope_sin, const int32_t* end_pos, int32_t B, int32_t T,
+                     int32_t S_max, int32_t dtype, void* q_out, float* q_scale, void* k_cache,
+                     float* k_scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

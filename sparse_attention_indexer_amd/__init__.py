@@ -68,6 +68,8 @@ def _bind(L):
                           ctypes.c_int),
         "dsa_q_absorb": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "dsa_out_proj": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+        "dsa_indexer_prep": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+                             ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -251,6 +253,42 @@ def out_proj(x, wkv_b, out=None, stream=None):
     _check(lib().dsa_out_proj(_ptr(x), _ptr(wkv_b), B, T, _ptr(out), _stream(stream)),
            "dsa_out_proj")
     return out
+
+
+def indexer_prep(q_in, k_in, rope_cos, rope_sin, end_pos, k_cache, k_scale=None, q_out=None,
+                 q_scale=None, stream=None):
+    """RoPE (rope dims first, non-interleaved), Hadamard rotation and, for an fp8
+    cache, block-128 e4m3 quantisation of the indexer's query heads
+    [B,T,64,128] and keys [B,T,128]; the keys go into k_cache [B,S_max,128]
+    (and k_scale [B,S_max]) at rows end_pos[b]-T+t.  The cache's dtype picks
+    the mode (bfloat16 or float8_e4m3fn).  Returns (q_out, q_scale); q_scale
+    is None for bf16."""
+    B, T = q_in.shape[:2]
+    dev = q_in.device
+    S_max = k_cache.shape[1] if k_cache.dim() == 3 else -1
+    _need(q_in, "q_in", torch.bfloat16, (B, T, 64, 128), dev)
+    _need(k_in, "k_in", torch.bfloat16, (B, T, 128), dev)
+    _need(rope_cos, "rope_cos", torch.float32, (S_max, 32), dev)
+    _need(rope_sin, "rope_sin", torch.float32, (S_max, 32), dev)
+    _need(end_pos, "end_pos", torch.int32, (B,), dev)
+    _need(k_cache, "k_cache", (torch.bfloat16, torch.float8_e4m3fn), (B, S_max, 128), dev)
+    fp8 = k_cache.dtype == torch.float8_e4m3fn
+    if q_out is None:
+        q_out = torch.empty((B, T, 64, 128), dtype=k_cache.dtype, device=dev)
+    _need(q_out, "q_out", k_cache.dtype, (B, T, 64, 128), dev)
+    if fp8:
+        if q_scale is None:
+            q_scale = torch.empty((B, T, 64), dtype=torch.float32, device=dev)
+        _need(q_scale, "q_scale", torch.float32, (B, T, 64), dev)
+        _need(k_scale, "k_scale", torch.float32, (B, S_max), dev)
+    else:
+        q_scale = None
+    _check(lib().dsa_indexer_prep(_ptr(q_in), _ptr(k_in), _ptr(rope_cos), _ptr(rope_sin),
+                                  _ptr(end_pos), B, T, S_max, 1 if fp8 else 0, _ptr(q_out),
+                                  _ptr(q_scale), _ptr(k_cache),
+                                  _ptr(k_scale) if fp8 else None, _stream(stream)),
+           "dsa_indexer_prep")
+    return q_out, q_scale
 
 
 def forward_workspace_size(B, T, S_max, k=MAX_TOPK) -> int:

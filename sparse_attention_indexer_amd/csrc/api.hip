@@ -239,3 +239,22 @@ DSA_EXPORT int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t
   if (!aligned16(x) || !aligned16(wkv_b) || !aligned16(y)) return kErrMisaligned;
   return dsa::launch_out_proj(x, wkv_b, B * T, y, stream);
 }
+
+DSA_EXPORT int dsa_indexer_prep(const void* q_in, const void* k_in, const float* rope_cos,
+                                const float* rope_sin, const int32_t* end_pos, int32_t B,
+                                int32_t T, int32_t S_max, int32_t dtype, void* q_out,
+                                float* q_scale, void* k_cache, float* k_scale,
+                                hipStream_t stream) {
+  if (!q_in || !k_in || !rope_cos || !rope_sin || !end_pos || !q_out || !k_cache)
+    return kErrInvalid;
+  if (B < 1 || T < 1 || S_max < T || (long)B * T > (1L << 24)) return kErrInvalid;
+  if (dtype != 0 && dtype != 1) return kErrUnsupported;
+  if (dtype == 1 && (!q_scale || !k_scale)) return kErrInvalid;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(rope_cos) || !aligned16(rope_sin) ||
+      !aligned4(end_pos) || !aligned16(q_out) || !aligned16(k_cache))
+    return kErrMisaligned;
+  if (dtype == 1 && (!aligned4(q_scale) || !aligned4(k_scale))) return kErrMisaligned;
+  return dsa::launch_indexer_prep(q_in, k_in, rope_cos, rope_sin, end_pos, B, T, S_max, dtype,
+                                  q_out, dtype == 1 ? q_scale : nullptr, k_cache,
+                                  dtype == 1 ? k_scale : nullptr, stream);
+}

@@ -47,5 +47,11 @@ int launch_dense_mla(const void* q_nope, const void* q_pe, const void* kv, const
 int launch_q_absorb(const void* q_nope, const void* wkv_b, int rows, void* q_abs,
                     hipStream_t stream);
 int launch_out_proj(const void* x, const void* wkv_b, int rows, void* y, hipStream_t stream);
+// Indexer input preparation (RoPE, Hadamard rotation, fp8 block quantisation or
+// bf16 rounding, key append); dtype 0 = bf16, 1 = fp8.
+int launch_indexer_prep(const void* q_in, const void* k_in, const float* rope_cos,
+                        const float* rope_sin, const int32_t* end_pos, int B, int T, int S_max,
+                        int dtype, void* q_out, float* q_scale, void* k_cache, float* k_scale,
+                        hipStream_t stream);
 
 }  // namespace dsa

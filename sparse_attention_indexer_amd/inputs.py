@@ -19,8 +19,9 @@ Shapes and distributions follow the workloads the pages describe:
   - Apply sparse mask", MQA decode excerpt).
 
 Encodings used here are conversions done by torch: fp32 -> bf16 and
-fp32 -> float8_e4m3fn are round-to-nearest-even; the fp8 block scale is
-amax/448 so every scaled value is in range.
+fp32 -> float8_e4m3fn are round-to-nearest-even.  fp8 indexer inputs are
+drawn as codes and block scales directly (``fp8_draw``), not quantised from
+fp32 data.
 """
 from __future__ import annotations
 
@@ -129,13 +130,15 @@ def _layer_norm(x, eps=1e-6):
     return (x - mu) / torch.sqrt(var + eps)
 
 
-def fp8_blocks(x: torch.Tensor):
-    """Block-128 e4m3fn encoding of the last dim: (codes, scale) with value = code * scale."""
-    assert x.shape[-1] == IDX_DIM
-    amax = x.abs().amax(dim=-1)
-    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
-    codes = (x / scale.unsqueeze(-1)).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
-    return codes, scale
+def fp8_draw(shape, g, device):
+    """Synthetic fp8 data of the shape act_quant produces, drawn directly: e4m3fn
+    codes of N(0,1) * 150 clamped to +-448 (so a 128-element block spans the
+    code range up to near its top) and fp32 block scales uniform in
+    [0.005, 0.01] (about the scale unit-variance data gets), one per block of
+    the last dim."""
+    x = (_normal(shape, g, device) * 150.0).clamp(-FP8_MAX, FP8_MAX)
+    scale = torch.rand(shape[:-1], generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.float8_e4m3fn), (0.005 + 0.005 * scale).contiguous()
 
 
 def make_case(name: str, B: int, T: int, end_pos, S_max: int, *, dtype: str = "bf16",
@@ -144,7 +147,8 @@ def make_case(name: str, B: int, T: int, end_pos, S_max: int, *, dtype: str = "b
               dup_period: int = 1024, recipe: str = "") -> Case:
     """Draw every input of one batch.
 
-    index_dist "normal": q, k, w ~ N(0,1) fp32 before encoding.
+    index_dist "normal": q, k, w ~ N(0,1) fp32 before encoding (fp8: codes and
+                         scales drawn by fp8_draw instead of q and k).
     index_dist "int":    q, k integers in [-4,4] and w = +-2^e, e in [-3,3];
                          with these every fp32 partial sum of the score is an
                          exact integer multiple of 2^-3 below 2^20.
@@ -185,8 +189,8 @@ def make_case(name: str, B: int, T: int, end_pos, S_max: int, *, dtype: str = "b
             q_scale = torch.ones((B, T, H), dtype=torch.float32, device=device)
             k_scale = torch.ones((B, S_max), dtype=torch.float32, device=device)
         else:
-            q, q_scale = fp8_blocks(qf)
-            k_cache, k_scale = fp8_blocks(kf)
+            q, q_scale = fp8_draw((B, T, H, D), g, device)
+            k_cache, k_scale = fp8_draw((B, S_max, D), g, device)
     else:
         raise ValueError(dtype)
     q_nope = _normal((B, T, N_HEADS, D_LATENT), g, device).to(torch.bfloat16)
@@ -250,6 +254,40 @@ SWEEP_CONTEXTS = (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
 
 
 # --- the products around the attention ----------------------------------------
+
+def make_prep(B: int, T: int, end_pos, S_max: int, kind: str = "normal", seed: int = 0,
+              device="cpu"):
+    """Inputs of the indexer input preparation: (q_in [B,T,64,128] bf16,
+    k_in [B,T,128] bf16, rope_cos [S_max,32] fp32, rope_sin [S_max,32] fp32,
+    end_pos [B] int32).
+
+    kind "normal": q ~ N(0,1) (the query projection's output), k ~ N(0,1)
+      centred and scaled to unit variance per row (standing in for k_norm), and
+      cos/sin of angles drawn uniform in [-pi, pi) per (position, pair).
+    kind "int": q, k integers in [-8, 8] and cos = 1, sin = 0, so every sum of
+      the rotation is an exact integer in fp32.
+    kind "zero": as "normal" but with some query heads and keys all zero.
+    """
+    g = _gen(seed, device)
+    end_pos_t = torch.as_tensor(end_pos, dtype=torch.int32).reshape(-1).to(device)
+    assert end_pos_t.numel() == B
+    shp_q, shp_k = (B, T, N_IDX_HEADS, IDX_DIM), (B, T, IDX_DIM)
+    if kind == "int":
+        q, k = _ints(shp_q, -8, 8, g, device), _ints(shp_k, -8, 8, g, device)
+        cos = torch.ones((S_max, 32), dtype=torch.float32, device=device)
+        sin = torch.zeros((S_max, 32), dtype=torch.float32, device=device)
+    elif kind in ("normal", "zero"):
+        q, k = _normal(shp_q, g, device), _layer_norm(_normal(shp_k, g, device))
+        ang = (torch.rand((S_max, 32), generator=g, device=device) * 2 - 1) * math.pi
+        cos, sin = torch.cos(ang), torch.sin(ang)
+        if kind == "zero":
+            q[..., ::7, :] = 0.0
+            k[..., ::3, :] = 0.0
+    else:
+        raise ValueError(kind)
+    bf = torch.bfloat16
+    return q.to(bf), k.to(bf), cos.contiguous(), sin.contiguous(), end_pos_t
+
 
 def make_proj(B: int, T: int, seed: int = 0, device="cpu"):
     """Inputs of the query absorption and output up-projection: q_nope

@@ -126,3 +126,29 @@ def test_projection_validation(L):
         assert fn(P, P, 0, 1, P, None) == -1
         assert fn(P, P, 1, 0, P, None) == -1
         assert fn(P, ctypes.c_void_p(P.value + 8), 1, 1, P, None) == -3
+
+
+def test_indexer_prep_validation(L):
+    """Input preparation: null, empty, inconsistent, unsupported and misaligned
+    arguments are rejected on the host before any launch."""
+    fn = L.dsa_indexer_prep
+    fn.restype = ctypes.c_int
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+
+    def call(**over):
+        a = dict(q=P, k=P, cos=P, sin=P, ep=P, B=1, T=1, S=16, dt=1, qo=P, qs=P, kc=P, ks=P)
+        a.update(over)
+        return fn(a["q"], a["k"], a["cos"], a["sin"], a["ep"], a["B"], a["T"], a["S"], a["dt"],
+                  a["qo"], a["qs"], a["kc"], a["ks"], None)
+
+    for name in ("q", "k", "cos", "sin", "ep", "qo", "kc"):
+        assert call(**{name: None}) == -1, name
+    assert call(qs=None) == -1 and call(ks=None) == -1          # fp8 needs both scales
+    assert call(B=0) == -1 and call(T=0) == -1 and call(S=0) == -1
+    assert call(T=17, S=16) == -1                                 # T > S_max
+    assert call(B=1 << 13, T=1 << 12) == -1                       # B*T > 2^24
+    assert call(dt=2) == -2
+    for name in ("q", "k", "cos", "sin", "qo", "kc"):
+        assert call(**{name: ctypes.c_void_p(P.value + 8)}) == -3, name
+    assert call(ep=ODD) == -3 and call(qs=ODD) == -3 and call(ks=ODD) == -3

@@ -553,3 +553,197 @@ def test_q_absorb_and_out_proj(B, T):
     for g, r in ((qa, ref_qa), (y, ref_y)):
         g = g.float().cpu().numpy().astype(np.float64)
         assert np.abs(g - r).max() <= 2.0 ** -8 * np.abs(r).max()
+
+
+# --- indexer input preparation -----------------------------------------------------
+
+E4M3_POISON = 0x7F      # an e4m3fn NaN code: a cache row the call must not touch keeps it
+BF16_POISON = 0x7FC1
+
+
+def _prep_run(m, q_in, k_in, cos, sin, ep, S_max, fp8):
+    B = q_in.shape[0]
+    if fp8:
+        kc = torch.full((B, S_max, 128), E4M3_POISON, dtype=torch.uint8, device=DEV)
+        kc = kc.view(torch.float8_e4m3fn)
+        ks = torch.full((B, S_max), -1.0, dtype=torch.float32, device=DEV)
+    else:
+        kc = torch.full((B, S_max, 128), BF16_POISON, dtype=torch.int16, device=DEV)
+        kc = kc.view(torch.bfloat16)
+        ks = None
+    qo, qs = m.indexer_prep(q_in, k_in, cos, sin, ep, kc, ks)
+    torch.cuda.synchronize()
+    return qo, qs, kc, ks
+
+
+def _e4m3_step(x):
+    """Spacing of e4m3 values around |x| (2^-9 below the normal range)."""
+    a = np.maximum(np.abs(x), 2.0 ** -6)
+    return 2.0 ** (np.floor(np.log2(a)) - 3)
+
+
+def _check_untouched(kc, ks, ep, T, fp8):
+    """Every cache row outside end_pos-T..end_pos-1 still holds the poison."""
+    kcb = inputs.to_numpy(kc).reshape(kc.shape[0], kc.shape[1], -1)
+    for b, e in enumerate(ep.tolist()):
+        keep = np.ones(kc.shape[1], bool)
+        keep[e - T:e] = False
+        poison = E4M3_POISON if fp8 else BF16_POISON
+        assert np.all(kcb[b][keep] == poison), f"sequence {b}: a row outside the new tokens changed"
+        if fp8:
+            assert np.all(ks[b].cpu().numpy()[keep] == -1.0)
+
+
+@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
+def test_indexer_prep_integer_exact(fp8):
+    """Integer q, k and the identity RoPE (cos 1, sin 0): every sum of the rotation
+    is exact in fp32, so codes and scales (fp8) are bit-exact and bf16 values are
+    the correctly rounded rotation; a ragged batch (end_pos 7 and 40, T = 5) and
+    cache rows outside the new tokens untouched."""
+    m = dsa()
+    B, T, S_max = 2, 5, 40
+    banner(f"prep int fp8={fp8} B={B} T={T}")
+    q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, [7, 40], S_max, kind="int", seed=71,
+                                                device=DEV)
+    qo, qs, kc, ks = _prep_run(m, q_in, k_in, cos, sin, ep, S_max, fp8)
+    rq, rqs, rk, rks, pos = oracle.indexer_prep(inputs.to_numpy(q_in), inputs.to_numpy(k_in),
+                                                cos.cpu().numpy(), sin.cpu().numpy(),
+                                                ep.cpu().numpy(), fp8=fp8)
+    kcn = inputs.to_numpy(kc)
+    if fp8:
+        assert np.array_equal(inputs.to_numpy(qo), rq)
+        assert np.array_equal(qs.cpu().numpy(), rqs)
+        for b in range(B):
+            assert np.array_equal(kcn[b, pos[b]], rk[b])
+            assert np.array_equal(ks[b].cpu().numpy()[pos[b]], rks[b])
+    else:
+        # bf16 keeps 8 significant bits: rounding moves a value by at most 2^-8 of it
+        g = qo.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(g - rq) <= 2.0 ** -8 * np.abs(rq))
+        gk = kc.float().cpu().numpy().astype(np.float64)
+        for b in range(B):
+            assert np.all(np.abs(gk[b, pos[b]] - rk[b]) <= 2.0 ** -8 * np.abs(rk[b]))
+    _check_untouched(kc, ks, ep.cpu(), T, fp8)
+
+
+def _compare_prep_fp8(qo, qs, rq, rqs):
+    """Scales within 1e-5 relative; dequantised values within one e4m3 step of
+    the oracle's (the code decision can go the other way when fp32 and fp64
+    land on opposite sides of a rounding midpoint); such flips are rare."""
+    gq = inputs.to_numpy(qo)
+    gs = np.asarray(qs, np.float64)
+    rs = np.asarray(rqs, np.float64)
+    assert np.all(np.abs(gs - rs) <= 1e-5 * np.abs(rs))
+    assert np.array_equal(gs == 0, rs == 0)
+    gv = torch.from_numpy(gq).view(torch.float8_e4m3fn).double().numpy()
+    rv = torch.from_numpy(np.ascontiguousarray(rq)).view(torch.float8_e4m3fn).double().numpy()
+    d = np.abs(gv - rv)
+    assert np.all(d <= _e4m3_step(np.maximum(np.abs(gv), np.abs(rv))) * 1.0001)
+    assert (d > 0).mean() < 0.01
+
+
+def _compare_prep_bf16(g, r):
+    g = np.asarray(g, np.float64)
+    assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 1e-6 * np.abs(r).max())
+
+
+@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
+@pytest.mark.parametrize("kind", ["normal", "zero"])
+def test_indexer_prep_random(fp8, kind):
+    """N(0,1) inputs, random RoPE angles, ragged batch of 3 sequences with 37 new
+    tokens each (end_pos 37, 100, 300); "zero" adds all-zero query heads and keys
+    (scale 0, zero codes)."""
+    m = dsa()
+    B, T, S_max = 3, 37, 300
+    banner(f"prep {kind} fp8={fp8} B={B} T={T}")
+    q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, [37, 100, 300], S_max, kind=kind,
+                                                seed=72, device=DEV)
+    qo, qs, kc, ks = _prep_run(m, q_in, k_in, cos, sin, ep, S_max, fp8)
+    rq, rqs, rk, rks, pos = oracle.indexer_prep(inputs.to_numpy(q_in), inputs.to_numpy(k_in),
+                                                cos.cpu().numpy(), sin.cpu().numpy(),
+                                                ep.cpu().numpy(), fp8=fp8)
+    gk = np.stack([inputs.to_numpy(kc[b])[pos[b]] for b in range(B)])
+    if fp8:
+        gks = np.stack([ks[b].cpu().numpy()[pos[b]] for b in range(B)])
+        _compare_prep_fp8(qo, qs.cpu().numpy(), rq, rqs)
+        _compare_prep_fp8(torch.from_numpy(gk).view(torch.float8_e4m3fn), gks, rk, rks)
+        if kind == "zero":
+            assert np.all(rqs[:, :, ::7] == 0) and np.all(qs.cpu().numpy()[:, :, ::7] == 0)
+            assert not inputs.to_numpy(qo)[:, :, ::7].any()
+    else:
+        _compare_prep_bf16(qo.float().cpu().numpy(), rq)
+        _compare_prep_bf16(torch.from_numpy(gk).view(torch.bfloat16).float().numpy(), rk)
+    _check_untouched(kc, ks, ep.cpu(), T, fp8)
+
+
+@pytest.mark.parametrize("shape", ["prefill_8192", "decode_b64"])
+def test_indexer_prep_full_size_sampled(shape):
+    """The two full-size shapes at which the preparation is timed -- one sequence
+    of 8192 new tokens, and 64 sequences decoding one token each at context
+    lengths up to 131072 -- checked on sampled tokens, each recomputed by the
+    oracle on its own (a one-token batch at that position)."""
+    m = dsa()
+    if shape == "prefill_8192":
+        B, T, S_max, ep_list = 1, 8192, 8192, [8192]
+        sample = [(0, t) for t in (0, 1, 15, 16, 2047, 4000, 8190, 8191)]
+    else:
+        g = torch.Generator().manual_seed(73)
+        B, T, S_max = 64, 1, 131072
+        ep_list = torch.randint(8192, S_max + 1, (B,), generator=g).tolist()
+        ep_list[0], ep_list[1] = 1, S_max
+        sample = [(b, 0) for b in (0, 1, 2, 31, 63)]
+    banner(f"prep full size {shape}")
+    q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, ep_list, S_max, seed=74, device=DEV)
+    qo, qs, kc, ks = _prep_run(m, q_in, k_in, cos, sin, ep, S_max, True)
+    cn, sn = cos.cpu().numpy(), sin.cpu().numpy()
+    for b, t in sample:
+        p = ep_list[b] - T + t
+        rq, rqs, rk, rks, _ = oracle.indexer_prep(
+            inputs.to_numpy(q_in[b:b + 1, t:t + 1]), inputs.to_numpy(k_in[b:b + 1, t:t + 1]),
+            cn, sn, np.array([p + 1], np.int32))
+        _compare_prep_fp8(qo[b:b + 1, t:t + 1], qs[b:b + 1, t:t + 1].cpu().numpy(), rq, rqs)
+        _compare_prep_fp8(kc[b:b + 1, p:p + 1].contiguous().view(1, 1, 128),
+                          ks[b:b + 1, p:p + 1].cpu().numpy(), rk, rks)
+        if T == 1:      # the neighbouring cache rows keep the poison
+            for r in (p - 1, p + 1):
+                if 0 <= r < S_max:
+                    assert np.all(inputs.to_numpy(kc[b, r]) == E4M3_POISON)
+
+
+def test_indexer_prep_feeds_index_scores():
+    """The preparation's fp8 outputs are the inputs of dsa_index_scores: scoring
+    the prepared query against the prepared cache on the GPU matches the oracle's
+    scores of the oracle's prepared tensors (ragged prefill batch)."""
+    m = dsa()
+    B, T, S_max = 2, 20, 64
+    banner("prep -> index_scores")
+    q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, [20, 64], S_max, seed=75, device=DEV)
+    # fill the earlier cache rows by preparing them as a first batch of tokens
+    kc = torch.zeros((B, S_max, 128), dtype=torch.float8_e4m3fn, device=DEV)
+    ks = torch.zeros((B, S_max), dtype=torch.float32, device=DEV)
+    q0, k0, _, _, _ = inputs.make_prep(B, 44, [44, 44], S_max, seed=76, device=DEV)
+    ep0 = torch.tensor([44, 44], dtype=torch.int32, device=DEV)
+    m.indexer_prep(q0, k0, cos, sin, ep0, kc, ks)
+    qo, qs = m.indexer_prep(q_in, k_in, cos, sin, ep, kc, ks)
+    w = torch.randn((B, T, 64), generator=torch.Generator(device=DEV).manual_seed(77),
+                    device=DEV)
+    scale = 128 ** -0.5
+    got = m.index_scores(qo, w, kc, ep, scale, q_scale=qs, k_scale=ks).cpu().numpy()
+    # The oracle's own preparation of the same inputs (first batch, then this one)
+    rk = np.zeros((B, S_max, 128), np.uint8)
+    rks = np.zeros((B, S_max), np.float32)
+    cn, sn = cos.cpu().numpy(), sin.cpu().numpy()
+    _, _, k0c, k0s, p0 = oracle.indexer_prep(inputs.to_numpy(q0), inputs.to_numpy(k0), cn, sn,
+                                             np.array([44, 44], np.int32))
+    rq, rqs, k1c, k1s, p1 = oracle.indexer_prep(inputs.to_numpy(q_in), inputs.to_numpy(k_in),
+                                                cn, sn, ep.cpu().numpy())
+    for b in range(B):
+        rk[b, p0[b]], rks[b, p0[b]] = k0c[b], k0s[b]
+        rk[b, p1[b]], rks[b, p1[b]] = k1c[b], k1s[b]
+    ref = oracle.index_scores(rq, w.cpu().numpy(), rk, ep.cpu().numpy(), scale, q_scale=rqs,
+                              k_scale=rks)
+    for b in range(B):
+        for t in range(T):
+            bound = int(ep[b]) - T + t
+            g, r = got[b, t, :bound + 1], ref[b, t, :bound + 1]
+            assert np.abs(g - r).max() <= 2e-2 * np.abs(r).max()
