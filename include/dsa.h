@@ -142,7 +142,9 @@ int dsa_topk(const float* index_score, const int32_t* end_pos, int32_t B, int32_
  *   topk_indices [B,T,k] int32 (as produced by dsa_topk)
  *   out      [B,T,128,512] bf16 (fp32 accumulation, rounded to nearest even)
  *   lse      [B,T,128] fp32 natural-log sum of exp(z) over the kept rows, or NULL
- * A row with no valid entry produces out = 0 and lse = -inf.
+ * A row with no valid entry produces out = 0 and lse = -inf.  softmax_scale
+ * must be positive and finite (else DSA_ERR_INVALID_ARGUMENT); this holds for
+ * dsa_dense_mla and dsa_forward too.
  * Arithmetic: both contractions on bf16 MFMA with fp32 accumulation, fp32
  * online softmax; the probabilities enter the value contraction as bf16. */
 size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t T, int32_t k);

@@ -24,6 +24,9 @@ constexpr size_t kWsAlign = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+// A softmax scale must be a positive finite number (the kernels take the
+// running maximum on unscaled scores).
+bool good_softmax_scale(float s) { return s > 0.f && __builtin_isfinite(s); }
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // Shared checks of the (B, T, S_max, max_end_pos) geometry.
@@ -151,6 +154,7 @@ DSA_EXPORT int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* 
   if (st) return st;
   if (!topk_indices) return kErrInvalid;
   if (B < 1 || T < 1 || S_max < 1 || k < 1) return kErrInvalid;
+  if (!good_softmax_scale(softmax_scale)) return kErrInvalid;
   if (k > kMaxTopk) return kErrUnsupported;
   if (!aligned4(topk_indices)) return kErrMisaligned;
   st = check_workspace(workspace, workspace_bytes, sparse_mla_ws(B, T, k));
@@ -176,6 +180,7 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   int st = check_indexer(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
                          max_end_pos, dtype);
   if (st) return st;
+  if (!good_softmax_scale(softmax_scale)) return kErrInvalid;
   st = check_mla_tensors(q_nope, q_pe, kv_cache, pe_cache, out, lse);
   if (st) return st;
   if (k < 1) return kErrInvalid;
@@ -213,6 +218,7 @@ DSA_EXPORT int dsa_dense_mla(const void* q_nope, const void* q_pe, const void* k
                              hipStream_t stream) {
   int st = check_mla_tensors(q_nope, q_pe, kv_cache, pe_cache, out, lse);
   if (st) return st;
+  if (!good_softmax_scale(softmax_scale)) return kErrInvalid;
   if (!end_pos) return kErrInvalid;
   st = check_geometry(B, T, S_max, max_end_pos);
   if (st) return st;

@@ -56,6 +56,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values to packed bf16 (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Order-preserving map from an fp32 score to an unsigned key: larger score,
 // larger key.  -0 is first turned into +0 so the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float x) {

@@ -5,10 +5,14 @@
 //   z[h,j] = (q_nope[h,:] . kv[pos_j,:] + q_pe[h,:] . pe[pos_j,:]) * softmax_scale
 //   out[h,:] = sum_j softmax_j(z[h,:]) * kv[pos_j,:]
 //
-// Work item: one query row and one split of its row list, all 128 heads.  A
-// 512-thread workgroup has 8 waves of 16 heads (two waves per SIMD, so one
-// wave's LDS reads overlap the other's MFMAs); it walks its split 64 rows at a
-// time, so every gathered row is read from HBM once for all heads.
+// Work item: one query row and one split of its row list.  Two forms:
+//   narrow (mla_kernel, few query rows, i.e. small-batch decode): a 2-wave
+//     workgroup takes 32 of the 128 heads, so one query spreads over many CUs;
+//   wide (mla_wide_kernel, many query rows): an 8-wave workgroup takes all
+//     128 heads, so every gathered row is read from HBM once for all heads;
+//     its layout and pipeline are described above the kernel.
+// The rest of this header describes the narrow form; the wide one shares its
+// gathers, score layout and online softmax.
 //
 // Gathers.  Rows are copied from HBM straight into LDS (global_load_lds, 16
 // bytes a lane, no register staging) into a 2-slot ring, so the next tile is
@@ -88,9 +92,7 @@ __device__ __forceinline__ float group_sum(float v) {
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return pack2_bf16(a, b); }
 __device__ __forceinline__ uint32_t pack_half(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
@@ -352,6 +354,375 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   }
 }
 
+// ---- Wide form: many query rows -------------------------------------------
+//
+// Eight waves (two per SIMD).  The two contractions are split differently:
+//   scores  S^T[row][head]: wave w takes heads 16w..16w+15, its query
+//           fragments in registers, exactly as in the narrow form;
+//   values  O^T[c][head]: wave w takes latent dims 64w..64w+63 for all 128
+//           heads (4 x 8 accumulator tiles, 128 registers), so each transposed
+//           V fragment feeds 8 head tiles and V is read from LDS once per tile
+//           instead of once per wave (in the narrow form the 8-fold re-reading
+//           of V through the transposing LDS read dominates).
+// The probabilities cross between the two through LDS: the lane of a score
+// wave that holds head n and rows {4g+i, 16+4g+i} holds exactly the B
+// fragment (same K order) that lane (n, g) of every value wave needs for that
+// head tile, so P is 16 bytes per lane per head tile (8 KiB a tile), plus one
+// rescale factor per head for tiles where some head's running maximum moved.
+// Tiles are 32 rows in a 3-slot ring, so two tiles are in flight during the
+// math; each wave copies 4 rows (one copy per latent row, one per rope part).
+// Row copies for the wide form, issued through inline asm: global_load_lds
+// with M0 = the LDS destination of lane 0 (lane i writes 16 bytes at M0 +
+// 16 i).  Written as a builtin, the compiler treats the copy as an LDS write
+// that may alias every later LDS read of the ring array and makes those reads
+// wait for all copies in flight, which serialises the gathers with the math;
+// here the kernel itself orders each slot's reads after that slot's copies
+// (a vmcnt wait, then a barrier).  The instruction has no register result.
+__device__ __forceinline__ void lds_copy16(const uint8_t* row, uint32_t lane_off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(lane_off), "s"(row) : "m0");
+}
+__device__ __forceinline__ void lds_copy16_v(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(addr) : "m0");
+}
+// The lane id through an empty asm: the compiler cannot hoist what is derived
+// from it out of a loop, so per-lane addresses are recomputed (a few VALU
+// ops) instead of being kept live across the loop or spilled.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+constexpr int kWdWaves = 8;
+constexpr int kWdThreads = kWdWaves * 64;
+constexpr int kWdRt = 32;                               // rows per tile
+constexpr int kWdRw = kWdRt / kWdWaves;                 // rows each wave copies (4)
+constexpr int kWdNbuf = 3;
+constexpr int kWdLoads = 2 * kWdRw;                     // copies per wave per tile
+// Latent rows sit 1056 bytes apart (8 banks), and the 16-byte chunks of rows
+// 8..15 and 24..31 of a tile are XOR-swizzled by 1: chunk c of row r is at
+// position c ^ ((r >> 3) & 1).  The score reads (16 rows, one chunk each per
+// quarter wave) and the transposing value reads (8 rows, two chunks each per
+// half wave) are then both free of bank conflicts.
+constexpr int kWdPitch = 1056;
+__device__ __forceinline__ int wd_swz(int row) { return (row >> 3) & 1; }
+constexpr int kWdTileKv = kWdRt * kWdPitch;
+constexpr int kWdTileBytes = kWdTileKv + kWdRt * 128;
+constexpr int kWdDims = kDc / kWdWaves;                 // latent dims per value wave (64)
+constexpr int kWdCt = kWdDims / 16;                     // their 16-dim tiles (4)
+static_assert(kWdRw == 4, "rope copies use lanes 8r..8r+7 for row r");
+
+template <bool kDense>
+__global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
+    int k, int rows_per_split, int n_splits, int n_items, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float4* __restrict__ part_ml) {
+  __shared__ __align__(16) uint8_t s_ring[kWdNbuf * kWdTileBytes];
+  __shared__ __align__(16) uint4 s_p[2][kHeads / 16][64];  // P fragments per head tile
+  __shared__ float s_alpha[2][kHeads];                    // a tile's rescale per head
+  __shared__ float s_fin[2 + kWdWaves][kHeads];         // m, l, then per-wave amax
+  __shared__ __align__(8) uint8_t s_vmask[kWdNbuf][kWdWaves];  // bit r: row 4w+r is valid
+  __shared__ __align__(16) uint4 s_qpe[2][kWdWaves][64];      // rope-part query fragments
+  __shared__ int s_grow[2];                             // last tile (per parity) whose max moved
+  __shared__ int s_idx[kDense ? 1 : kMaxSplitRows];     // the split's positions
+
+  const int X = blockIdx.x;
+  if (X >= n_items) return;
+  const int row = X / n_splits, split = X - row * n_splits;
+  const int b = row / T, t = row - b * T;
+  int n_list;
+  if constexpr (kDense) {
+    const int ep = min(max(end_pos[b], T), S_max);
+    n_list = ep - T + t + 1;
+  } else {
+    n_list = k;
+  }
+  const int j_begin = split * rows_per_split;
+  const int j_end = min(j_begin + rows_per_split, n_list);
+  const int n_rows = max(j_end - j_begin, 0);
+  const int n_tiles = (n_rows + kWdRt - 1) / kWdRt;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  // The split's positions are copied into LDS once, so the gathers of later
+  // tiles never wait on a load of their positions.
+  if constexpr (!kDense) {
+    const int32_t* src = idx + (size_t)row * k + j_begin;
+    for (int j = threadIdx.x; j < n_rows; j += kWdThreads) {
+      const int pos = src[j];
+      s_idx[j] = (pos < 0 || pos >= S_max) ? -1 : pos;
+    }
+  }
+  auto entry_pos = [&](int j) {
+    int pos = -1;
+    if (j < n_rows) {
+      if constexpr (kDense) pos = j_begin + j;
+      else pos = s_idx[j];
+    }
+    return pos;
+  };
+
+  // Query fragments of the wave's head tile (head 16*wave + r16): the latent
+  // part in registers, the rope part parked in LDS (each wave reads back only
+  // its own), which keeps the register budget of two waves per SIMD.
+  const int head = 16 * wave + r16;
+  uint4 qb[16];
+  {
+    const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc;
+    const uint16_t* qp = q_pe + ((size_t)row * kHeads + head) * kDr;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qb[kk] = ldg16(qn + kk * 32 + g * 8);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) s_qpe[kk][wave][lane] = ldg16(qp + kk * 32 + g * 8);
+  }
+
+  const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
+  const uint8_t* pe_b = reinterpret_cast<const uint8_t*>(pe) + (size_t)b * S_max * kDr * 2;
+
+  // This wave copies rows 4*wave .. 4*wave+3 of tile `tile` into its ring
+  // slot (empty entries copy row 0 and are masked by their position -1).
+  auto issue = [&](int tile) {
+    uint8_t* base = s_ring + (tile % kWdNbuf) * kWdTileBytes;
+    int rpos[kWdRw];
+#pragma unroll
+    for (int r = 0; r < kWdRw; ++r) rpos[r] = entry_pos(tile * kWdRt + kWdRw * wv + r);
+    {
+      uint32_t vm = 0;
+#pragma unroll
+      for (int r = 0; r < kWdRw; ++r) vm |= (rpos[r] >= 0 ? 1u : 0u) << r;
+      if (lane == 0) s_vmask[tile % kWdNbuf][wv] = (uint8_t)vm;
+    }
+#pragma unroll
+    for (int r = 0; r < kWdRw; ++r) rpos[r] = max(rpos[r], 0);
+#pragma unroll
+    for (int r = 0; r < kWdRw; ++r) {
+      // The position is uniform over the wave: the row's address is scalar.
+      const int pu = __builtin_amdgcn_readfirstlane(rpos[r]);
+      const uint8_t* rowp = kv_b + (size_t)pu * (kDc * 2);
+      const int trow = kWdRw * wv + r;
+      // Lane L writes position L, so it fetches chunk L ^ swizzle.
+      lds_copy16(rowp, (opaque_lane() ^ wd_swz(trow)) * 16,
+                 __builtin_amdgcn_readfirstlane(lds_addr(base + trow * kWdPitch)));
+    }
+    // Rope parts of the 4 rows, one copy per row by lanes 8r..8r+7 (so the
+    // row's address is scalar): lane 8r+c writes chunk c of row r, holding the
+    // row's global chunk c ^ (row & 7).
+    {
+      const int ln = opaque_lane();
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(base + kWdTileKv + kWdRw * wv * 128));
+#pragma unroll
+      for (int r = 0; r < kWdRw; ++r) {
+        const int trow = kWdRw * wv + r;
+        const int pu = __builtin_amdgcn_readfirstlane(rpos[r]);
+        if ((ln >> 3) == r)
+          lds_copy16(pe_b + (size_t)pu * (kDr * 2), (uint32_t)(((ln & 7) ^ (trow & 7)) * 16), m0);
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[kWdCt][8];  // [c-tile kWdCt*wave + j][head tile]: dims ct*16 + 4g + i, head 16*h + r16
+#pragma unroll
+  for (int j = 0; j < kWdCt; ++j)
+#pragma unroll
+    for (int h = 0; h < 8; ++h) o[j][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (threadIdx.x < 2) s_grow[threadIdx.x] = -1;
+  __syncthreads();  // s_idx and s_grow
+
+  if (n_tiles > 0) issue(0);
+
+  // Iteration it: scores and softmax of tile it, values of tile it-1 (whose P
+  // was written in the previous iteration), so that one barrier per tile
+  // suffices and a wave's softmax arithmetic can interleave with its MFMAs.
+#pragma unroll 1
+  for (int it = 0; it <= n_tiles; ++it) {
+    static_assert(kWdNbuf == 3, "slots: tile it-1 (values), tile it (scores), tile it+1 (copies)");
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's copies of tile it have landed
+    lds_barrier();  // ... and every wave's; P(it-1) is visible; slot (it+1)%3 is free
+    if (it + 1 < n_tiles) issue(it + 1);
+    const int lane = opaque_lane(), g = lane >> 4, r16 = lane & 15;  // recomputed addresses
+    const int head = 16 * wave + r16;
+
+    // ---- scores of tile it for this wave's 16 heads: rows mt*16 + 4g + i ----
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const bool have_s = it < n_tiles;
+    const int slot = it % kWdNbuf;
+    if (have_s) {
+      const uint8_t* buf = s_ring + slot * kWdTileBytes;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int trow = mt * 16 + r16;
+          const uint8_t* a;
+          if (kk < 16) {
+            a = buf + trow * kWdPitch + (((kk * 4 + g) ^ wd_swz(trow)) << 4);
+          } else {
+            const int chunk = ((kk - 16) * 4 + g) ^ (trow & 7);
+            a = buf + kWdTileKv + trow * 128 + chunk * 16;
+          }
+          const uint4 bq = kk < 16 ? qb[kk] : s_qpe[kk - 16][wave][lane];
+          sc[mt] = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(a)),
+                                      as_bf16x8(bq), sc[mt]);
+        }
+      }
+    }
+
+    // ---- values of tile it-1 for this wave's 64 latent dims, all heads ----
+    if (it > 0) {
+      const int pt = it - 1, pp = pt & 1;
+      if (s_grow[pp] == pt) {  // some head's reference moved at tile it-1
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const float al = s_alpha[pp][16 * h + r16];
+#pragma unroll
+          for (int j = 0; j < kWdCt; ++j) o[j][h] *= al;
+        }
+      }
+      // Rows 4g + r16/4 (+16): their swizzle is g >> 1 for both halves.
+      const uint8_t* vrow = s_ring + (pt % kWdNbuf) * kWdTileBytes +
+                            (4 * g + (r16 >> 2)) * kWdPitch + 8 * (r16 & 1);
+      const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+#pragma unroll
+      for (int jh = 0; jh < kWdCt; jh += 2) {
+        uint4 va[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ct = kWdCt * wave + jh + jj;
+          const int off = ((2 * ct + vch) ^ vsw) << 4;  // this lane's 16-byte chunk
+          const i16x4 lo = lds_read_tr16(vrow + off);
+          const i16x4 hi = lds_read_tr16(vrow + 16 * kWdPitch + off);
+          va[jj] = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint4 pb = s_p[pp][h][lane];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            o[jh + jj][h] = mfma_bf16_16x16x32(as_bf16x8(va[jj]), as_bf16x8(pb), o[jh + jj][h]);
+        }
+      }
+    }
+
+    // ---- online softmax of tile it for this lane's head (branch-free) ----
+    if (have_s) {
+      const int cp = it & 1;
+      // Rows 4g+i were copied by wave g, rows 16+4g+i by wave 4+g.
+      const uint32_t vm = (uint32_t)s_vmask[slot][g] | ((uint32_t)s_vmask[slot][4 + g] << 4);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[mt][i] = (vm >> (4 * mt + i)) & 1u ? sc[mt][i] : -INFINITY;  // raw score, masked
+          mx = fmaxf(mx, sc[mt][i]);
+        }
+      mx = group_max(mx) * scale_log2;  // log2-domain tile max
+      // Lazy rescaling: the reference moves only when the tile's max exceeds
+      // it by more than kRescaleSlack, so probabilities stay below 2^8.
+      const bool grow = mx > m_run + kRescaleSlack;
+      const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.f;
+      m_run = grow ? mx : m_run;
+      l_part *= alpha;
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float p[2][4], psum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[mt][i] = __builtin_amdgcn_exp2f(fmaf(sc[mt][i], scale_log2, -m_use));
+          psum += p[mt][i];
+        }
+      l_part += psum;
+      s_p[cp][wave][lane] = uint4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                                  pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+      if (g == 0) s_alpha[cp][head] = alpha;
+      if (__ballot(grow) != 0 && lane == 0) s_grow[cp] = it;
+    }
+  }
+
+  // ---- finish: (m, l) per head from the score waves to the value waves ----
+  {
+    const float l_tot = group_sum(l_part);
+    if (g == 0) {
+      s_fin[0][head] = m_run;
+      s_fin[1][head] = l_tot;
+      if (n_splits == 1 && lse != nullptr)
+        lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+  lds_barrier();
+  float inv[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const float l = s_fin[1][16 * h + r16];
+    inv[h] = l > 0.f ? 1.f / l : 0.f;
+  }
+  if (n_splits == 1) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      uint16_t* orow = out + ((size_t)row * kHeads + 16 * h + r16) * kDc + 4 * g;
+#pragma unroll
+      for (int j = 0; j < kWdCt; ++j) {
+        const int ct = kWdCt * wave + j;
+        *reinterpret_cast<uint2*>(orow + ct * 16) =
+            uint2{pack_bf16(o[j][h][0] * inv[h], o[j][h][1] * inv[h]),
+                  pack_bf16(o[j][h][2] * inv[h], o[j][h][3] * inv[h])};
+      }
+    }
+  } else {
+    // Partial o/l in fp16 with a per-(split, head) power-of-two scale that puts
+    // the largest of its 512 elements in [2^14, 2^15): each wave's maximum over
+    // its 64 dims goes through LDS.
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < kWdCt; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[j][h][i]));
+      amax = group_max(amax) * inv[h];
+      if (g == 0) s_fin[2 + wave][16 * h + r16] = amax;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int hd = 16 * h + r16;
+      float amax = s_fin[2][hd];
+#pragma unroll
+      for (int w = 1; w < kWdWaves; ++w) amax = fmaxf(amax, s_fin[2 + w][hd]);
+      int e;
+      frexpf(amax, &e);  // amax < 2^e
+      e = min(max(e, -100), 100);
+      const float sc = ldexpf(inv[h], 15 - e);
+      uint16_t* prow = part_o + ((size_t)X * kHeads + hd) * kDc + 4 * g;
+#pragma unroll
+      for (int j = 0; j < kWdCt; ++j) {
+        const int ct = kWdCt * wave + j;
+        *reinterpret_cast<uint2*>(prow + ct * 16) =
+            uint2{pack_half(o[j][h][0] * sc, o[j][h][1] * sc),
+                  pack_half(o[j][h][2] * sc, o[j][h][3] * sc)};
+      }
+      if (wave == 0 && g == 0)
+        part_ml[(size_t)X * kHeads + hd] =
+            float4{s_fin[0][hd], s_fin[1][hd], ldexpf(1.f, e - 15), 0.f};
+    }
+  }
+}
+
 __device__ __forceinline__ float half_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
 }
@@ -516,12 +887,19 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
     part_ml = reinterpret_cast<float4*>(part_o + (size_t)n_items * kHeads * kDc);
   }
   int st;
-  if (plan.waves == 2)
+  if (plan.waves == 8) {
+    hipLaunchKernelGGL((mla_wide_kernel<kDense>), dim3((unsigned)n_items), dim3(kWdThreads), 0,
+                       stream, reinterpret_cast<const uint16_t*>(q_nope),
+                       reinterpret_cast<const uint16_t*>(q_pe),
+                       reinterpret_cast<const uint16_t*>(kv), reinterpret_cast<const uint16_t*>(pe),
+                       idx, end_pos, T, S_max, k, plan.rows_per_split, plan.n_splits, n_items,
+                       softmax_scale * kLog2e, reinterpret_cast<uint16_t*>(out), lse, part_o,
+                       part_ml);
+    st = hipGetLastError() == hipSuccess ? 0 : -5;
+  } else {
     st = launch_mla_shape<kDense, 2, 16>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
                                          rows, softmax_scale, out, lse, part_o, part_ml, stream);
-  else
-    st = launch_mla_shape<kDense, 8, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
-                                        rows, softmax_scale, out, lse, part_o, part_ml, stream);
+  }
   if (st) return st;
   if (plan.n_splits > 1) {
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * kHeads)), dim3(128), 0, stream,

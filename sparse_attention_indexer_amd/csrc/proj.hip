@@ -52,10 +52,6 @@ __device__ __forceinline__ i16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-}
-
 // Workgroup (head h, latent columns c0 .. c0+127, query rows r0 .. r0+63).
 __global__ __launch_bounds__(kAbWaves * 64) void absorb_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ wkv,

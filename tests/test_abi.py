@@ -81,6 +81,10 @@ def test_sparse_mla_validation(L):
     bad = list(args)
     bad[8] = 4096
     assert L.dsa_sparse_mla(*bad, P, 1 << 40, None) == -2
+    for s in (0.0, -0.1, float("nan"), float("inf")):  # the softmax scale must be > 0, finite
+        bad = list(args)
+        bad[9] = s
+        assert L.dsa_sparse_mla(*bad, P, need, None) == -1
 
 
 def test_forward_validation(L):

@@ -325,6 +325,46 @@ def test_sparse_mla_single_row_and_empty():
     assert torch.isinf(lse[0, 1]).all() and (lse[0, 1] < 0).all()
 
 
+@pytest.mark.parametrize("B,T,S,ep,k,fill", [
+    (2, 60, 5000, [5000, 1500], 2048, "random"),   # 120 rows: the many-row form, 2 splits
+    (1, 300, 3000, [3000], 2048, "random"),        # 300 rows: one split, direct output
+    (4, 9, 400, [400, 30, 200, 9], 100, "last"),   # splits of 64 + 36, short rows, ragged
+])
+def test_sparse_mla_many_rows(B, T, S, ep, k, fill):
+    """Batches with more than 16 query rows take the 8-wave form (scores per
+    16 heads, values per 64 latent dims, probabilities exchanged through LDS);
+    checked on sampled rows, including the first and last."""
+    m = dsa()
+    banner(f"sparse_mla many rows B={B} T={T} k={k}")
+    case = _mla_inputs(B, T, S, ep, 15)
+    idx = inputs.make_indices(B, T, ep, k, seed=9, fill=fill, device=DEV)
+    out, lse = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, idx,
+                            case.softmax_scale)
+    h = np_case(case)
+    n = B * T
+    rows = sorted({0, 1, T - 1, T, n // 2, n - 2, n - 1} & set(range(n)))
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, indices=idx.cpu().numpy(),
+                                rows=rows)
+    assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
+
+
+def test_dense_mla_many_rows():
+    """Dense attention for 40 query rows over 3000 positions: the many-row form
+    with splits of 512 positions (the last one partial)."""
+    m = dsa()
+    banner("dense_mla many rows")
+    B, T, S = 1, 40, 3000
+    case = _mla_inputs(B, T, S, [S], 16)
+    out, lse = m.dense_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, case.end_pos,
+                           case.softmax_scale, max_end_pos=S)
+    h = np_case(case)
+    rows = [0, 1, 17, 38, 39]
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, rows=rows)
+    assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
+
+
 @pytest.mark.parametrize("S,ep", [(3000, [3000, 1200]), (20000, [20000, 9000])])
 def test_dense_mla_vs_oracle(S, ep):
     m = dsa()
