@@ -98,6 +98,36 @@ __device__ __forceinline__ uint32_t pack_half(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// Row copies issued through inline asm: global_load_lds
+// with M0 = the LDS destination of lane 0 (lane i writes 16 bytes at M0 +
+// 16 i).  Written as a builtin, the compiler treats the copy as an LDS write
+// that may alias every later LDS read of the ring array and makes those reads
+// wait for all copies in flight, which serialises the gathers with the math;
+// here the kernel itself orders each slot's reads after that slot's copies
+// (a vmcnt wait, then a barrier).  The instruction has no register result.
+__device__ __forceinline__ void lds_copy16(const uint8_t* row, uint32_t lane_off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(lane_off), "s"(row) : "m0");
+}
+__device__ __forceinline__ void lds_copy16_v(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(addr) : "m0");
+}
+// The lane id through an empty asm: the compiler cannot hoist what is derived
+// from it out of a loop, so per-lane addresses are recomputed (a few VALU
+// ops) instead of being kept live across the loop or spilled.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+// Most positions a split of the narrow form holds (its plans stay below).
+constexpr int kNarrowMaxRows = 512;
+
 template <bool kDense, int kWaves, int kRw>
 __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
@@ -112,6 +142,7 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   constexpr int kTileKv = S::kTileKv, kTileBytes = S::kTileBytes;
   __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
   __shared__ int s_pos[kNbuf][kRt];  // positions of the tiles in the ring (-1 = empty)
+  __shared__ int s_idx[kDense ? 1 : kNarrowMaxRows];  // the split's positions
 
   // Block -> (item = row * n_splits + split, head group).  The head groups of
   // one item get ids that are 8 apart, i.e. fall on the same XCD (ids are dealt
@@ -149,12 +180,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   auto entry_pos = [&](int j) {
     int pos = -1;
     if (j < n_rows) {
-      if constexpr (kDense) {
-        pos = j_begin + j;
-      } else {
-        pos = idx[(size_t)row * k + j_begin + j];
-        if (pos < 0 || pos >= S_max) pos = -1;
-      }
+      if constexpr (kDense) pos = j_begin + j;
+      else pos = s_idx[j];
     }
     return pos;
   };
@@ -170,6 +197,16 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     for (int kk = 0; kk < 16; ++kk) qb[kk] = ldg16(qn + kk * 32 + g * 8);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = ldg16(qp + kk * 32 + g * 8);
+  }
+  // The split's positions go to LDS in one go, their loads in flight together
+  // with the query's, so no tile's copies wait on a load of its positions.
+  if constexpr (!kDense) {
+    const int32_t* src = idx + (size_t)row * k + j_begin;
+    for (int j = threadIdx.x; j < n_rows; j += kThreads) {
+      const int pos = src[j];
+      s_idx[j] = (pos < 0 || pos >= S_max) ? -1 : pos;
+    }
+    __syncthreads();
   }
 
   const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
@@ -196,8 +233,9 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 #pragma unroll
     for (int r = 0; r < kRw; ++r) {
       const int trow = kRw * wv + r;
-      __builtin_amdgcn_global_load_lds((glb_void*)(kv_b + (size_t)rpos[r] * (kDc * 2) + lane * 16),
-                                       (lds_void*)(base + trow * kKvPitch), 16, 0, 0);
+      const int pu = __builtin_amdgcn_readfirstlane(rpos[r]);
+      lds_copy16(kv_b + (size_t)pu * (kDc * 2), lane * 16,
+                 __builtin_amdgcn_readfirstlane(lds_addr(base + trow * kKvPitch)));
     }
     // Rope parts, 8 rows per instruction: lane L writes chunk L%8 of row L/8,
     // holding the row's global chunk (L%8) ^ (row & 7).
@@ -209,9 +247,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
       for (int rr = 1; rr < kRw; ++rr) pos = r == rr ? rpos[rr] : pos;
       const int trow = kRw * wv + r;
       const int chunk = (lane & 7) ^ (trow & 7);
-      __builtin_amdgcn_global_load_lds((glb_void*)(pe_b + (size_t)pos * (kDr * 2) + chunk * 16),
-                                       (lds_void*)(base + kTileKv + (kRw * wv + 8 * q8) * 128),
-                                       16, 0, 0);
+      lds_copy16_v(pe_b + (size_t)pos * (kDr * 2) + chunk * 16,
+                   __builtin_amdgcn_readfirstlane(lds_addr(base + kTileKv + (kRw * wv + 8 * q8) * 128)));
     }
   };
 
@@ -371,33 +408,6 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 // rescale factor per head for tiles where some head's running maximum moved.
 // Tiles are 32 rows in a 3-slot ring, so two tiles are in flight during the
 // math; each wave copies 4 rows (one copy per latent row, one per rope part).
-// Row copies for the wide form, issued through inline asm: global_load_lds
-// with M0 = the LDS destination of lane 0 (lane i writes 16 bytes at M0 +
-// 16 i).  Written as a builtin, the compiler treats the copy as an LDS write
-// that may alias every later LDS read of the ring array and makes those reads
-// wait for all copies in flight, which serialises the gathers with the math;
-// here the kernel itself orders each slot's reads after that slot's copies
-// (a vmcnt wait, then a barrier).  The instruction has no register result.
-__device__ __forceinline__ void lds_copy16(const uint8_t* row, uint32_t lane_off, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m0), "v"(lane_off), "s"(row) : "m0");
-}
-__device__ __forceinline__ void lds_copy16_v(const uint8_t* addr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0), "v"(addr) : "m0");
-}
-// The lane id through an empty asm: the compiler cannot hoist what is derived
-// from it out of a loop, so per-lane addresses are recomputed (a few VALU
-// ops) instead of being kept live across the loop or spilled.
-__device__ __forceinline__ int opaque_lane() {
-  int l = __lane_id();
-  asm volatile("" : "+v"(l));
-  return l;
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
-}
-
 constexpr int kWdWaves = 8;
 constexpr int kWdThreads = kWdWaves * 64;
 constexpr int kWdRt = 32;                               // rows per tile
@@ -819,7 +829,7 @@ MlaPlan sparse_mla_plan(int B, int T, int k) {
     // about 128 items of 2 head groups each.
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)k * rows) rps *= 2;
-    return MlaPlan{rps, (k + rps - 1) / rps, 2};
+    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (k + rps - 1) / rps, 2};
   }
   long ns = DSA_MLA_TARGET_BLOCKS / rows;
   const long max_ns = (k + 63) / 64;
@@ -839,7 +849,7 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   if (rows <= DSA_MLA_SMALL_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK) {
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)S_max * rows) rps *= 2;
-    return MlaPlan{rps, (ext + rps - 1) / rps, 2};
+    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (ext + rps - 1) / rps, 2};
   }
   long rps = (long)S_max * rows / DSA_MLA_TARGET_BLOCKS;
   rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
