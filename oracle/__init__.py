@@ -9,9 +9,10 @@ The arithmetic of the three decode stages lives in ``dsa_oracle.c`` (plain
 C, fp64 sums, OpenMP over query rows), built with gcc into ``liboracle.so``;
 for them this module only marshals numpy arrays.  The two per-head products
 around the attention (``q_absorb``, ``out_proj``) are written out below as
-fp64 numpy contractions, and so is the weight-free indexer input preparation
+fp64 numpy contractions, and so are the weight-free indexer input preparation
 (``indexer_prep``: RoPE, Hadamard rotation, fp8 block quantisation; its code
-decisions are taken in fp32, the precision of the quantiser on the GPU).  Conventions for array arguments:
+decisions are taken in fp32, the precision of the quantiser on the GPU) and
+the MHA-form prefill attention (``sparse_mha_prefill``).  Conventions for array arguments:
 
 * bf16 tensors are ``np.uint16`` arrays of raw bfloat16 bits;
 * fp8 tensors are ``np.uint8`` arrays of OCP e4m3fn codes;
@@ -318,3 +319,45 @@ def indexer_prep(q_in, k_in, rope_cos, rope_sin, end_pos, fp8=True):
     qc, qs = act_quant_128(hadamard128(q, scaled=False), post)
     kc, ks = act_quant_128(hadamard128(k, scaled=False), post)
     return qc, qs, kc, ks, pos
+
+
+# --- MHA-form prefill attention (the `mask is not None` branch) ----------------
+# The MHA prefill excerpt on "DeepSeek-V3.2-Exp - Keep top-k positions": keys
+# and values are up-projected per head from the latent; each head's key is its
+# non-rotary part followed by the shared rotary key; scores are scaled, the
+# index mask (0 at the selected positions, -inf elsewhere, built by a scatter,
+# so a position listed twice counts once) and the causal mask are added, then
+# softmax and the weighted sum of the values.  Token s of a sequence is query
+# position s and sees key positions t <= s of the same sequence.
+
+def sparse_mha_prefill(q, k_nope, k_pe, v, indices, softmax_scale, rows=None):
+    """q [B,T,H,192] (non-rotary 128 then rotary 64), k_nope [B,T,H,128],
+    k_pe [B,T,64], v [B,T,H,128] as bf16 bits; indices [B,T,k] int32 (entries
+    outside 0..T-1 select nothing).  Returns (out [B,T,H,128] float64,
+    lse [B,T,H] float64, natural log); rows selects flattened b*T+s rows to
+    compute (others NaN).  A query with no position both selected and causal
+    gets out 0 and lse -inf."""
+    qf, kn, kp, vf = _as_f64(q), _as_f64(k_nope), _as_f64(k_pe), _as_f64(v)
+    idx = np.asarray(indices)
+    B, T, H = qf.shape[:3]
+    dv = vf.shape[-1]
+    out = np.full((B, T, H, dv), np.nan)
+    lse = np.full((B, T, H), np.nan)
+    todo = range(B * T) if rows is None else rows
+    for r in todo:
+        b, s = divmod(int(r), T)
+        sel = idx[b, s]
+        sel = np.unique(sel[(sel >= 0) & (sel < T)])
+        sel = sel[sel <= s]                                   # the causal mask
+        if sel.size == 0:
+            out[b, s], lse[b, s] = 0.0, -np.inf
+            continue
+        keys = np.concatenate([kn[b, sel], np.broadcast_to(kp[b, sel][:, None, :],
+                                                           (sel.size, H, kp.shape[-1]))], -1)
+        z = np.einsum("hd,nhd->hn", qf[b, s], keys) * float(softmax_scale)
+        m = z.max(-1, keepdims=True)
+        p = np.exp(z - m)
+        l = p.sum(-1, keepdims=True)
+        out[b, s] = np.einsum("hn,nhd->hd", p, vf[b, sel]) / l
+        lse[b, s] = (m + np.log(l))[:, 0]
+    return out, lse

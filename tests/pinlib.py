@@ -17,7 +17,11 @@ test_oracle_mutants.py).  What each pin compares against:
 * for the indexer input preparation: torch's complex multiply (RoPE), scipy's
   Hadamard matrix (rotation), torch's float8_e4m3fn cast (encoder), RoPE's
   relative-position property, the position convention of the k_cache write,
-  and e4m3's half-step error bound (block quantisation).
+  and e4m3's half-step error bound (block quantisation);
+* for the MHA-form prefill attention: torch scaled_dot_product_attention and
+  logsumexp with a boolean (selected and causal) mask, closed forms, and the
+  identity with the absorbed form (q_absorb -> mla -> up-projection) on
+  up-projected keys and values.
 """
 from __future__ import annotations
 
@@ -560,6 +564,103 @@ def check_prep_quantised_pipeline(lib, mod=oracle):
         assert np.allclose(sc, np.abs(want).max(-1) / 448.0, rtol=1e-6)
 
 
+# --- MHA-form prefill attention ----------------------------------------------
+
+def _mha_case(rng, B, T, H, k):
+    q = bf16(rng.standard_normal((B, T, H, 192)))
+    kn = bf16(rng.standard_normal((B, T, H, 128)))
+    kp = bf16(rng.standard_normal((B, T, 64)))
+    v = bf16(rng.standard_normal((B, T, H, 128)))
+    idx = rng.integers(-2, T + 2, (B, T, k)).astype(np.int32)   # some out of range, duplicates
+    return q, kn, kp, v, idx
+
+
+def check_mha_sdpa(lib, mod=oracle):
+    """Against torch scaled_dot_product_attention in float64 with a boolean mask
+    that is true at the selected positions (a set) that are also causal."""
+    rng = np.random.default_rng(81)
+    B, T, H, k = 2, 9, 3, 5
+    q, kn, kp, v, idx = _mha_case(rng, B, T, H, k)
+    scale = 0.07
+    out, lse = mod.sparse_mha_prefill(q, kn, kp, v, idx, scale)
+    for b in range(B):
+        mask = torch.zeros(T, T, dtype=torch.bool)
+        for s in range(T):
+            for t in idx[b, s]:
+                if 0 <= t <= s:
+                    mask[s, t] = True
+        qq = torch.from_numpy(bf16_val(q[b])).permute(1, 0, 2)          # [H,T,192]
+        kk = torch.cat([torch.from_numpy(bf16_val(kn[b])),
+                        torch.from_numpy(bf16_val(kp[b]))[:, None, :].expand(T, H, 64)], -1)
+        kk = kk.permute(1, 0, 2)
+        vv = torch.from_numpy(bf16_val(v[b])).permute(1, 0, 2)
+        for s in range(T):
+            if not mask[s].any():
+                assert not out[b, s].any() and np.all(np.isneginf(lse[b, s]))
+                continue
+            o = torch.nn.functional.scaled_dot_product_attention(
+                qq[:, s:s + 1], kk, vv, attn_mask=mask[s:s + 1], scale=scale)[:, 0]
+            assert np.allclose(out[b, s], o.numpy(), rtol=1e-10, atol=1e-12)
+            z = torch.einsum("hd,htd->ht", qq[:, s], kk) * scale
+            ref_lse = torch.logsumexp(z.masked_fill(~mask[s], float("-inf")), -1)
+            assert np.allclose(lse[b, s], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_mha_closed_forms(lib, mod=oracle):
+    """One selected causal position returns its value row for every head; a zero
+    query weighs the selected causal positions equally (their mean); a query
+    whose selections all lie in its future gets 0 and lse -inf."""
+    rng = np.random.default_rng(82)
+    B, T, H = 1, 6, 2
+    q, kn, kp, v, _ = _mha_case(rng, B, T, H, 1)
+    idx = np.full((B, T, 3), -1, np.int32)
+    idx[0, 4, :] = [2, 2, 5]           # position 2 twice, position 5 in the future
+    idx[0, 3, :] = [4, 5, -1]          # only future positions
+    out, lse = mod.sparse_mha_prefill(q, kn, kp, v, idx, 0.1)
+    assert np.array_equal(out[0, 4], bf16_val(v)[0, 2])
+    assert not out[0, 3].any() and np.all(np.isneginf(lse[0, 3]))
+    q0 = np.zeros_like(q)
+    idx[0, 5, :] = [0, 3, 5]
+    out0, lse0 = mod.sparse_mha_prefill(q0, kn, kp, v, idx, 0.1)
+    assert np.allclose(out0[0, 5], bf16_val(v)[0, [0, 3, 5]].mean(0), rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse0[0, 5], np.log(3.0))
+
+
+def check_mha_equals_absorbed(lib, mod=oracle):
+    """The prefill branch's MHA form against the decode branch's absorbed form on
+    the same latent cache ("Keep top-k positions" and "Apply sparse mask"): with
+    k_nope = W_k c and v = W_v c per head, MHA attention over the selection equals
+    absorbing the query (oracle.q_absorb), attending over the latent rows
+    (oracle.mla with the same index lists) and up-projecting (oracle.out_proj).
+    Small integers keep every bf16 operand exact on both sides."""
+    rng = np.random.default_rng(83)
+    B, T, H, k = 1, 7, 128, 4
+    scale = float(np.float32(0.03))
+    c = rng.integers(-2, 3, (B, T, 512)).astype(np.float64)      # latent rows
+    wk = rng.integers(-1, 2, (H, 128, 512)) * (rng.random((H, 128, 512)) < 0.05)
+    wv = rng.integers(-1, 2, (H, 128, 512)) * (rng.random((H, 128, 512)) < 0.05)
+    qn = rng.integers(-2, 3, (B, T, H, 128))
+    qp = rng.integers(-2, 3, (B, T, H, 64))
+    kp = rng.integers(-2, 3, (B, T, 64))
+    k_nope = np.einsum("hdc,btc->bthd", wk, c)
+    v = np.einsum("hdc,btc->bthd", wv, c)
+    assert np.abs(k_nope).max() <= 256 and np.abs(v).max() <= 256  # exact in bf16
+    idx = np.full((1, T, k), -1, np.int32)          # causal selections (the decode form's contract)
+    for t in range(T):
+        sel = rng.permutation(t + 1)[:k]
+        idx[0, t, :sel.size] = np.sort(sel)
+    out, lse = mod.sparse_mha_prefill(bf16(np.concatenate([qn, qp], -1)), bf16(k_nope), bf16(kp),
+                                      bf16(v), idx, scale)
+    wb = bf16(np.concatenate([wk, wv], 1))
+    qa = oracle.q_absorb(bf16(qn), wb)
+    assert np.abs(qa).max() <= 256 and np.array_equal(qa, np.round(qa))
+    x, lse_a = oracle.mla(bf16(qa), bf16(qp), bf16(c), bf16(kp), np.array([T], np.int32), scale,
+                          indices=idx, lib=lib)
+    y = np.einsum("bthc,hdc->bthd", x, wv)          # the up-projection, on the fp64 latent output
+    assert np.allclose(out, y, rtol=1e-9, atol=1e-9)
+    assert np.allclose(lse, lse_a, rtol=1e-9, atol=1e-9)
+
+
 ALL_CHECKS = [
     check_indexer_golden, check_fp8_decoding, check_bf16_decoding, check_single_head_matmul,
     check_fp8_single_head_matmul, check_head_sum_and_linearity, check_topk_bruteforce,
@@ -570,4 +671,5 @@ PREP_CHECKS = [
     check_prep_rope_complex, check_prep_hadamard, check_prep_e4m3_encoding, check_prep_act_quant,
     check_prep_positions, check_prep_relative_position, check_prep_quantised_pipeline,
 ]
-ALL_CHECKS += PREP_CHECKS
+MHA_CHECKS = [check_mha_sdpa, check_mha_closed_forms, check_mha_equals_absorbed]
+ALL_CHECKS += PREP_CHECKS + MHA_CHECKS

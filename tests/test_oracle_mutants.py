@@ -73,9 +73,10 @@ def test_mutant_is_caught(name, old, new, tmp_path):
     assert failures, f"mutant {name} passed every pin"
 
 
-# Planted mistakes in the Python part of the oracle (indexer input preparation):
+# Planted mistakes in the Python part of the oracle (indexer input preparation,
+# MHA-form prefill attention):
 # (name, text in oracle/__init__.py, replacement).  Each patched copy is loaded as
-# a module of its own and run against the preparation pins.
+# a module of its own and run against the preparation and MHA pins.
 PY_SRC = os.path.join(pinlib.ROOT, "oracle", "__init__.py")
 PY_MUTANTS = [
     ("rope_sign", "x1 * cos - x2 * sin", "x1 * cos + x2 * sin"),
@@ -92,6 +93,16 @@ PY_MUTANTS = [
     ("e4m3_subnormal_step", "m * 2.0 ** -9 if e == 0", "m * 2.0 ** -10 if e == 0"),
     ("amax_signed", "np.max(np.abs(u32), axis=-1)", "np.max(u32, axis=-1)"),
     ("post_scale_dropped", "(scale_u * np.float32(post_scale))", "(scale_u)"),
+    ("mha_no_causal_mask", "        sel = sel[sel <= s]                                   # the causal mask\n", ""),
+    ("mha_causal_strict", "sel = sel[sel <= s]", "sel = sel[sel < s]"),
+    ("mha_duplicates_counted", "sel = np.unique(sel[(sel >= 0) & (sel < T)])",
+     "sel = sel[(sel >= 0) & (sel < T)]"),
+    ("mha_rope_key_dropped", "np.broadcast_to(kp[b, sel][:, None, :],",
+     "np.broadcast_to(0 * kp[b, sel][:, None, :],"),
+    ("mha_scale_dropped", "* float(softmax_scale)", ""),
+    ("mha_lse_without_max", "lse[b, s] = (m + np.log(l))[:, 0]", "lse[b, s] = np.log(l)[:, 0]"),
+    ("mha_value_of_wrong_key", 'np.einsum("hn,nhd->hd", p, vf[b, sel])',
+     'np.einsum("hn,nhd->hd", p, vf[b, np.roll(sel, 1)])'),
 ]
 
 
@@ -106,7 +117,7 @@ def test_python_mutant_is_caught(name, old, new, tmp_path):
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     failures = []
-    for check in pinlib.PREP_CHECKS:
+    for check in pinlib.PREP_CHECKS + pinlib.MHA_CHECKS:
         try:
             check(None, mod=mod)
         except (AssertionError, ValueError, IndexError) as e:
