@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse-attn decode query-tok/s at 32K ctx; % HBM roofline; dense break-even"
 ROTATION_BYTES = 1 << 30
 
@@ -295,6 +296,28 @@ def bench_prep(dsa, torch, steps, dev, shapes=((1, 1), (64, 1), (1, 8192))):
     return res
 
 
+def bench_mha_prefill(dsa, torch, steps, dev, T=8192, k=2048):
+    """MHA-form prefill attention on one T-token sequence with k random causal
+    selections per query: time per call and MFMA roofline of the algorithmic
+    FLOPs (selected (query, key) pairs x 128 heads x (192 + 128) x 2)."""
+    from sparse_attention_indexer_amd import inputs
+    q, kn, kp, v = inputs.make_mha(1, T, seed=7, device=dev)
+    idx = inputs.make_indices(1, T, [T], k, seed=7, fill="random", device=dev)
+    out = torch.empty((1, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(int(dsa.lib().dsa_sparse_mha_prefill_workspace_size(1, T)), dtype=torch.uint8,
+                     device=dev)
+    fn = lambda i: dsa.sparse_mha_prefill(q, kn, kp, v, idx, 192 ** -0.5, out=out,
+                                          want_lse=False, workspace=ws)
+    fn(0)
+    ms = Timer(torch).time(fn, steps)
+    pairs = sum(min(k, s + 1) for s in range(T))
+    flop = pairs * 128 * (192 + 128) * 2
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": f"prefill_{T}_mha_bf16", "ms": round(ms, 4), "pairs": pairs,
+            "algorithmic_flop": flop, "achieved_tflops": round(tf, 1),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def break_even(contexts, sparse_ms, dense_ms):
     """Context where sparse and dense times cross (log-linear interpolation), or None."""
     diff = [s - d for s, d in zip(sparse_ms, dense_ms)]
@@ -400,6 +423,8 @@ def main(argv=None):
     line["projections"] = bench_projections(dsa, torch, B, T, max(20, args.steps // 4), dev)
     # The weight-free indexer input preparation (RoPE, rotation, fp8 quantisation).
     line["indexer_prep"] = bench_prep(dsa, torch, max(20, args.steps // 4), dev)
+    # The MHA-form prefill attention (per-head keys and values).
+    line["mha_prefill"] = bench_mha_prefill(dsa, torch, 5, dev)
 
     # --- sparse vs dense over context (batch 8, fp8 indexer) ---
     if not args.no_sweep:

@@ -194,6 +194,31 @@ int dsa_q_absorb(const void* q_nope, const void* wkv_b, int32_t B, int32_t T, vo
 int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t T, void* y,
                  hipStream_t stream);
 
+/* MHA-form prefill attention - the `mask is not None` branch of the attention
+ * excerpt on "DeepSeek-V3.2-Exp - Keep top-k positions": keys and values
+ * up-projected per head (by the caller), a head's key = its 128 non-rotary
+ * dims followed by the 64 rotary dims shared by all heads, scores times
+ * softmax_scale, plus the index mask (0 at the selected positions, -inf
+ * elsewhere; a position listed twice counts once) and the causal mask,
+ * softmax, weighted sum of the head's values.  B sequences of T tokens each,
+ * token s at position s (a prefill from position 0); query s sees key t iff t
+ * is in s's list and t <= s.
+ *   q      [B,T,128,192] bf16 (non-rotary 128 dims, then rotary 64)
+ *   k_nope [B,T,128,128] bf16   k_pe [B,T,64] bf16   v [B,T,128,128] bf16
+ *   topk_indices [B,T,k] int32: entries outside 0..T-1 select nothing
+ *   out    [B,T,128,128] bf16 (fp32 accumulation, round to nearest even)
+ *   lse    [B,T,128] fp32 natural-log sum of exp(z) over the kept keys, or NULL
+ * A query that keeps no key gets out = 0 and lse = -inf.  The workspace holds
+ * the selection as a bitmap (B * ceil(T/32) * roundup(T,64) words).
+ * Arithmetic: bf16 MFMA with fp32 accumulation, fp32 online softmax, the
+ * probabilities enter the value product as bf16.  1 <= B*T <= 2^24;
+ * softmax_scale positive and finite. */
+size_t dsa_sparse_mha_prefill_workspace_size(int32_t B, int32_t T);
+int dsa_sparse_mha_prefill(const void* q, const void* k_nope, const void* k_pe, const void* v,
+                           const int32_t* topk_indices, int32_t B, int32_t T, int32_t k,
+                           float softmax_scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Indexer input preparation - the weight-free steps of the Indexer.forward
  * excerpt on "DeepSeek-V3.2-Exp - Keep top-k positions" between the
  * projections (wq_b, wk + k_norm) and fp8_index: RoPE on the first 64 dims of

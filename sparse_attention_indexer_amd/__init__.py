@@ -68,6 +68,9 @@ def _bind(L):
                           ctypes.c_int),
         "dsa_q_absorb": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "dsa_out_proj": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+        "dsa_sparse_mha_prefill_workspace_size": ([i32, i32], sz),
+        "dsa_sparse_mha_prefill": ([vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp],
+                                   ctypes.c_int),
         "dsa_indexer_prep": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
                              ctypes.c_int),
     }
@@ -289,6 +292,35 @@ def indexer_prep(q_in, k_in, rope_cos, rope_sin, end_pos, k_cache, k_scale=None,
                                   _ptr(k_scale) if fp8 else None, _stream(stream)),
            "dsa_indexer_prep")
     return q_out, q_scale
+
+
+def sparse_mha_prefill(q, k_nope, k_pe, v, topk_indices, softmax_scale, out=None, lse=None,
+                       want_lse=True, workspace=None, stream=None):
+    """MHA-form prefill attention (per-head keys/values, index and causal masks):
+    (out [B,T,128,128] bf16, lse [B,T,128] fp32 or None)."""
+    B, T = q.shape[:2]
+    dev = q.device
+    k = topk_indices.shape[-1]
+    _need(q, "q", torch.bfloat16, (B, T, 128, 192), dev)
+    _need(k_nope, "k_nope", torch.bfloat16, (B, T, 128, 128), dev)
+    _need(k_pe, "k_pe", torch.bfloat16, (B, T, 64), dev)
+    _need(v, "v", torch.bfloat16, (B, T, 128, 128), dev)
+    _need(topk_indices, "topk_indices", torch.int32, (B, T, k), dev)
+    if out is None:
+        out = torch.empty((B, T, 128, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, 128, 128), dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, T, 128), dev)
+    L = lib()
+    workspace, nbytes = _workspace(int(L.dsa_sparse_mha_prefill_workspace_size(B, T)), dev,
+                                   workspace)
+    _check(L.dsa_sparse_mha_prefill(_ptr(q), _ptr(k_nope), _ptr(k_pe), _ptr(v), _ptr(topk_indices),
+                                    B, T, k, float(softmax_scale), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), nbytes, _stream(stream)),
+           "dsa_sparse_mha_prefill")
+    return out, lse
 
 
 def forward_workspace_size(B, T, S_max, k=MAX_TOPK) -> int:

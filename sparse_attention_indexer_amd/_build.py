@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "proj.hip", "prep.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "proj.hip", "prep.hip", "mha.hip"]
 
 
 def hipcc() -> str:

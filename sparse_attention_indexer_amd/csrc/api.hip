@@ -264,3 +264,25 @@ DSA_EXPORT int dsa_indexer_prep(const void* q_in, const void* k_in, const float*
                                   q_out, dtype == 1 ? q_scale : nullptr, k_cache,
                                   dtype == 1 ? k_scale : nullptr, stream);
 }
+
+DSA_EXPORT size_t dsa_sparse_mha_prefill_workspace_size(int32_t B, int32_t T) {
+  if (B < 1 || T < 1 || (long)B * T > (1L << 24)) return 0;
+  return dsa::mha_prefill_workspace_bytes(B, T);
+}
+
+DSA_EXPORT int dsa_sparse_mha_prefill(const void* q, const void* k_nope, const void* k_pe,
+                                      const void* v, const int32_t* topk_indices, int32_t B,
+                                      int32_t T, int32_t k, float softmax_scale, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (!q || !k_nope || !k_pe || !v || !topk_indices || !out) return kErrInvalid;
+  if (B < 1 || T < 1 || k < 1 || (long)B * T > (1L << 24)) return kErrInvalid;
+  if (!good_softmax_scale(softmax_scale)) return kErrInvalid;
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_pe) || !aligned16(v) ||
+      !aligned4(topk_indices) || !aligned16(out) || (lse && !aligned4(lse)))
+    return kErrMisaligned;
+  int st = check_workspace(workspace, workspace_bytes, dsa::mha_prefill_workspace_bytes(B, T));
+  if (st) return st;
+  return dsa::launch_mha_prefill(q, k_nope, k_pe, v, topk_indices, B, T, k, softmax_scale, out,
+                                 lse, workspace, stream);
+}

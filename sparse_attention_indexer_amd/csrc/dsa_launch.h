@@ -47,6 +47,12 @@ int launch_dense_mla(const void* q_nope, const void* q_pe, const void* kv, const
 int launch_q_absorb(const void* q_nope, const void* wkv_b, int rows, void* q_abs,
                     hipStream_t stream);
 int launch_out_proj(const void* x, const void* wkv_b, int rows, void* y, hipStream_t stream);
+// MHA-form prefill attention over per-head keys/values with a selection
+// bitmap built in the workspace.
+size_t mha_prefill_workspace_bytes(int B, int T);
+int launch_mha_prefill(const void* q, const void* k_nope, const void* k_pe, const void* v,
+                       const int32_t* idx, int B, int T, int k, float softmax_scale, void* out,
+                       float* lse, void* workspace, hipStream_t stream);
 // Indexer input preparation (RoPE, Hadamard rotation, fp8 block quantisation or
 // bf16 rounding, key append); dtype 0 = bf16, 1 = fp8.
 int launch_indexer_prep(const void* q_in, const void* k_in, const float* rope_cos,

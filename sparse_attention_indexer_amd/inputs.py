@@ -289,6 +289,19 @@ def make_prep(B: int, T: int, end_pos, S_max: int, kind: str = "normal", seed: i
     return q.to(bf), k.to(bf), cos.contiguous(), sin.contiguous(), end_pos_t
 
 
+def make_mha(B: int, T: int, seed: int = 0, device="cpu"):
+    """Inputs of the MHA-form prefill attention, standing in for keys and values
+    up-projected from the latent: q [B,T,128,192] (non-rotary 128, rotary 64),
+    k_nope [B,T,128,128], k_pe [B,T,64], v [B,T,128,128], all N(0,1) in bf16."""
+    g = _gen(seed, device)
+    bf = torch.bfloat16
+    q = _normal((B, T, N_HEADS, 192), g, device).to(bf)
+    kn = _normal((B, T, N_HEADS, 128), g, device).to(bf)
+    kp = _normal((B, T, D_ROPE), g, device).to(bf)
+    v = _normal((B, T, N_HEADS, 128), g, device).to(bf)
+    return q, kn, kp, v
+
+
 def make_proj(B: int, T: int, seed: int = 0, device="cpu"):
     """Inputs of the query absorption and output up-projection: q_nope
     [B,T,128,128] ~N(0,1), a synthetic wkv_b [128,256,512] ~N(0,1)/sqrt(fan-in)

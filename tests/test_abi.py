@@ -156,3 +156,33 @@ def test_indexer_prep_validation(L):
     for name in ("q", "k", "cos", "sin", "qo", "kc"):
         assert call(**{name: ctypes.c_void_p(P.value + 8)}) == -3, name
     assert call(ep=ODD) == -3 and call(qs=ODD) == -3 and call(ks=ODD) == -3
+
+
+def test_mha_prefill_validation(L):
+    """MHA prefill: null, empty, bad-scale, misaligned and short-workspace
+    arguments are rejected on the host."""
+    fn = L.dsa_sparse_mha_prefill
+    fn.restype = ctypes.c_int
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dsa_sparse_mha_prefill_workspace_size.restype = ctypes.c_size_t
+    L.dsa_sparse_mha_prefill_workspace_size.argtypes = [i32, i32]
+    need = L.dsa_sparse_mha_prefill_workspace_size(1, 100)
+    assert need == 4 * 4 * 128          # ceil(100/32) words x 128 padded queries
+    assert L.dsa_sparse_mha_prefill_workspace_size(0, 100) == 0
+
+    def call(**over):
+        a = dict(q=P, kn=P, kp=P, v=P, idx=P, B=1, T=100, k=8, s=0.07, out=P, lse=None, ws=P,
+                 nb=need)
+        a.update(over)
+        return fn(a["q"], a["kn"], a["kp"], a["v"], a["idx"], a["B"], a["T"], a["k"], a["s"],
+                  a["out"], a["lse"], a["ws"], a["nb"], None)
+
+    for name in ("q", "kn", "kp", "v", "idx", "out"):
+        assert call(**{name: None}) == -1, name
+    assert call(B=0) == -1 and call(T=0) == -1 and call(k=0) == -1
+    assert call(s=0.0) == -1 and call(s=float("nan")) == -1
+    assert call(nb=need - 1) == -4 and call(ws=None) == -1
+    for name in ("q", "kn", "kp", "v", "out"):
+        assert call(**{name: ctypes.c_void_p(P.value + 8)}) == -3, name
+    assert call(idx=ODD) == -3 and call(lse=ODD) == -3

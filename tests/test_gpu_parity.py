@@ -90,7 +90,9 @@ def assert_out_close(out_gpu, lse_gpu, o_ref, lse_ref, rows=None):
                 continue
             err = np.abs(og[b, t] - o_ref[b, t]).max()
             assert err <= OUT_TOL, f"row ({b},{t}): max |out error| {err:.3e}"
-            lerr = np.abs(lg[b, t] - lse_ref[b, t]).max()
+            same = lg[b, t] == lse_ref[b, t]  # also -inf on both sides (nothing kept)
+            with np.errstate(invalid="ignore"):
+                lerr = np.where(same, 0.0, np.abs(lg[b, t] - lse_ref[b, t])).max()
             assert lerr <= LSE_TOL, f"row ({b},{t}): max |lse error| {lerr:.3e}"
 
 
@@ -787,3 +789,49 @@ def test_indexer_prep_feeds_index_scores():
             bound = int(ep[b]) - T + t
             g, r = got[b, t, :bound + 1], ref[b, t, :bound + 1]
             assert np.abs(g - r).max() <= 2e-2 * np.abs(r).max()
+
+
+
+# --- MHA-form prefill attention ------------------------------------------------------
+
+def _mha_indices(B, T, k, kind, seed):
+    """Index lists: "random" (any of 0..T+2, -1, ...: duplicates, future and out
+    of range entries), or make_indices' causal "random" / "last" selections."""
+    if kind == "messy":
+        g = torch.Generator().manual_seed(seed)
+        return torch.randint(-3, T + 3, (B, T, k), generator=g, dtype=torch.int32).to(DEV)
+    return inputs.make_indices(B, T, [T] * B, k, seed=seed, fill=kind, device=DEV)
+
+
+def _mha_check(B, T, k, kind, seed, rows=None):
+    m = dsa()
+    q, kn, kp, v = inputs.make_mha(B, T, seed=seed, device=DEV)
+    idx = _mha_indices(B, T, k, kind, seed)
+    scale = 192 ** -0.5
+    out, lse = m.sparse_mha_prefill(q, kn, kp, v, idx, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.sparse_mha_prefill(inputs.to_numpy(q), inputs.to_numpy(kn),
+                                               inputs.to_numpy(kp), inputs.to_numpy(v),
+                                               idx.cpu().numpy(), scale, rows=rows)
+    assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
+
+
+@pytest.mark.parametrize("B,T,k,kind", [
+    (2, 100, 16, "messy"),    # duplicates, future and out-of-range entries; ragged 64-query tail
+    (1, 37, 64, "last"),      # fewer tokens than one query block
+    (1, 200, 2048, "random"), # k >= T: every causal position selected (dense causal)
+    (2, 130, 24, "random"),   # causal random selections, two sequences
+])
+def test_mha_prefill_vs_oracle(B, T, k, kind):
+    """MHA-form prefill (selection bitmap + masked tiles) against the oracle on
+    every query row."""
+    banner(f"mha prefill B={B} T={T} k={k} {kind}")
+    _mha_check(B, T, k, kind, seed=B * 1000 + T)
+
+
+def test_mha_prefill_8192_sampled():
+    """The timed size, one 8192-token sequence with 2048 random causal
+    selections per query, on sampled rows (first and last of query blocks, the
+    first row with more than k candidates, the last row)."""
+    banner("mha prefill T=8192 sampled")
+    _mha_check(1, 8192, 2048, "random", seed=91, rows=[0, 1, 63, 64, 2047, 2048, 5000, 8191])
