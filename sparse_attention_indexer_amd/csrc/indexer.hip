@@ -30,20 +30,32 @@ constexpr int kIdxTile = 16;
 #endif
 
 // Key fragment of one 16-key tile for this lane: 64 bytes (bf16) or 32 (fp8)
-// of key s, starting at dim 32*g.
+// of key s, starting at dim 32*g, and (fp8) the key's scale, loaded with it so
+// the epilogue never waits on a load of its own.
 template <bool kFp8>
 struct KeyFrag {
   uint4 v[kFp8 ? 2 : 4];
+  float ks;
 };
 
 template <bool kFp8>
-__device__ __forceinline__ KeyFrag<kFp8> load_key_frag(const uint8_t* kbase, int s, int g) {
+__device__ __forceinline__ KeyFrag<kFp8> load_key_frag(const uint8_t* kbase, const float* ksrow,
+                                                       int s, int g) {
   KeyFrag<kFp8> f;
   constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
   const uint8_t* p = kbase + (size_t)s * kRowBytes + g * (kRowBytes / 4);
 #pragma unroll
   for (int u = 0; u < (kFp8 ? 2 : 4); ++u) f.v[u] = ldg16(p + 16 * u);
+  f.ks = kFp8 ? ksrow[s] : 1.0f;
   return f;
+}
+
+// Sum over the 4 lanes l%16 + 16j (the four dim groups of one key's dot).
+__device__ __forceinline__ float idx_group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
 template <bool kFp8>
@@ -73,10 +85,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int g = lane >> 4;     // lane group: which 32 of the 128 dims this lane carries
   const int r16 = lane & 15;   // head within an M-tile (A) / key within a tile (B)
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + (size_t)b * S_max * kRowBytes;
+  const float* ksrow = kFp8 ? k_scale + (size_t)b * S_max : nullptr;
   auto tile_start = [&](int tile) { return blk_start + (tile * kIdxWaves + wave) * kIdxTile; };
 
   // First key tile in flight before anything else.
-  KeyFrag<kFp8> cur = load_key_frag<kFp8>(kbase, min(tile_start(0) + r16, bound), g);
+  KeyFrag<kFp8> cur = load_key_frag<kFp8>(kbase, ksrow, min(tile_start(0) + r16, bound), g);
 
   // Query -> LDS: thread tid copies a quarter of head tid/4.
   {
@@ -113,7 +126,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
                                                   g * (kRowBytes / 4) + 16 * u);
 
   float* orow = out + (size_t)row * S_max;
-  const float* ksrow = kFp8 ? k_scale + (size_t)b * S_max : nullptr;
 
   for (int tile = 0; tile < tiles_per_wave; ++tile) {
     const int s0 = tile_start(tile);
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const int s0n = tile_start(tile + 1);
     const bool has_next = tile + 1 < tiles_per_wave && s0n <= bound;
     KeyFrag<kFp8> nxt;
-    if (has_next) nxt = load_key_frag<kFp8>(kbase, min(s0n + r16, bound), g);
+    if (has_next) nxt = load_key_frag<kFp8>(kbase, ksrow, min(s0n + r16, bound), g);
 
     float v = 0.f;
     if constexpr (!kFp8) {
@@ -150,11 +162,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(
         for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
       }
     }
-    v += xor_shfl(v, 16);
-    v += xor_shfl(v, 32);
+    v = idx_group_sum(v);
     const int s = s0 + r16;
     if (g == 0 && s <= bound) {
-      if constexpr (kFp8) v *= ksrow[s];
+      if constexpr (kFp8) v *= cur.ks;
       orow[s] = v * scale;
     }
     if (has_next) cur = nxt;
