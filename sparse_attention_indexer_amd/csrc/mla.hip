@@ -93,10 +93,6 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return pack2_bf16(a, b); }
-__device__ __forceinline__ uint32_t pack_half(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
 
 // Row copies issued through inline asm: global_load_lds
 // with M0 = the LDS destination of lane 0 (lane i writes 16 bytes at M0 +
@@ -308,14 +304,19 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     // Lazy rescaling: the reference m_run moves only when this tile's max
     // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
     // below 2^kRescaleSlack and the accumulators are rarely touched.
+    // Until a head has seen a valid row its accumulators and sum are zero, so
+    // its first reference needs no rescaling.
     const bool grow = mx > m_run + kRescaleSlack;
+    const bool fresh = m_run == -INFINITY;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      const float alpha = fresh ? 0.f : exp2f(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
+      if (__ballot(grow && !fresh) != 0) {
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
+        for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
+      }
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
@@ -368,26 +369,14 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     if (lse != nullptr && g == 0)
       lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    // Partial output o/l in fp16, scaled by a power of two that puts its
-    // largest element in [2^14, 2^15) (fp16 keeps 11 significant bits at any
-    // magnitude of the cache values), plus (max, sum, 1/scale) in fp32.
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float amax = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[ct][i]));
-    amax = group_max(amax) * inv;
-    int e;
-    frexpf(amax, &e);  // amax < 2^e
-    e = min(max(e, -100), 100);
-    const float sc = ldexpf(inv, 15 - e);
+    // Partial output: the unnormalised accumulator rounded to bf16 (the
+    // range of fp32, so no scaling is needed), plus (max, sum) in fp32.
     uint16_t* prow = part_o + ((size_t)X * kHeads + head) * kDc + 4 * g;
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct)
       *reinterpret_cast<uint2*>(prow + ct * 16) =
-          uint2{pack_half(o[ct][0] * sc, o[ct][1] * sc), pack_half(o[ct][2] * sc, o[ct][3] * sc)};
-    if (g == 0) part_ml[(size_t)X * kHeads + head] = float4{m_run, l_tot, ldexpf(1.f, e - 15), 0.f};
+          uint2{pack_bf16(o[ct][0], o[ct][1]), pack_bf16(o[ct][2], o[ct][3])};
+    if (g == 0) part_ml[(size_t)X * kHeads + head] = float4{m_run, l_tot, 0.f, 0.f};
   }
 }
 
@@ -438,7 +427,7 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   __shared__ __align__(16) uint8_t s_ring[kWdNbuf * kWdTileBytes];
   __shared__ __align__(16) uint4 s_p[2][kHeads / 16][64];  // P fragments per head tile
   __shared__ float s_alpha[2][kHeads];                    // a tile's rescale per head
-  __shared__ float s_fin[2 + kWdWaves][kHeads];         // m, l, then per-wave amax
+  __shared__ float s_fin[2][kHeads];                    // m, l per head
   __shared__ __align__(8) uint8_t s_vmask[kWdNbuf][kWdWaves];  // bit r: row 4w+r is valid
   __shared__ __align__(16) uint4 s_qpe[2][kWdWaves][64];      // rope-part query fragments
   __shared__ int s_grow[2];                             // last tile (per parity) whose max moved
@@ -644,7 +633,8 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
       // Lazy rescaling: the reference moves only when the tile's max exceeds
       // it by more than kRescaleSlack, so probabilities stay below 2^8.
       const bool grow = mx > m_run + kRescaleSlack;
-      const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.f;
+      const bool fresh = m_run == -INFINITY;
+      const float alpha = grow ? (fresh ? 0.f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.f;
       m_run = grow ? mx : m_run;
       l_part *= alpha;
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -660,7 +650,8 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
       s_p[cp][wave][lane] = uint4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
                                   pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
       if (g == 0) s_alpha[cp][head] = alpha;
-      if (__ballot(grow) != 0 && lane == 0) s_grow[cp] = it;
+      // A head's first reference needs no rescaling (its accumulators are zero).
+      if (__ballot(grow && !fresh) != 0 && lane == 0) s_grow[cp] = it;
     }
   }
 
@@ -694,56 +685,58 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
       }
     }
   } else {
-    // Partial o/l in fp16 with a per-(split, head) power-of-two scale that puts
-    // the largest of its 512 elements in [2^14, 2^15): each wave's maximum over
-    // its 64 dims goes through LDS.
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      float amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < kWdCt; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[j][h][i]));
-      amax = group_max(amax) * inv[h];
-      if (g == 0) s_fin[2 + wave][16 * h + r16] = amax;
-    }
-    lds_barrier();
+    // Partial output: the unnormalised accumulators rounded to bf16, plus
+    // (max, sum) per head in fp32.
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       const int hd = 16 * h + r16;
-      float amax = s_fin[2][hd];
-#pragma unroll
-      for (int w = 1; w < kWdWaves; ++w) amax = fmaxf(amax, s_fin[2 + w][hd]);
-      int e;
-      frexpf(amax, &e);  // amax < 2^e
-      e = min(max(e, -100), 100);
-      const float sc = ldexpf(inv[h], 15 - e);
       uint16_t* prow = part_o + ((size_t)X * kHeads + hd) * kDc + 4 * g;
 #pragma unroll
       for (int j = 0; j < kWdCt; ++j) {
         const int ct = kWdCt * wave + j;
         *reinterpret_cast<uint2*>(prow + ct * 16) =
-            uint2{pack_half(o[j][h][0] * sc, o[j][h][1] * sc),
-                  pack_half(o[j][h][2] * sc, o[j][h][3] * sc)};
+            uint2{pack_bf16(o[j][h][0], o[j][h][1]), pack_bf16(o[j][h][2], o[j][h][3])};
       }
       if (wave == 0 && g == 0)
-        part_ml[(size_t)X * kHeads + hd] =
-            float4{s_fin[0][hd], s_fin[1][hd], ldexpf(1.f, e - 15), 0.f};
+        part_ml[(size_t)X * kHeads + hd] = float4{s_fin[0][hd], s_fin[1][hd], 0.f, 0.f};
     }
   }
 }
 
-__device__ __forceinline__ float half_lo(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Maximum and sum over the 64 lanes of a wave (all lanes active), returned in
+// every lane: an inclusive scan by DPP row shifts and row broadcasts, read
+// back from lane 63.  Lanes a shift leaves without a source take the
+// identity (-inf for the maximum, 0 for the sum).
+__device__ __forceinline__ float wave_max_f(float v) {
+  const int id = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-__device__ __forceinline__ float half_hi(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Merge the per-split partial outputs of one (row, head) per 128-thread block;
 // each thread owns 4 latent dims.  The splits are read 32 at a time (their
-// loads all in flight together), with an online maximum across batches, so a
-// decode row with up to 32 splits costs one round trip to memory.
+// loads all in flight together), so a decode row with up to 32 splits costs
+// one round trip to memory.  Wave 0 turns the batch's (max, sum) pairs into
+// one weight per split, 2^(its max - M) with M the running maximum, and the
+// factor that rescales what was accumulated before; every thread then only
+// reads the weights and accumulates.
 __global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float4* __restrict__ part_ml,
                                                           int n_splits, uint16_t* __restrict__ out,
@@ -751,56 +744,65 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __rest
   constexpr int kBatch = 32;
   const int rh = blockIdx.x;  // row * 128 + head
   const int row = rh / kHeads, head = rh - row * kHeads;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const float4* ml = part_ml + (size_t)row * n_splits * kHeads + head;
   const int c0 = tid * 4;
   const uint16_t* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
   const size_t stride = (size_t)kHeads * kDc;
+  __shared__ __align__(16) float s_w[2][kBatch];  // by batch parity
+  __shared__ float s_alpha[2];
+  __shared__ float s_inv;
   float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f, M = -INFINITY;
-  __shared__ float4 s_ml[kBatch];
-  for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
-    // The batch's partials and its (max, sum, 1/scale) triples, all in
-    // flight at once; the triples go through LDS to every thread.
+  float L = 0.f, M = -INFINITY;  // kept by wave 0
+  int par = 0;
+  for (int s0 = 0; s0 < n_splits; s0 += kBatch, par ^= 1) {
     uint2 a[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
       a[u] = *reinterpret_cast<const uint2*>(src + (size_t)min(s0 + u, n_splits - 1) * stride);
-    if (tid < kBatch) s_ml[tid] = ml[(size_t)min(s0 + tid, n_splits - 1) * kHeads];
+    if (tid < 64) {
+      const int s = min(s0 + min(lane, kBatch - 1), n_splits - 1);
+      const float4 v = ml[(size_t)s * kHeads];
+      const bool valid = lane < kBatch && s0 + lane < n_splits && v.y > 0.f;
+      const float mb = fmaxf(M, wave_max_f(valid ? v.x : -INFINITY));
+      // Nothing was accumulated while M was -inf, so the factor is then moot.
+      const float alpha = M == -INFINITY ? 0.f : exp2f(M - mb);
+      const float w = valid ? exp2f(v.x - mb) : 0.f;
+      L = L * alpha + wave_sum_f(w * v.y);
+      M = mb;
+      if (lane < kBatch) s_w[par][lane] = w;
+      if (lane == 0) s_alpha[par] = alpha;
+    }
+    // One barrier per batch: a wave can only refill this parity's weights
+    // after every wave has passed the next batch's barrier.
     __syncthreads();
-    float4 v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = s_ml[u];
-    __syncthreads();  // s_ml is refilled by the next batch
-    float mb = M;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (s0 + u < n_splits && v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
-    if (mb == -INFINITY) continue;  // nothing kept so far
-    const float alpha = M == -INFINITY ? 0.f : exp2f(M - mb);
-    M = mb;
-    L *= alpha;
+    const float alpha = s_alpha[par];
     acc.x *= alpha;
     acc.y *= alpha;
     acc.z *= alpha;
     acc.w *= alpha;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      // Split weight: its sum times 2^(its max - M); the stored partial is
-      // o/sum times a power-of-two scale whose inverse is v.z.
-      const float w = (s0 + u < n_splits && v[u].y > 0.f) ? v[u].y * exp2f(v[u].x - M) : 0.f;
-      const float ws = w * v[u].z;
-      L += w;
-      acc.x += half_lo(a[u].x) * ws;
-      acc.y += half_hi(a[u].x) * ws;
-      acc.z += half_lo(a[u].y) * ws;
-      acc.w += half_hi(a[u].y) * ws;
+    for (int u4 = 0; u4 < kBatch; u4 += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&s_w[par][u4]);
+      const float ws[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 av = a[u4 + j];
+        acc.x += bf16_lo(av.x) * ws[j];
+        acc.y += bf16_hi(av.x) * ws[j];
+        acc.z += bf16_lo(av.y) * ws[j];
+        acc.w += bf16_hi(av.y) * ws[j];
+      }
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (tid == 0) {
+    s_inv = L > 0.f ? 1.f / L : 0.f;
+    if (lse != nullptr) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  const float inv = s_inv;
   *reinterpret_cast<uint2*>(out + (size_t)rh * kDc + c0) =
       uint2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
-  if (lse != nullptr && tid == 0) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }

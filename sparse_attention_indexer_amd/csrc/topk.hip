@@ -221,7 +221,7 @@ struct TopkShared {
   uint32_t ncand;
 };
 
-__device__ void full_row_topk(const float* __restrict__ x, int n, int k,
+__device__ __noinline__ void full_row_topk(const float* __restrict__ x, int n, int k,
                               int32_t* __restrict__ o, TopkShared& sh) {
   uint32_t* s_keys = sh.keys;
   uint32_t* s_hist = sh.hist;
@@ -467,6 +467,46 @@ __device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
   }
 }
 
+// Ordered output from the two position bitmaps (winners strictly above the
+// threshold in `sure`, keys equal to it in `eq`, of which the need_eq
+// smallest positions are kept).  bitmap_prefixes stores, per 32-position
+// word, the number of set `sure` bits before the word (bits 0..15) and of
+// set `eq` bits before it (bits 16..31), each capped at 65535 (both are only
+// compared with k <= 2048); thread t owns a run of consecutive words.  The
+// caller synchronises before reading `pre`.  A winner then finds its output
+// slot from three LDS words, with no loop over set bits.
+__device__ __forceinline__ void bitmap_prefixes(const uint32_t* sure, const uint32_t* eq,
+                                                uint32_t* pre, int nwords, uint32_t* s_wave) {
+  const int tid = threadIdx.x;
+  const int wpt = (nwords + kTkThreads - 1) / kTkThreads;
+  const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int w = w0; w < w1; ++w) {
+    n_gt += (uint32_t)__popc(sure[w]);
+    n_eq += (uint32_t)__popc(eq[w]);
+  }
+  uint32_t gt, eqb, tot_gt, tot_eq;
+  block_exclusive_scan2(n_gt, n_eq, s_wave, gt, eqb, tot_gt, tot_eq);
+  for (int w = w0; w < w1; ++w) {
+    pre[w] = min(gt, 0xFFFFu) | (min(eqb, 0xFFFFu) << 16);
+    gt += (uint32_t)__popc(sure[w]);
+    eqb += (uint32_t)__popc(eq[w]);
+  }
+}
+
+// Output slot of position p (marked in `sure` when above the threshold, else
+// in `eq`), or -1 when p is an equal key beyond the first need_eq.
+__device__ __forceinline__ int winner_slot(const uint32_t* sure, const uint32_t* eq,
+                                           const uint32_t* pre, uint32_t p, bool above,
+                                           uint32_t need_eq) {
+  const uint32_t w = p >> 5, below = (1u << (p & 31)) - 1u;
+  const uint32_t pw = pre[w];
+  const uint32_t n_gt = (pw & 0xFFFFu) + (uint32_t)__popc(sure[w] & below);
+  const uint32_t n_eq = (pw >> 16) + (uint32_t)__popc(eq[w] & below);
+  if (above) return (int)(n_gt + min(n_eq, need_eq));
+  return n_eq < need_eq ? (int)(n_gt + n_eq) : -1;
+}
+
 // ---------------------------------------------------------------------------
 // Up to 1024 rows: each row is spread over workgroups of 512 * kSpPer
 // positions (topk_split_kernel), and a second launch with one workgroup per
@@ -536,7 +576,7 @@ struct SplitShared {
   uint32_t hist2[kHistWords];
   uint32_t sure[kSpMaxN / 32];
   uint32_t eq[kSpMaxN / 32];
-  int32_t outs[kMaxK];
+  uint32_t pre[kSpMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
   uint32_t wave[2 * kTkWaves];
   uint32_t sel[2];
   uint32_t small[kWave];
@@ -552,7 +592,7 @@ union SplitLds {
 // registers: entry tid + 512u of the set is (ek[u], ep[u]) for every
 // tid + 512u < M.  Writes the row's ordered output.
 template <int kEnt>
-__device__ void split_select(uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt], int M, int n,
+__device__ __forceinline__ void split_select(uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt], int M, int n,
                              int k, int32_t* __restrict__ o, uint32_t L, SplitShared& sh) {
   const int tid = threadIdx.x;
   const int nwords = (n + 31) >> 5;
@@ -646,39 +686,21 @@ __device__ void split_select(uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt], i
     }
   }
   lds_barrier();
-  // Ordered output: thread t owns bitmap words [w0, w1).
-  const int wpt = (nwords + kTkThreads - 1) / kTkThreads;
-  const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int w = w0; w < w1; ++w) {
-    n_gt += (uint32_t)__popc(sh.sure[w]);
-    n_eq += (uint32_t)__popc(sh.eq[w]);
-  }
-  uint32_t gt, eqb, tot_gt, tot_eq;
-  block_exclusive_scan2(n_gt, n_eq, sh.wave, gt, eqb, tot_gt, tot_eq);
-  for (int w = w0; w < w1; ++w) {
-    const uint32_t sw = sh.sure[w], ew = sh.eq[w];
-    uint32_t bits = sw | ew;
-    while (bits != 0u) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int32_t p = 32 * w + b;
-      if ((sw >> b) & 1u) {
-        const uint32_t at = gt + min(eqb, need_eq);
-        if (at < (uint32_t)k) sh.outs[at] = p;
-        ++gt;
-      } else {
-        if (eqb < need_eq && gt + eqb < (uint32_t)k) sh.outs[gt + eqb] = p;
-        ++eqb;
-      }
+  // Ordered output: each winner writes its position at its rank among the
+  // winners by position.
+  bitmap_prefixes(sh.sure, sh.eq, sh.pre, nwords, sh.wave);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < kEnt; ++u) {
+    if (tid + kTkThreads * u < (int)M && ek[u] >= thr) {
+      const int at = winner_slot(sh.sure, sh.eq, sh.pre, ep[u], ek[u] > thr, need_eq);
+      if (at >= 0 && at < k) o[at] = (int32_t)ep[u];
     }
   }
-  lds_barrier();
-  for (int i = tid; i < k; i += kTkThreads) o[i] = sh.outs[i];
 }
 
 // Step 3 for the row's last workgroup: the list -> registers -> selection.
-__device__ void split_finish(const float* __restrict__ x, int n, int k, int32_t* __restrict__ o,
+__device__ __forceinline__ void split_finish(const float* __restrict__ x, int n, int k, int32_t* __restrict__ o,
                              const uint32_t* count, const uint2* __restrict__ list, uint32_t L,
                              SplitLds& lds) {
   const int tid = threadIdx.x;
@@ -858,7 +880,7 @@ struct LeanShared {
   uint16_t cp[kLeanCap];       // their positions
   uint32_t sure[kLeanMaxN / 32];
   uint32_t eq[kLeanMaxN / 32];
-  int32_t outs[kMaxK];         // the output row, staged
+  uint32_t pre[kLeanMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
   uint32_t ncw[kTkWaves];
   uint32_t wave[2 * kTkWaves];
   uint32_t sel[2];
@@ -1041,35 +1063,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
         else if (kk == thr) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
       }
       lds_barrier();
-      // 4. Ordered output: thread t owns 32-bit words 2t and 2t+1.
-      const int nwords = (n + 31) >> 5;
-      const int w0 = min(2 * tid, nwords), w1 = min(w0 + 2, nwords);
-      uint32_t n_gt = 0, n_eq = 0;
-      for (int w = w0; w < w1; ++w) {
-        n_gt += (uint32_t)__popc(sh.sure[w]);
-        n_eq += (uint32_t)__popc(sh.eq[w]);
-      }
-      uint32_t gt, eqb, tot_gt, tot_eq;
-      block_exclusive_scan2(n_gt, n_eq, sh.wave, gt, eqb, tot_gt, tot_eq);
-      for (int w = w0; w < w1; ++w) {
-        const uint32_t sw = sh.sure[w], ew = sh.eq[w];
-        uint32_t bits = sw | ew;
-        while (bits != 0u) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1u;
-          const int32_t p = 32 * w + b;
-          if ((sw >> b) & 1u) {
-            const uint32_t at = gt + min(eqb, need_eq);
-            if (at < (uint32_t)k) sh.outs[at] = p;
-            ++gt;
-          } else {
-            if (eqb < need_eq && gt + eqb < (uint32_t)k) sh.outs[gt + eqb] = p;
-            ++eqb;
-          }
+      // 4. Ordered output: each winner writes its position at its rank.
+      bitmap_prefixes(sh.sure, sh.eq, sh.pre, (n + 31) >> 5, sh.wave);
+      lds_barrier();
+      for (int j = lane; j < my_nc; j += kWave) {
+        const uint32_t kk = sh.ck[region + j], p = sh.cp[region + j];
+        if (kk >= thr) {
+          const int at = winner_slot(sh.sure, sh.eq, sh.pre, p, kk > thr, need_eq);
+          if (at >= 0 && at < k) o[at] = (int32_t)p;
         }
       }
-      lds_barrier();
-      for (int i = tid; i < k; i += kTkThreads) o[i] = sh.outs[i];
     }
   }
   if (!ok) {
