@@ -73,6 +73,10 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 }
 
 // Exclusive prefix sums over the block of two per-thread values, plus totals.
+// kLdsOnly: the barrier is an LDS-only one (global accesses in flight stay in
+// flight) and there is no trailing barrier, for callers that synchronise
+// before s_wave is written again.
+template <bool kLdsOnly = false>
 __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* s_wave,
                                                       uint32_t& ex_a, uint32_t& ex_b,
                                                       uint32_t& tot_a, uint32_t& tot_b) {
@@ -82,7 +86,8 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
     s_wave[wave] = ia;
     s_wave[kTkWaves + wave] = ib;
   }
-  __syncthreads();
+  if constexpr (kLdsOnly) lds_barrier();
+  else __syncthreads();
   uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int w4 = 0; w4 < kTkWaves; w4 += 4) {
@@ -97,7 +102,7 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
       sb += vb[u];
     }
   }
-  __syncthreads();
+  if constexpr (!kLdsOnly) __syncthreads();
   ex_a = pa + ia - a;
   ex_b = pb + ib - b;
   tot_a = sa;
@@ -486,7 +491,7 @@ __device__ __forceinline__ void bitmap_prefixes(const uint32_t* sure, const uint
     n_eq += (uint32_t)__popc(eq[w]);
   }
   uint32_t gt, eqb, tot_gt, tot_eq;
-  block_exclusive_scan2(n_gt, n_eq, s_wave, gt, eqb, tot_gt, tot_eq);
+  block_exclusive_scan2<true>(n_gt, n_eq, s_wave, gt, eqb, tot_gt, tot_eq);
   for (int w = w0; w < w1; ++w) {
     pre[w] = min(gt, 0xFFFFu) | (min(eqb, 0xFFFFu) << 16);
     gt += (uint32_t)__popc(sure[w]);
