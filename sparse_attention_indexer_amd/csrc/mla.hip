@@ -370,11 +370,13 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
       lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     // Partial output: the unnormalised accumulator rounded to bf16 (the
-    // range of fp32, so no scaling is needed), plus (max, sum) in fp32.
-    uint16_t* prow = part_o + ((size_t)X * kHeads + head) * kDc + 4 * g;
+    // range of fp32, so no scaling is needed), plus (max, sum) in fp32.  The
+    // layout is [item][16-dim tile][head][16]: each store instruction writes
+    // 512 contiguous bytes (the wave's 16 heads), i.e. whole cache lines.
+    uint16_t* prow = part_o + (size_t)X * kHeads * kDc + head * 16 + 4 * g;
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct)
-      *reinterpret_cast<uint2*>(prow + ct * 16) =
+      *reinterpret_cast<uint2*>(prow + ct * kHeads * 16) =
           uint2{pack_bf16(o[ct][0], o[ct][1]), pack_bf16(o[ct][2], o[ct][3])};
     if (g == 0) part_ml[(size_t)X * kHeads + head] = float4{m_run, l_tot, 0.f, 0.f};
   }
@@ -690,11 +692,11 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       const int hd = 16 * h + r16;
-      uint16_t* prow = part_o + ((size_t)X * kHeads + hd) * kDc + 4 * g;
+      uint16_t* prow = part_o + (size_t)X * kHeads * kDc + hd * 16 + 4 * g;  // [item][tile][head][16]
 #pragma unroll
       for (int j = 0; j < kWdCt; ++j) {
         const int ct = kWdCt * wave + j;
-        *reinterpret_cast<uint2*>(prow + ct * 16) =
+        *reinterpret_cast<uint2*>(prow + ct * kHeads * 16) =
             uint2{pack_bf16(o[j][h][0], o[j][h][1]), pack_bf16(o[j][h][2], o[j][h][3])};
       }
       if (wave == 0 && g == 0)
@@ -730,39 +732,47 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Merge the per-split partial outputs of one (row, head) per 128-thread block;
-// each thread owns 4 latent dims.  The splits are read 32 at a time (their
-// loads all in flight together), so a decode row with up to 32 splits costs
-// one round trip to memory.  Wave 0 turns the batch's (max, sum) pairs into
-// one weight per split, 2^(its max - M) with M the running maximum, and the
-// factor that rescales what was accumulated before; every thread then only
-// reads the weights and accumulates.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                          const float4* __restrict__ part_ml,
-                                                          int n_splits, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
+// Merge the per-split partial outputs of four heads of one row per 512-thread
+// block.  Thread t owns 4 latent dims of one head: 16-dim tile t/16, head
+// t/4 % 4, quarter t % 4, so a wave's load of one split covers 4 tiles x 4
+// heads x 32 bytes, i.e. four whole 128-byte lines of the [tile][head][16]
+// partial layout.  The splits are read 32 at a time (their loads all in flight
+// together), so a decode row with up to 32 splits costs one round trip to
+// memory.  Wave q < 4 turns the batch's (max, sum) pairs of head q into one
+// weight per split, 2^(its max - M) with M the running maximum, and the factor
+// that rescales what was accumulated before; every thread then only reads its
+// head's weights and accumulates.
+constexpr int kCbHeads = 4;
+constexpr int kCbThreads = 512;
+static_assert(kCbThreads == (kDc / 16) * kCbHeads * 4 && kHeads % kCbHeads == 0,
+              "one thread per (16-dim tile, head, quarter of the tile)");
+__global__ __launch_bounds__(kCbThreads) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                                 const float4* __restrict__ part_ml,
+                                                                 int n_splits, uint16_t* __restrict__ out,
+                                                                 float* __restrict__ lse) {
   constexpr int kBatch = 32;
-  const int rh = blockIdx.x;  // row * 128 + head
-  const int row = rh / kHeads, head = rh - row * kHeads;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const float4* ml = part_ml + (size_t)row * n_splits * kHeads + head;
-  const int c0 = tid * 4;
-  const uint16_t* src = part_o + ((size_t)row * n_splits * kHeads + head) * kDc + c0;
-  const size_t stride = (size_t)kHeads * kDc;
-  __shared__ __align__(16) float s_w[2][kBatch];  // by batch parity
-  __shared__ float s_alpha[2];
-  __shared__ float s_inv;
+  constexpr int kGroups = kHeads / kCbHeads;
+  const int row = blockIdx.x / kGroups, h0 = (blockIdx.x - row * kGroups) * kCbHeads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ct = tid >> 4, q = (tid >> 2) & 3, quarter = tid & 3;
+  const int head = h0 + q;
+  const size_t item0 = (size_t)row * n_splits;
+  const uint16_t* src = part_o + item0 * kHeads * kDc + ((size_t)ct * kHeads + head) * 16 + 4 * quarter;
+  const size_t stride = (size_t)kHeads * kDc;  // one split
+  __shared__ __align__(16) float s_w[2][kCbHeads][kBatch];  // by batch parity
+  __shared__ float s_alpha[2][kCbHeads];
+  __shared__ float s_inv[kCbHeads];
   float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f, M = -INFINITY;  // kept by wave 0
+  float L = 0.f, M = -INFINITY;  // kept by wave q < 4 for head h0 + q
   int par = 0;
   for (int s0 = 0; s0 < n_splits; s0 += kBatch, par ^= 1) {
     uint2 a[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
       a[u] = *reinterpret_cast<const uint2*>(src + (size_t)min(s0 + u, n_splits - 1) * stride);
-    if (tid < 64) {
+    if (wave < kCbHeads) {
       const int s = min(s0 + min(lane, kBatch - 1), n_splits - 1);
-      const float4 v = ml[(size_t)s * kHeads];
+      const float4 v = part_ml[(item0 + s) * kHeads + h0 + wave];
       const bool valid = lane < kBatch && s0 + lane < n_splits && v.y > 0.f;
       const float mb = fmaxf(M, wave_max_f(valid ? v.x : -INFINITY));
       // Nothing was accumulated while M was -inf, so the factor is then moot.
@@ -770,20 +780,20 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __rest
       const float w = valid ? exp2f(v.x - mb) : 0.f;
       L = L * alpha + wave_sum_f(w * v.y);
       M = mb;
-      if (lane < kBatch) s_w[par][lane] = w;
-      if (lane == 0) s_alpha[par] = alpha;
+      if (lane < kBatch) s_w[par][wave][lane] = w;
+      if (lane == 0) s_alpha[par][wave] = alpha;
     }
     // One barrier per batch: a wave can only refill this parity's weights
     // after every wave has passed the next batch's barrier.
     __syncthreads();
-    const float alpha = s_alpha[par];
+    const float alpha = s_alpha[par][q];
     acc.x *= alpha;
     acc.y *= alpha;
     acc.z *= alpha;
     acc.w *= alpha;
 #pragma unroll
     for (int u4 = 0; u4 < kBatch; u4 += 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&s_w[par][u4]);
+      const float4 w4 = *reinterpret_cast<const float4*>(&s_w[par][q][u4]);
       const float ws[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -795,13 +805,14 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __rest
       }
     }
   }
-  if (tid == 0) {
-    s_inv = L > 0.f ? 1.f / L : 0.f;
-    if (lse != nullptr) lse[rh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (wave < kCbHeads && lane == 0) {
+    s_inv[wave] = L > 0.f ? 1.f / L : 0.f;
+    if (lse != nullptr)
+      lse[(size_t)row * kHeads + h0 + wave] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  const float inv = s_inv;
-  *reinterpret_cast<uint2*>(out + (size_t)rh * kDc + c0) =
+  const float inv = s_inv[q];
+  *reinterpret_cast<uint2*>(out + ((size_t)row * kHeads + head) * kDc + ct * 16 + 4 * quarter) =
       uint2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
 }
 
@@ -914,7 +925,8 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
   }
   if (st) return st;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * kHeads)), dim3(128), 0, stream,
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * (kHeads / kCbHeads))),
+                       dim3(kCbThreads), 0, stream,
                        part_o, part_ml, plan.n_splits, reinterpret_cast<uint16_t*>(out), lse);
     if (hipGetLastError() != hipSuccess) return -5;
   }
