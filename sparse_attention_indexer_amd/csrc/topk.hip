@@ -1097,12 +1097,23 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
   const int rows = B * T;
   if (rows <= kMultiRows) {
     const SplitWs ws = carve_split_ws(workspace, rows, max_end_pos);
-    if (!counters_clear) {
+    if (!counters_clear && ws.n_blk > 1) {  // the lists are only used with several workgroups
       hipLaunchKernelGGL(topk_reset_kernel, dim3((unsigned)((kCtrWords * rows + 255) / 256)),
                          dim3(256), 0, stream, ws.ctr, kCtrWords * rows);
       if (hipGetLastError() != hipSuccess) return -5;
     }
     const dim3 grid((unsigned)((long)rows * ws.n_blk));
+    // With one workgroup per row the first launch selects every row itself
+    // (or sends it to full_row_topk): no list, no second launch.
+    if (ws.n_blk == 1) {
+      if (split_per_thread(max_end_pos) == kSpPerShort)
+        hipLaunchKernelGGL(topk_split_kernel<kSpPerShort>, grid, dim3(kTkThreads), 0, stream,
+                           scores, end_pos, T, S_max, k, out, ws);
+      else
+        hipLaunchKernelGGL(topk_split_kernel<kSpPerLong>, grid, dim3(kTkThreads), 0, stream,
+                           scores, end_pos, T, S_max, k, out, ws);
+      return hipGetLastError() == hipSuccess ? 0 : -5;
+    }
     if (split_per_thread(max_end_pos) == kSpPerShort) {
       hipLaunchKernelGGL(topk_split_kernel<kSpPerShort>, grid, dim3(kTkThreads), 0, stream,
                          scores, end_pos, T, S_max, k, out, ws);
