@@ -29,7 +29,7 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
 struct MlaPlan {
   int rows_per_split;
   int n_splits;
-  int waves;  // 2 (32 heads per block) or 8 (all 128 heads per block)
+  int waves;  // 2 or 4 (16 heads per wave, 32 or 64 per block) or 8 (all 128 heads per block)
 };
 MlaPlan sparse_mla_plan(int B, int T, int k);
 MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos);

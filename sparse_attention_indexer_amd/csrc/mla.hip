@@ -831,10 +831,15 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #define DSA_MLA_DENSE_SMALL_WORK 65536
 #endif
 
-// Few query rows (decode at small batch): 2-wave blocks of 32 heads (16 rows
-// per wave per tile) and short splits, so one query is spread over many CUs.
+// Few query rows (decode at small batch): blocks of 2 waves (32 heads, 16 rows
+// per wave per tile) for one or two rows, else of 4 waves (64 heads, 8 rows
+// per wave per tile: half the L2 re-reads of each gathered row, which pays
+// once several rows fill the chip), and short splits, so one query is spread
+// over many CUs.
 // Otherwise 8-wave blocks of all 128 heads (every gathered row read once) and
 // about one block per CU.
+static int narrow_waves(long rows) { return rows <= 2 ? 2 : 4; }
+
 MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
   if (rows <= DSA_MLA_SMALL_ROWS) {
@@ -842,7 +847,7 @@ MlaPlan sparse_mla_plan(int B, int T, int k) {
     // about 128 items of 2 head groups each.
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)k * rows) rps *= 2;
-    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (k + rps - 1) / rps, 2};
+    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (k + rps - 1) / rps, narrow_waves(rows)};
   }
   long ns = DSA_MLA_TARGET_BLOCKS / rows;
   const long max_ns = (k + 63) / 64;
@@ -862,7 +867,7 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   if (rows <= DSA_MLA_SMALL_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK) {
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)S_max * rows) rps *= 2;
-    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (ext + rps - 1) / rps, 2};
+    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (ext + rps - 1) / rps, narrow_waves(rows)};
   }
   long rps = (long)S_max * rows / DSA_MLA_TARGET_BLOCKS;
   rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
@@ -919,6 +924,9 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
                        softmax_scale * kLog2e, reinterpret_cast<uint16_t*>(out), lse, part_o,
                        part_ml);
     st = hipGetLastError() == hipSuccess ? 0 : -5;
+  } else if (plan.waves == 4) {
+    st = launch_mla_shape<kDense, 4, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
+                                        rows, softmax_scale, out, lse, part_o, part_ml, stream);
   } else {
     st = launch_mla_shape<kDense, 2, 16>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
                                          rows, softmax_scale, out, lse, part_o, part_ml, stream);
