@@ -24,6 +24,7 @@
 // needs the workspace to hold anything in particular beforehand.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "select.h"
 
 namespace dsa {
 
@@ -31,82 +32,14 @@ constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kSeg = 64;                   // positions per thread per chunk
 constexpr int kChunk = kTkThreads * kSeg;  // 32768 positions per chunk
-constexpr int kBins = 2048;
 constexpr int kCandCap = 4096;             // candidate keys
-constexpr int kHistWords = kBins + kBins / 32;
-constexpr int kMaxK = 2048;
-
-// Histogram bins are stored with one pad word per 32 so that a lane reading
-// 32 consecutive bins (the bin search) does not collide with other lanes.
-__device__ __forceinline__ int hpad(uint32_t bin) { return (int)(bin + (bin >> 5)); }
+static_assert(kTkThreads == kSplitThreads && kChunk == kSpShortMax, "split workspace layout");
 
 // Word of element j of segment t in the LDS chunk: 16-byte group j/4 is
 // XOR-swizzled with the low bits of t, so lanes reading the same group of
 // consecutive segments hit different 4-bank sets.
 __device__ __forceinline__ int swz(int t, int j) {
   return kSeg * t + 4 * ((j >> 2) ^ (t & (kSeg / 4 - 1))) + (j & 3);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): sums
-// within rows of 16 lanes by DPP row shifts, then the row totals are carried
-// over with row broadcasts (lane 15 into row 1 and 3, lane 31 into rows 2, 3).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return v;
-}
-
-// Maximum over the 64 lanes of a wave (all lanes active), in every lane:
-// the scan pattern of wave_incl_scan with max, read back from lane 63.
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Exclusive prefix sums over the block of two per-thread values, plus totals.
-// kLdsOnly: the barrier is an LDS-only one (global accesses in flight stay in
-// flight) and there is no trailing barrier, for callers that synchronise
-// before s_wave is written again.
-template <bool kLdsOnly = false>
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* s_wave,
-                                                      uint32_t& ex_a, uint32_t& ex_b,
-                                                      uint32_t& tot_a, uint32_t& tot_b) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
-  if (lane == 63) {
-    s_wave[wave] = ia;
-    s_wave[kTkWaves + wave] = ib;
-  }
-  if constexpr (kLdsOnly) lds_barrier();
-  else __syncthreads();
-  uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
-#pragma unroll
-  for (int w4 = 0; w4 < kTkWaves; w4 += 4) {
-    const uint4 wa = *reinterpret_cast<const uint4*>(s_wave + w4);
-    const uint4 wb = *reinterpret_cast<const uint4*>(s_wave + kTkWaves + w4);
-    const uint32_t va[4] = {wa.x, wa.y, wa.z, wa.w}, vb[4] = {wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pa += (w4 + u < wave) ? va[u] : 0u;
-      pb += (w4 + u < wave) ? vb[u] : 0u;
-      sa += va[u];
-      sb += vb[u];
-    }
-  }
-  if constexpr (!kLdsOnly) __syncthreads();
-  ex_a = pa + ia - a;
-  ex_b = pb + ib - b;
-  tot_a = sa;
-  tot_b = sb;
 }
 
 // Keys of chunk positions [base, base+len): coalesced global loads -> keys ->
@@ -149,52 +82,6 @@ __device__ __forceinline__ void read_batch(const uint32_t* s_keys, int bt, uint3
     kb[4 * c + 2] = q4.z;
     kb[4 * c + 3] = q4.w;
   }
-}
-
-// One wave finds the bin holding the `remaining`-th largest counted element
-// (counting from the top bin down): returns its digit and the count of
-// elements in higher bins.  Lane l owns the kNB/64 bins just below those of
-// lane l-1 (they share one pad offset, so a lane reads them at fixed offsets
-// from one address, and consecutive lanes hit different banks).  The crossing
-// lane comes from the scan of the per-lane sums; then its bins are scanned
-// with one bin per lane.  All 64 lanes must be active.  With no crossing (an
-// inconsistent histogram) the digit is meaningless but in range.
-template <int kNB, bool kPadded>
-__device__ __forceinline__ void wave_select_bin_t(const uint32_t* hist, uint32_t remaining,
-                                                  uint32_t& digit, uint32_t& above_out) {
-  constexpr int kPer = kNB / kWave;  // 32 or 16
-  const int lane = threadIdx.x & 63;
-  auto lane_bins = [&](int l) {
-    const int low = kNB - kPer * (l + 1);  // lowest bin of lane l
-    return hist + (kPadded ? low + (low >> 5) : low);
-  };
-  const uint32_t* hb = lane_bins(lane);
-  uint32_t sum = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) sum += hb[u];
-  const uint32_t incl = wave_incl_scan(sum);
-  const uint32_t excl = incl - sum;
-  const uint64_t who = __builtin_amdgcn_ballot_w64(excl < remaining && remaining <= incl);
-  const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
-  const uint32_t above_src = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
-  // Lane j < kPer takes bin (top bin of lane src) - j.
-  const uint32_t v = lane_bins(src)[kPer - 1 - min(lane, kPer - 1)];
-  const uint32_t cj = lane < kPer ? v : 0u;
-  const uint32_t incl2 = wave_incl_scan(cj) + above_src;
-  const uint32_t excl2 = incl2 - cj;
-  const uint64_t who2 =
-      __builtin_amdgcn_ballot_w64(lane < kPer && excl2 < remaining && remaining <= incl2);
-  const int j = who2 ? (int)__ffsll((long long)who2) - 1 : 0;
-  digit = (uint32_t)(kNB - 1 - kPer * src - j);
-  above_out = (uint32_t)__builtin_amdgcn_readlane((int)excl2, j);
-}
-
-template <bool kPadded = true>
-__device__ __forceinline__ void wave_select_bin(const uint32_t* hist, int nbins,
-                                                uint32_t remaining, uint32_t& digit,
-                                                uint32_t& above_out) {
-  if (nbins == kBins) wave_select_bin_t<kBins, kPadded>(hist, remaining, digit, above_out);
-  else wave_select_bin_t<kBins / 2, kPadded>(hist, remaining, digit, above_out);
 }
 
 // Block-wide version: wave 0 searches, everyone receives the result.
@@ -419,99 +306,6 @@ __device__ __noinline__ void full_row_topk(const float* __restrict__ x, int n, i
 // (a candidate set holding every element >= L with at least k elements
 // contains the top k).  A zero-filled workspace gets the fast path at once.
 // ---------------------------------------------------------------------------
-static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-__device__ __forceinline__ int row_len(const int32_t* end_pos, int row, int T, int S_max) {
-  const int b = row / T, t = row - b * T;
-  const int ep = min(max(end_pos[b], T), S_max);
-  return ep - T + t + 1;
-}
-
-// select_bin with LDS-only barriers (global loads in flight stay in flight).
-template <bool kPadded = true>
-__device__ __forceinline__ uint32_t sel_select_bin(const uint32_t* hist, int nbins,
-                                                   uint32_t& remaining, uint32_t* s_sel) {
-  lds_barrier();
-  if (threadIdx.x < kWave) {
-    uint32_t digit, above;
-    wave_select_bin<kPadded>(hist, nbins, remaining, digit, above);
-    if (threadIdx.x == 0) {
-      s_sel[0] = digit;
-      s_sel[1] = above;
-    }
-  }
-  lds_barrier();
-  const uint32_t digit = s_sel[0];
-  remaining -= s_sel[1];
-  return digit;
-}
-
-// The few keys (at most 64) left after round 2, gathered in s_small: one wave
-// ranks them and publishes the `remaining`-th largest (thr) and how many keys
-// equal to it are kept (need_eq).
-__device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
-                                           uint32_t remaining, uint32_t* s_sel) {
-  const int lane = threadIdx.x & 63;
-  const bool valid = lane < (int)m;
-  const uint32_t mine = s_small[min(lane, (int)m - 1)];
-  uint32_t gt = 0, ge = 0;
-  for (int j = 0; j < (int)m; ++j) {
-    const uint32_t other = s_small[j];
-    gt += other > mine ? 1u : 0u;
-    ge += other >= mine ? 1u : 0u;
-  }
-  // Fewer than `remaining` keys above it, at least `remaining` at or above it.
-  const bool hit = valid && gt < remaining && remaining <= ge;
-  const uint64_t who = __builtin_amdgcn_ballot_w64(hit);
-  const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
-  const uint32_t t_key = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
-  const uint32_t t_gt = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
-  if (lane == 0) {
-    s_sel[0] = t_key;
-    s_sel[1] = remaining - t_gt;
-  }
-}
-
-// Ordered output from the two position bitmaps (winners strictly above the
-// threshold in `sure`, keys equal to it in `eq`, of which the need_eq
-// smallest positions are kept).  bitmap_prefixes stores, per 32-position
-// word, the number of set `sure` bits before the word (bits 0..15) and of
-// set `eq` bits before it (bits 16..31), each capped at 65535 (both are only
-// compared with k <= 2048); thread t owns a run of consecutive words.  The
-// caller synchronises before reading `pre`.  A winner then finds its output
-// slot from three LDS words, with no loop over set bits.
-__device__ __forceinline__ void bitmap_prefixes(const uint32_t* sure, const uint32_t* eq,
-                                                uint32_t* pre, int nwords, uint32_t* s_wave) {
-  const int tid = threadIdx.x;
-  const int wpt = (nwords + kTkThreads - 1) / kTkThreads;
-  const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int w = w0; w < w1; ++w) {
-    n_gt += (uint32_t)__popc(sure[w]);
-    n_eq += (uint32_t)__popc(eq[w]);
-  }
-  uint32_t gt, eqb, tot_gt, tot_eq;
-  block_exclusive_scan2<true>(n_gt, n_eq, s_wave, gt, eqb, tot_gt, tot_eq);
-  for (int w = w0; w < w1; ++w) {
-    pre[w] = min(gt, 0xFFFFu) | (min(eqb, 0xFFFFu) << 16);
-    gt += (uint32_t)__popc(sure[w]);
-    eqb += (uint32_t)__popc(eq[w]);
-  }
-}
-
-// Output slot of position p (marked in `sure` when above the threshold, else
-// in `eq`), or -1 when p is an equal key beyond the first need_eq.
-__device__ __forceinline__ int winner_slot(const uint32_t* sure, const uint32_t* eq,
-                                           const uint32_t* pre, uint32_t p, bool above,
-                                           uint32_t need_eq) {
-  const uint32_t w = p >> 5, below = (1u << (p & 31)) - 1u;
-  const uint32_t pw = pre[w];
-  const uint32_t n_gt = (pw & 0xFFFFu) + (uint32_t)__popc(sure[w] & below);
-  const uint32_t n_eq = (pw >> 16) + (uint32_t)__popc(eq[w] & below);
-  if (above) return (int)(n_gt + min(n_eq, need_eq));
-  return n_eq < need_eq ? (int)(n_gt + n_eq) : -1;
-}
-
 // ---------------------------------------------------------------------------
 // Up to 1024 rows: each row is spread over workgroups of 512 * kSpPer
 // positions (topk_split_kernel), and a second launch with one workgroup per
@@ -534,37 +328,9 @@ __device__ __forceinline__ int winner_slot(const uint32_t* sure, const uint32_t*
 // workgroup selects the row from scratch (full_row_topk).  The list counter
 // of each row must be zero when the first launch starts: the indexer clears
 // it in the fused call, a small kernel otherwise.
-constexpr int kMultiRows = 1024;
-constexpr int kSpPerShort = 8;                        // positions per thread, rows <= 32768
-constexpr int kSpPerLong = 32;                        // longer rows (fewer workgroups per row)
 constexpr int kSpSample = 2048;                       // sampled positions per row
 constexpr int kSpSamplePer = kSpSample / kTkThreads;  // 4 per thread
-constexpr int kSpCap = 8192;                          // list entries per row
 constexpr int kSpListPer = kSpCap / kTkThreads;       // 16 per thread
-constexpr int kSpMaxN = 131072;                       // longest row the bitmaps cover
-
-constexpr int kCtrWords = 4;  // per row: unused, list length, cut L, unused
-
-struct SplitWs {
-  uint32_t* ctr;  // [rows][kCtrWords]
-  uint2* list;    // [rows][kSpCap]: (key, position) of the keys >= L
-  int n_blk;      // workgroups per row
-};
-
-__host__ inline int split_per_thread(int max_end_pos) {
-  return max_end_pos <= kChunk ? kSpPerShort : kSpPerLong;
-}
-
-__host__ inline SplitWs carve_split_ws(void* ws, int rows, int max_end_pos) {
-  SplitWs w;
-  char* p = reinterpret_cast<char*>(ws);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * kCtrWords * 4);
-  w.list = reinterpret_cast<uint2*>(p);
-  const int blk = kTkThreads * split_per_thread(max_end_pos);
-  w.n_blk = max(1, (max_end_pos + blk - 1) / blk);
-  return w;
-}
 
 size_t topk_workspace_bytes(int B, int T, int, int) {
   const size_t rows = (size_t)B * T;
@@ -576,132 +342,34 @@ uint32_t* topk_counters(void* workspace, int B, int T) {
   return B * T > kMultiRows ? nullptr : reinterpret_cast<uint32_t*>(workspace);
 }
 
-struct SplitShared {
-  uint32_t hist[kHistWords];
-  uint32_t hist2[kHistWords];
-  uint32_t sure[kSpMaxN / 32];
-  uint32_t eq[kSpMaxN / 32];
-  uint32_t pre[kSpMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
-  uint32_t wave[2 * kTkWaves];
-  uint32_t sel[2];
-  uint32_t small[kWave];
-  uint32_t nsmall;
-};
-
 union SplitLds {
   TopkShared full;
-  SplitShared sp;
+  SelectShared sp;
 };
 
 // Exact selection of the k largest among M >= k keys, all >= L, held in
 // registers: entry tid + 512u of the set is (ek[u], ep[u]) for every
 // tid + 512u < M.  Writes the row's ordered output.
 template <int kEnt>
-__device__ __forceinline__ void split_select(uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt], int M, int n,
-                             int k, int32_t* __restrict__ o, uint32_t L, SplitShared& sh) {
-  const int tid = threadIdx.x;
-  const int nwords = (n + 31) >> 5;
-  for (int i = tid; i < kHistWords; i += kTkThreads) {
-    sh.hist[i] = 0;
-    sh.hist2[i] = 0;
-  }
-  for (int i = tid; i < nwords; i += kTkThreads) {
-    sh.sure[i] = 0;
-    sh.eq[i] = 0;
-  }
-  if (tid == 0) sh.nsmall = 0;
-  lds_barrier();
-  // Every key is >= L; the rounds work on D = key - L, whose range is known
-  // from the largest key, so the first digit spreads the keys over the
-  // histogram instead of piling them into the few top-bit bins they share.
-  uint32_t mx = 0;
+__device__ __forceinline__ void split_select(const uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt],
+                                             int M, int n, int k, int32_t* __restrict__ o,
+                                             uint32_t L, SelectShared& sh) {
+  RegCandidates<kTkThreads, kEnt> cand;
 #pragma unroll
   for (int u = 0; u < kEnt; ++u) {
-    ek[u] -= L;
-    if (tid + kTkThreads * u < (int)M) mx = max(mx, ek[u]);
+    cand.d[u] = ek[u] - L;
+    cand.p[u] = ep[u];
   }
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) sh.wave[tid >> 6] = mx;
-  lds_barrier();
-#pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) mx = max(mx, sh.wave[w]);
-  const int bits = 32 - __clz((int)mx);           // D < 2^bits
-  const int s1 = bits > 11 ? bits - 11 : 0;       // round 1: D >> s1 (< 2048)
-  const int s2 = s1 > 11 ? s1 - 11 : 0;           // round 2: bits s2.. of D
-  // Round 1.
-#pragma unroll
-  for (int u = 0; u < kEnt; ++u)
-    if (tid + kTkThreads * u < (int)M) atomicAdd(&sh.hist[hpad(ek[u] >> s1)], 1u);
-  uint32_t remaining = (uint32_t)k;
-  const uint32_t d1 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
-  const uint32_t m1 = sh.hist[hpad(d1)];  // keys left in the running
-  uint32_t thr, need_eq;                  // threshold as a D value
-  // The keys whose D >> shift equals pre are gathered and ranked directly.
-  auto rank_direct = [&](int shift, uint32_t pre, uint32_t m) {
-#pragma unroll
-    for (int u = 0; u < kEnt; ++u)
-      if (tid + kTkThreads * u < (int)M && (ek[u] >> shift) == pre)
-        sh.small[atomicAdd(&sh.nsmall, 1u)] = ek[u];
-    lds_barrier();
-    if (tid < kWave) rank_small(sh.small, m, remaining, sh.sel);
-    lds_barrier();
-    thr = sh.sel[0];
-    need_eq = sh.sel[1];
-  };
-  if (s1 == 0) {
-    thr = d1;
-    need_eq = remaining;
-  } else if (m1 <= (uint32_t)kWave) {
-    rank_direct(s1, d1, m1);
-  } else {
-    // Round 2: bits s2 .. s1-1 of D (with the constant bits above when the
-    // span is shorter than 11).
-#pragma unroll
-    for (int u = 0; u < kEnt; ++u)
-      if (tid + kTkThreads * u < (int)M && (ek[u] >> s1) == d1)
-        atomicAdd(&sh.hist2[hpad((ek[u] >> s2) & (kBins - 1))], 1u);
-    const uint32_t d2 = sel_select_bin(sh.hist2, kBins, remaining, sh.sel);
-    const uint32_t m2 = sh.hist2[hpad(d2)];
-    const uint32_t low = (1u << (s1 - s2)) - 1u;
-    const uint32_t p2 = (d1 << (s1 - s2)) | (d2 & low);  // D >> s2 of the survivors
-    if (s2 == 0) {
-      thr = p2;
-      need_eq = remaining;
-    } else if (m2 <= (uint32_t)kWave) {
-      rank_direct(s2, p2, m2);
-    } else {
-      // Round 3: the last s2 (<= 10) bits.
-      for (int i = tid; i < kHistWords; i += kTkThreads) sh.hist[i] = 0;
-      lds_barrier();
-#pragma unroll
-      for (int u = 0; u < kEnt; ++u)
-        if (tid + kTkThreads * u < (int)M && (ek[u] >> s2) == p2)
-          atomicAdd(&sh.hist[hpad(ek[u] & ((1u << s2) - 1u))], 1u);
-      const uint32_t d3 = sel_select_bin(sh.hist, 1024, remaining, sh.sel);
-      thr = (p2 << s2) | d3;
-      need_eq = remaining;
+  cand.M = M;
+  uint32_t thr, need_eq;
+  block_select<kTkThreads>(cand, n, k, sh, thr, need_eq);
+  // Each winner writes its position at its rank among the winners by position.
+  cand.each([&](uint32_t d, uint32_t p) {
+    if (d >= thr) {
+      const int at = winner_slot(sh.sure, sh.eq, sh.pre, p, d > thr, need_eq);
+      if (at >= 0 && at < k) o[at] = (int32_t)p;
     }
-  }
-#pragma unroll
-  for (int u = 0; u < kEnt; ++u) {
-    if (tid + kTkThreads * u < (int)M) {
-      const uint32_t p = ep[u];
-      if (ek[u] > thr) atomicOr(&sh.sure[p >> 5], 1u << (p & 31));
-      else if (ek[u] == thr) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
-    }
-  }
-  lds_barrier();
-  // Ordered output: each winner writes its position at its rank among the
-  // winners by position.
-  bitmap_prefixes(sh.sure, sh.eq, sh.pre, nwords, sh.wave);
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < kEnt; ++u) {
-    if (tid + kTkThreads * u < (int)M && ek[u] >= thr) {
-      const int at = winner_slot(sh.sure, sh.eq, sh.pre, ep[u], ek[u] > thr, need_eq);
-      if (at >= 0 && at < k) o[at] = (int32_t)ep[u];
-    }
-  }
+  });
 }
 
 // Step 3 for the row's last workgroup: the list -> registers -> selection.
@@ -731,7 +399,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
     int k, int32_t* __restrict__ out, SplitWs ws) {
   constexpr int kSpBlk = kTkThreads * kSpPer;  // positions per workgroup
   __shared__ __align__(16) SplitLds lds;
-  SplitShared& sh = lds.sp;
+  SelectShared& sh = lds.sp;
   const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
   const int n = row_len(end_pos, row, T, S_max);
   const float* x = scores + (size_t)row * S_max;
@@ -826,7 +494,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   __shared__ __align__(16) SplitLds lds;
   const int row = blockIdx.x;
   const int n = row_len(end_pos, row, T, S_max);
-  if (n <= k || n <= kSpBlk || n > ws.n_blk * kSpBlk) return;  // done by the first launch
+  if (!row_uses_list(n, k, ws)) return;  // done by the first launch
   const float* x = scores + (size_t)row * S_max;
   split_finish(x, n, k, out + (size_t)row * k, ws.ctr + kCtrWords * row + 1,
                ws.list + (size_t)row * kSpCap, ws.ctr[kCtrWords * row + 2], lds);

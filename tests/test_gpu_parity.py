@@ -447,6 +447,46 @@ def test_forward_decode_32k_normal():
     assert_out_close(out, lse, o_ref, lse_ref)
 
 
+def test_forward_rows_mix():
+    """Four decode rows mixing the top-k's forms: candidate-list rows of 20000 and 9000
+    positions (split over workgroups, finished by the second launch), one that fits a
+    single workgroup (3000) and one with fewer than k positions (1500); the attention
+    takes its 4-wave small-batch form.  Integer inputs, indices exact end to end."""
+    banner("forward rows mix")
+    case = inputs.make_case("fused_mix", 4, 1, [20000, 3000, 9000, 1500], 20000,
+                            index_dist="int", seed=17, device=DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    assert np.array_equal(idx, ref_idx)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
+def test_forward_sample_misjudged():
+    """A 32768-token row built so that the split top-k's sampled cut lets fewer than k
+    candidates through: of the sampled positions (every 16th) the even-numbered ones score
+    highest and the odd-numbered ones lowest, all other positions in between and equal.
+    The finishing launch then selects over the whole row; the answer is the 1024 high
+    positions plus the first 1024 of the middle ones (ties to the smaller position)."""
+    banner("forward, sample misjudged")
+    n = 32768
+    case = inputs.make_case("fused_fallback", 1, 1, [n], n, seed=18, device=DEV)
+    pos = torch.arange(n)
+    c = torch.full((n,), 2.0)
+    c[pos % 32 == 0] = 3.0
+    c[pos % 32 == 16] = 1.0
+    q = torch.zeros(1, 1, 64, 128)
+    q[..., 0] = 1.0
+    k_cache = torch.zeros(1, n, 128)
+    k_cache[0, :, 0] = c
+    case.q = q.to(torch.bfloat16).to(DEV)
+    case.w = torch.ones(1, 1, 64, device=DEV)
+    case.k_cache = k_cache.to(torch.bfloat16).to(DEV)
+    out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
+    expect = np.sort(np.concatenate([np.arange(0, n, 32), np.flatnonzero(pos.numpy() % 16 != 0)[:1024]]))
+    assert np.array_equal(ref_idx[0, 0], expect)
+    assert np.array_equal(idx, ref_idx)
+    assert_out_close(out, lse, o_ref, lse_ref)
+
+
 def test_forward_b64_varlen_fp8_sampled():
     """The batch-64 fp8 workload at full size; the oracle checks sampled sequences."""
     banner("forward decode_b64_varlen fp8 (sampled)")
