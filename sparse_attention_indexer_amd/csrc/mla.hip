@@ -736,9 +736,10 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 // block.  Thread t owns 4 latent dims of one head: 16-dim tile t/16, head
 // t/4 % 4, quarter t % 4, so a wave's load of one split covers 4 tiles x 4
 // heads x 32 bytes, i.e. four whole 128-byte lines of the [tile][head][16]
-// partial layout.  The splits are read 32 at a time (their loads all in flight
-// together), so a decode row with up to 32 splits costs one round trip to
-// memory.  Wave q < 4 turns the batch's (max, sum) pairs of head q into one
+// partial layout.  The splits are read kBatch at a time (their loads all in
+// flight together; kBatch = 4, 8, 16 or 32, the least that covers the splits,
+// so no load is spent on a missing split), so a row with up to 32 splits costs
+// one round trip to memory.  Wave q < 4 turns the batch's (max, sum) pairs of head q into one
 // weight per split, 2^(its max - M) with M the running maximum, and the factor
 // that rescales what was accumulated before; every thread then only reads its
 // head's weights and accumulates.
@@ -746,11 +747,12 @@ constexpr int kCbHeads = 4;
 constexpr int kCbThreads = 512;
 static_assert(kCbThreads == (kDc / 16) * kCbHeads * 4 && kHeads % kCbHeads == 0,
               "one thread per (16-dim tile, head, quarter of the tile)");
+template <int kBatch>
 __global__ __launch_bounds__(kCbThreads) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                  const float4* __restrict__ part_ml,
                                                                  int n_splits, uint16_t* __restrict__ out,
                                                                  float* __restrict__ lse) {
-  constexpr int kBatch = 32;
+  static_assert(kBatch % 4 == 0 && kBatch <= 32, "batches of 4 to 32 splits");
   constexpr int kGroups = kHeads / kCbHeads;
   const int row = blockIdx.x / kGroups, h0 = (blockIdx.x - row * kGroups) * kCbHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -933,9 +935,20 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
   }
   if (st) return st;
   if (plan.n_splits > 1) {
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * (kHeads / kCbHeads))),
-                       dim3(kCbThreads), 0, stream,
-                       part_o, part_ml, plan.n_splits, reinterpret_cast<uint16_t*>(out), lse);
+    const dim3 grid((unsigned)(rows * (kHeads / kCbHeads))), block(kCbThreads);
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
+    if (plan.n_splits <= 4)
+      hipLaunchKernelGGL(mla_combine_kernel<4>, grid, block, 0, stream, part_o, part_ml,
+                         plan.n_splits, o16, lse);
+    else if (plan.n_splits <= 8)
+      hipLaunchKernelGGL(mla_combine_kernel<8>, grid, block, 0, stream, part_o, part_ml,
+                         plan.n_splits, o16, lse);
+    else if (plan.n_splits <= 16)
+      hipLaunchKernelGGL(mla_combine_kernel<16>, grid, block, 0, stream, part_o, part_ml,
+                         plan.n_splits, o16, lse);
+    else
+      hipLaunchKernelGGL(mla_combine_kernel<32>, grid, block, 0, stream, part_o, part_ml,
+                         plan.n_splits, o16, lse);
     if (hipGetLastError() != hipSuccess) return -5;
   }
   return 0;
