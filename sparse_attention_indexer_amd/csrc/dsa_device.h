@@ -96,4 +96,39 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Row copies issued through inline asm: global_load_lds
+// with M0 = the LDS destination of lane 0 (lane i writes 16 bytes at M0 +
+// 16 i).  Written as a builtin, the compiler treats the copy as an LDS write
+// that may alias every later LDS read of the ring array and makes those reads
+// wait for all copies in flight, which serialises the gathers with the math;
+// here the kernel itself orders each slot's reads after that slot's copies
+// (a vmcnt wait, then a barrier).  The instruction has no register result.
+__device__ __forceinline__ void lds_copy16(const uint8_t* row, uint32_t lane_off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(lane_off), "s"(row) : "m0");
+}
+__device__ __forceinline__ void lds_copy16_v(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(addr) : "m0");
+}
+// 4 bytes a lane (lane i writes at M0 + 4 i).
+__device__ __forceinline__ void lds_copy4_v(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(m0), "v"(addr) : "m0");
+}
+// The lane id through an empty asm: the compiler cannot hoist what is derived
+// from it out of a loop, so per-lane addresses are recomputed (a few VALU
+// ops) instead of being kept live across the loop or spilled.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
 }  // namespace dsa

@@ -172,6 +172,185 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   }
 }
 
+// Streaming form of the decode kernel, for long key ranges per wave (at least
+// 4 tiles): the same products, but each wave copies its key tiles straight
+// from HBM into its own LDS ring (global_load_lds, 16 bytes a lane, issued
+// through inline asm so that the compiler's waits never cover them) and keeps
+// kDepth tiles in flight; a tile's wait is a fixed vmcnt (every copy is
+// issued, clamped to the workgroup's last key), and no barrier is needed since
+// a wave reads only the slots it filled.  The 16-byte chunks of key row r sit
+// XOR-swizzled by r & 7, so the B-fragment reads (16 rows, one or two chunks
+// each) spread over the banks.  Scores are collected in LDS and stored after
+// the wave's last tile, so no store sits between the copies the loop waits
+// for.
+constexpr int kIdxMaxTpw = 16;  // key tiles per wave, at most
+
+template <bool kFp8>
+__global__ __launch_bounds__(256) void indexer_stream_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ end_pos, int T, int S_max, float scale, int blocks_per_row,
+    int tiles_per_wave, float* __restrict__ out, uint32_t* __restrict__ topk_ctr) {
+  constexpr int kRowBytes = kFp8 ? kIdxDim : 2 * kIdxDim;
+  constexpr int kDepth = kFp8 ? 4 : 2;                      // tiles in flight per wave
+  constexpr int kLanesPerKey = kRowBytes / 16;              // 8 (fp8) or 16 (bf16)
+  constexpr int kKeysPerCopy = kWave / kLanesPerKey;        // 8 or 4
+  constexpr int kKeyCopies = kIdxTile / kKeysPerCopy;       // 2 or 4
+  constexpr int kCopies = kKeyCopies + (kFp8 ? 1 : 0);      // + the tile's 16 scales
+  constexpr int kSlotBytes = kIdxTile * kRowBytes + (kFp8 ? 16 * 4 : 0);
+  __shared__ __align__(16) uint8_t s_q[kIdxHeads * kRowBytes];
+  __shared__ __align__(16) uint8_t s_ring[kIdxWaves][kDepth][kSlotBytes];
+  __shared__ float s_out[kIdxWaves][kIdxMaxTpw * kIdxTile];
+  __shared__ __align__(16) float s_w[2][kIdxHeads];  // head weights, then (fp8) q scales
+
+  const int row = blockIdx.x / blocks_per_row;
+  const int blk = blockIdx.x - row * blocks_per_row;
+  const int b = row / T, t = row - b * T;
+  const int ep = min(max(end_pos[b], T), S_max);
+  const int bound = ep - T + t;  // last valid position, in [0, S_max)
+  const int keys_per_block = kIdxWaves * tiles_per_wave * kIdxTile;
+  const int blk_start = blk * keys_per_block;
+  if (blk_start > bound) return;
+  if (topk_ctr != nullptr && blk == 0 && threadIdx.x < 2) topk_ctr[4 * row + threadIdx.x] = 0u;
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + (size_t)b * S_max * kRowBytes;
+  const float* ksrow = kFp8 ? k_scale + (size_t)b * S_max : nullptr;
+  const int last = min(bound, blk_start + keys_per_block - 1);  // the workgroup's last key
+  auto tile_start = [&](int tile) { return blk_start + (tile * kIdxWaves + wave) * kIdxTile; };
+  // Tiles of this wave that hold a valid key.
+  const int first = blk_start + wave * kIdxTile;
+  const int n_tiles = first > bound ? 0 : min(tiles_per_wave, (bound - first) / (kIdxWaves * kIdxTile) + 1);
+
+  // The query and the head weights go to LDS by copies as well, issued before
+  // the first tiles' copies: one wait covers them and leaves the tiles in
+  // flight.  The query is unpadded, chunk c of head h at chunk c ^ (h & 7)
+  // (as the keys), the weights and (fp8) query scales one float a lane.
+  {
+    constexpr int kHeadsPerCopy = kWave / kLanesPerKey;                    // 8 or 4
+    constexpr int kQCopiesPerWave = kIdxHeads / kHeadsPerCopy / kIdxWaves;  // 2 or 4
+    const int ln = opaque_lane();
+    const uint8_t* qrow =
+        reinterpret_cast<const uint8_t*>(q) + (size_t)row * kIdxHeads * kRowBytes;
+#pragma unroll
+    for (int c = 0; c < kQCopiesPerWave; ++c) {
+      const int cc = wave * kQCopiesPerWave + c;
+      const int h = cc * kHeadsPerCopy + ln / kLanesPerKey;
+      const int chunk = (ln % kLanesPerKey) ^ (h & 7);
+      lds_copy16_v(qrow + h * kRowBytes + chunk * 16,
+                   __builtin_amdgcn_readfirstlane(lds_addr(s_q + cc * 1024)));
+    }
+    if (wave == 0)
+      lds_copy4_v(reinterpret_cast<const uint8_t*>(w + (size_t)row * kIdxHeads + ln),
+                  __builtin_amdgcn_readfirstlane(lds_addr(&s_w[0][0])));
+    if (kFp8 && wave == 1)
+      lds_copy4_v(reinterpret_cast<const uint8_t*>(q_scale + (size_t)row * kIdxHeads + ln),
+                  __builtin_amdgcn_readfirstlane(lds_addr(&s_w[1][0])));
+  }
+
+  // Copies of tile `tile` into ring slot tile % kDepth: copy c puts keys
+  // kKeysPerCopy*c .. +kKeysPerCopy-1 (lane L: key L / kLanesPerKey, slot
+  // chunk L % kLanesPerKey, holding the row's chunk (L % kLanesPerKey) ^
+  // (key & 7)); with fp8 one more copy puts the 16 scales (lanes 0..15).
+  auto issue = [&](int tile) {
+    uint8_t* slot = &s_ring[wave][tile % kDepth][0];
+    const int s0 = tile_start(tile);
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int c = 0; c < kKeyCopies; ++c) {
+      const int key = c * kKeysPerCopy + ln / kLanesPerKey;
+      const int chunk = (ln % kLanesPerKey) ^ (key & 7);
+      const int s = min(s0 + key, last);
+      lds_copy16_v(kbase + (size_t)s * kRowBytes + chunk * 16,
+                   __builtin_amdgcn_readfirstlane(lds_addr(slot + c * 1024)));
+    }
+    if constexpr (kFp8) {
+      if (ln < kIdxTile)
+        lds_copy4_v(reinterpret_cast<const uint8_t*>(ksrow + min(s0 + ln, last)),
+                    __builtin_amdgcn_readfirstlane(lds_addr(slot + kIdxTile * kRowBytes)));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) issue(j);
+
+  // Everything but the first tiles has landed (this wave's copies), and the
+  // other waves' too after the barrier.
+  __builtin_amdgcn_s_waitcnt(wait_vm(kDepth * kCopies));
+  lds_barrier();
+  float wv[4][4];  // weights of the 16 heads whose results this lane holds
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = mt * 16 + 4 * g + i;
+      wv[mt][i] = kFp8 ? s_w[0][h] * s_w[1][h] : s_w[0][h];
+    }
+  uint4 qa[4][kFp8 ? 2 : 4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int h = mt * 16 + r16;
+#pragma unroll
+    for (int u = 0; u < (kFp8 ? 2 : 4); ++u)
+      qa[mt][u] = *reinterpret_cast<const uint4*>(
+          s_q + h * kRowBytes + ((((kRowBytes / 64) * g + u) ^ (h & 7)) << 4));
+  }
+
+#pragma unroll 1
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    __builtin_amdgcn_s_waitcnt(wait_vm((kDepth - 1) * kCopies));  // this tile's copies have landed
+    const uint8_t* slot = &s_ring[wave][tile % kDepth][0];
+    const uint8_t* krow = slot + r16 * kRowBytes;
+    float v = 0.f;
+    if constexpr (!kFp8) {
+      uint4 kb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kb[u] = *reinterpret_cast<const uint4*>(krow + (((4 * g + u) ^ (r16 & 7)) << 4));
+      f32x4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = mfma_bf16_16x16x32(as_bf16x8(qa[mt][kk]), as_bf16x8(kb[kk]), acc[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[mt][i], 0.f);
+    } else {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(krow + (((2 * g) ^ (r16 & 7)) << 4));
+      const uint4 k1 = *reinterpret_cast<const uint4*>(krow + (((2 * g + 1) ^ (r16 & 7)) << 4));
+      const i32x8 kb = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                             (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const i32x8 a = i32x8{(int)qa[mt][0].x, (int)qa[mt][0].y, (int)qa[mt][0].z,
+                              (int)qa[mt][0].w, (int)qa[mt][1].x, (int)qa[mt][1].y,
+                              (int)qa[mt][1].z, (int)qa[mt][1].w};
+        const f32x4 acc = mfma_fp8_16x16x128(a, kb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
+      }
+      v *= reinterpret_cast<const float*>(slot + kIdxTile * kRowBytes)[r16];
+    }
+    v = idx_group_sum(v);
+    if (g == 0) s_out[wave][tile * kIdxTile + r16] = v * scale;
+    // The slot's reads are done (their values fed the math): refill it.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    issue(tile + kDepth);
+  }
+  // No copy may still be writing LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  float* orow = out + (size_t)row * S_max;
+  for (int i = lane; i < n_tiles * kIdxTile; i += kWave) {
+    const int s = tile_start(i / kIdxTile) + (i % kIdxTile);
+    if (s <= bound) orow[s] = s_out[wave][i];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill form (many queries per sequence): the same products as one GEMM of
 // the queries' [T*64, 128] against the keys' [S, 128]^T.  A 512-thread
@@ -374,10 +553,21 @@ int launch_index_scores(const void* q, const float* q_scale, const float* w, con
   // Enough blocks to cover all 256 CUs several times over, but at least one
   // 16-key tile per wave and at most 16.
   long tpw = rows * tiles_per_row / ((long)DSA_IDX_TARGET_BLOCKS * kIdxWaves);
-  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
+  tpw = tpw < 1 ? 1 : (tpw > kIdxMaxTpw ? kIdxMaxTpw : tpw);
   const int keys_per_block = (int)(kIdxWaves * tpw * kIdxTile);
   const int blocks_per_row = (max_end_pos + keys_per_block - 1) / keys_per_block;
   const dim3 grid((unsigned)(rows * blocks_per_row));
+  if (tpw >= 4) {  // long key ranges per wave: the streaming form
+    if (dtype == 0)
+      hipLaunchKernelGGL(indexer_stream_kernel<false>, grid, dim3(256), 0, stream, q, q_scale, w,
+                         k, k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out,
+                         topk_ctr);
+    else
+      hipLaunchKernelGGL(indexer_stream_kernel<true>, grid, dim3(256), 0, stream, q, q_scale, w,
+                         k, k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out,
+                         topk_ctr);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   if (dtype == 0)
     hipLaunchKernelGGL(indexer_kernel<false>, grid, dim3(256), 0, stream, q, q_scale, w, k,
                        k_scale, end_pos, T, S_max, scale, blocks_per_row, (int)tpw, out,

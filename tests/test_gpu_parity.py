@@ -189,6 +189,32 @@ def test_indexer_decode_32k_full_row():
     assert_scores_close(gpu.cpu().numpy(), ref, h["end_pos"], 1, SCORE_TOL["bf16"])
 
 
+@pytest.mark.parametrize("dtype,dist", [("bf16", "int"), ("fp8", "normal")])
+def test_indexer_streaming_form(dtype, dist):
+    """Long decode rows (4 x 131072 cached positions: at least 4 key tiles per wave) take
+    the streaming form (per-wave LDS ring of key tiles, 4 or 2 in flight): ragged lengths
+    ending inside a workgroup, a tile and a 16-key group; integer bf16 inputs exactly,
+    fp8 within tolerance; entries past each bound untouched."""
+    m = dsa()
+    banner(f"indexer streaming form {dtype} {dist}")
+    S = 131072
+    ep = [S, 100003, 5000, 4097]
+    case = inputs.make_case("stream", 4, 1, ep, S, dtype=dtype, index_dist=dist, seed=19,
+                            device=DEV)
+    out = torch.full((4, 1, S), float("nan"), device=DEV)
+    m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
+                   q_scale=case.q_scale, k_scale=case.k_scale, max_end_pos=S, out=out)
+    g = out.cpu().numpy()
+    h = np_case(case)
+    msk = valid_mask(h["end_pos"], 1, S)
+    assert not np.isnan(g[msk]).any() and np.isnan(g[~msk]).all()
+    ref = oracle_scores(case, h)
+    if dist == "int":
+        assert np.array_equal(g[msk], ref[msk])
+    else:
+        assert_scores_close(g, ref, h["end_pos"], 1, SCORE_TOL[dtype])
+
+
 def test_untouched_past_bound():
     """Entries past each causal bound are left as they were (poisoned with NaN here)."""
     m = dsa()
