@@ -276,18 +276,21 @@ __device__ __forceinline__ bool row_uses_list(int n, int k, const SplitWs& ws) {
   return n > k && n > ws.blk_pos && n <= ws.n_blk * ws.blk_pos;
 }
 
-// LDS of a selection.
-struct SelectShared {
+// LDS of a selection over rows of at most kMaxN positions.
+template <int kMaxN>
+struct SelectSharedT {
+  static constexpr int kMaxPositions = kMaxN;
   uint32_t hist[kHistWords];
   uint32_t hist2[kHistWords];
-  uint32_t sure[kSpMaxN / 32];
-  uint32_t eq[kSpMaxN / 32];
-  uint32_t pre[kSpMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
+  uint32_t sure[kMaxN / 32];
+  uint32_t eq[kMaxN / 32];
+  uint32_t pre[kMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
   uint32_t wave[2 * 8];
   uint32_t sel[2];
   uint32_t small[kWave];
   uint32_t nsmall;
 };
+using SelectShared = SelectSharedT<kSpMaxN>;
 
 // Candidates held in registers: entry tid + kThreads*u is (d[u], p[u]) for
 // every tid + kThreads*u < M.
@@ -306,13 +309,13 @@ struct RegCandidates {
 };
 
 // Exact selection of the k largest among the candidates (at least k of them,
-// positions < n <= kSpMaxN), by a workgroup of kThreads threads.  Returns the
+// positions < n <= Sh::kMaxPositions), by a workgroup of kThreads threads.  Returns the
 // threshold D value and need_eq; on return the bitmaps and their prefixes are
 // complete (the workgroup is synchronised), so that
 //   winner_slot(sh.sure, sh.eq, sh.pre, p, d > thr, need_eq)
 // gives the output slot of every candidate (d, p) with d >= thr.
-template <int kThreads, class Cand>
-__device__ __forceinline__ void block_select(const Cand& cand, int n, int k, SelectShared& sh,
+template <int kThreads, class Cand, class Sh>
+__device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh& sh,
                                              uint32_t& thr, uint32_t& need_eq) {
   constexpr int kWaves = kThreads / kWave;
   static_assert(kThreads % kWave == 0 && kWaves <= 8, "up to 8 waves");

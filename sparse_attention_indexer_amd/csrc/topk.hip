@@ -26,6 +26,8 @@
 #include "dsa_launch.h"
 #include "select.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 constexpr int kTkThreads = 512;
@@ -350,10 +352,10 @@ union SplitLds {
 // Exact selection of the k largest among M >= k keys, all >= L, held in
 // registers: entry tid + 512u of the set is (ek[u], ep[u]) for every
 // tid + 512u < M.  Writes the row's ordered output.
-template <int kEnt>
+template <int kEnt, class Sh>
 __device__ __forceinline__ void split_select(const uint32_t (&ek)[kEnt], const uint32_t (&ep)[kEnt],
                                              int M, int n, int k, int32_t* __restrict__ o,
-                                             uint32_t L, SelectShared& sh) {
+                                             uint32_t L, Sh& sh) {
   RegCandidates<kTkThreads, kEnt> cand;
 #pragma unroll
   for (int u = 0; u < kEnt; ++u) {
@@ -393,13 +395,33 @@ __device__ __forceinline__ void split_finish(const float* __restrict__ x, int n,
   split_select<kSpListPer>(ek, ep, (int)M, n, k, o, L, lds.sp);
 }
 
-template <int kSpPer>
-__global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
+// kFallback: this launch is the only one (every row fits one workgroup), so
+// it also selects rows longer than max_end_pos promised (full_row_topk, with
+// its large LDS); otherwise the finishing launch does, and this one's LDS is
+// sized for its own positions only (several workgroups per CU).
+template <int kSpPer, bool kFallback>
+struct SplitKernelLds {
+  using Sel = SelectSharedT<kTkThreads * kSpPer>;
+  union U {
+    TopkShared full;
+    Sel sp;
+  };
+  using Type = typename std::conditional<kFallback, U, Sel>::type;
+};
+
+// Without kFallback: at most 128 registers (4 waves per SIMD), two
+// workgroups per CU.
+template <int kSpPer, bool kFallback>
+__global__ __launch_bounds__(kTkThreads, kFallback ? 1 : 4) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int32_t* __restrict__ out, SplitWs ws) {
   constexpr int kSpBlk = kTkThreads * kSpPer;  // positions per workgroup
-  __shared__ __align__(16) SplitLds lds;
-  SelectShared& sh = lds.sp;
+  using Lds = typename SplitKernelLds<kSpPer, kFallback>::Type;
+  __shared__ __align__(16) Lds lds;
+  auto& sh = [&]() -> typename SplitKernelLds<kSpPer, kFallback>::Sel& {
+    if constexpr (kFallback) return lds.sp;
+    else return lds;
+  }();
   const int row = blockIdx.x / ws.n_blk, blk = blockIdx.x - row * ws.n_blk;
   const int n = row_len(end_pos, row, T, S_max);
   const float* x = scores + (size_t)row * S_max;
@@ -411,8 +433,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_split_kernel(
     return;
   }
   if (n > ws.n_blk * kSpBlk) {  // longer than max_end_pos promised: not split
-    if (blk == 0) full_row_topk(x, n, k, o, lds.full);
-    return;
+    if constexpr (kFallback) {
+      if (blk == 0) full_row_topk(x, n, k, o, lds.full);
+    }
+    return;  // (without kFallback, the finishing launch selects the row)
   }
   const int base = blk * kSpBlk;
   if (base >= n) return;
@@ -494,8 +518,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   __shared__ __align__(16) SplitLds lds;
   const int row = blockIdx.x;
   const int n = row_len(end_pos, row, T, S_max);
-  if (!row_uses_list(n, k, ws)) return;  // done by the first launch
+  if (n <= k || n <= ws.blk_pos) return;  // done by the first launch
   const float* x = scores + (size_t)row * S_max;
+  if (n > ws.n_blk * ws.blk_pos) {  // longer than max_end_pos promised: not split
+    full_row_topk(x, n, k, out + (size_t)row * k, lds.full);
+    return;
+  }
   split_finish(x, n, k, out + (size_t)row * k, ws.ctr + kCtrWords * row + 1,
                ws.list + (size_t)row * kSpCap, ws.ctr[kCtrWords * row + 2], lds);
 }
@@ -775,22 +803,22 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
     // (or sends it to full_row_topk): no list, no second launch.
     if (ws.n_blk == 1) {
       if (split_per_thread(max_end_pos) == kSpPerShort)
-        hipLaunchKernelGGL(topk_split_kernel<kSpPerShort>, grid, dim3(kTkThreads), 0, stream,
-                           scores, end_pos, T, S_max, k, out, ws);
+        hipLaunchKernelGGL((topk_split_kernel<kSpPerShort, true>), grid, dim3(kTkThreads), 0,
+                           stream, scores, end_pos, T, S_max, k, out, ws);
       else
-        hipLaunchKernelGGL(topk_split_kernel<kSpPerLong>, grid, dim3(kTkThreads), 0, stream,
-                           scores, end_pos, T, S_max, k, out, ws);
+        hipLaunchKernelGGL((topk_split_kernel<kSpPerLong, true>), grid, dim3(kTkThreads), 0,
+                           stream, scores, end_pos, T, S_max, k, out, ws);
       return hipGetLastError() == hipSuccess ? 0 : -5;
     }
     if (split_per_thread(max_end_pos) == kSpPerShort) {
-      hipLaunchKernelGGL(topk_split_kernel<kSpPerShort>, grid, dim3(kTkThreads), 0, stream,
-                         scores, end_pos, T, S_max, k, out, ws);
+      hipLaunchKernelGGL((topk_split_kernel<kSpPerShort, false>), grid, dim3(kTkThreads), 0,
+                         stream, scores, end_pos, T, S_max, k, out, ws);
       if (hipGetLastError() != hipSuccess) return -5;
       hipLaunchKernelGGL(topk_finish_kernel<kSpPerShort>, dim3((unsigned)rows), dim3(kTkThreads),
                          0, stream, scores, end_pos, T, S_max, k, out, ws);
     } else {
-      hipLaunchKernelGGL(topk_split_kernel<kSpPerLong>, grid, dim3(kTkThreads), 0, stream,
-                         scores, end_pos, T, S_max, k, out, ws);
+      hipLaunchKernelGGL((topk_split_kernel<kSpPerLong, false>), grid, dim3(kTkThreads), 0,
+                         stream, scores, end_pos, T, S_max, k, out, ws);
       if (hipGetLastError() != hipSuccess) return -5;
       hipLaunchKernelGGL(topk_finish_kernel<kSpPerLong>, dim3((unsigned)rows), dim3(kTkThreads),
                          0, stream, scores, end_pos, T, S_max, k, out, ws);
