@@ -268,6 +268,21 @@ def test_topk_longest_rows():
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("max_end_pos", [9000, 4000])
+def test_topk_row_longer_than_promised(max_end_pos):
+    """A row longer than max_end_pos (a broken promise the host cannot see) is still
+    selected exactly: by the finishing launch when rows are split over several
+    workgroups (9000: 3 per row), by the single launch otherwise (4000)."""
+    m = dsa()
+    banner(f"topk row longer than max_end_pos={max_end_pos}")
+    B, T, S, k = 2, 1, 40000, 2048
+    ep = np.array([40000, 3000], np.int32)
+    scores = inputs.make_scores(B, T, S, kind="normal", seed=23, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=max_end_pos)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("B,T,S,kind", [(1, 1100, 3000, "ties"), (2, 520, 33000, "normal")])
 def test_topk_many_rows(B, T, S, kind):
     """More than 1024 query rows: one workgroup per row (rows of up to 32768
