@@ -131,4 +131,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): 4 bf16 of a 16x16 block's column.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// max / sum over the 4 lanes l%16 + 16j that hold the same head.
+__device__ __forceinline__ float group_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
 }  // namespace dsa

@@ -50,14 +50,6 @@ __device__ __forceinline__ KeyFrag<kFp8> load_key_frag(const uint8_t* kbase, con
   return f;
 }
 
-// Sum over the 4 lanes l%16 + 16j (the four dim groups of one key's dot).
-__device__ __forceinline__ float idx_group_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  v = __int_as_float(a[0]) + __int_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return __int_as_float(b[0]) + __int_as_float(b[1]);
-}
-
 template <bool kFp8>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -162,7 +154,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
         for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
       }
     }
-    v = idx_group_sum(v);
+    v = group_sum(v);
     const int s = s0 + r16;
     if (g == 0 && s <= bound) {
       if constexpr (kFp8) v *= cur.ks;
@@ -336,7 +328,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
       }
       v *= reinterpret_cast<const float*>(slot + kIdxTile * kRowBytes)[r16];
     }
-    v = idx_group_sum(v);
+    v = group_sum(v);
     if (g == 0) s_out[wave][tile * kIdxTile + r16] = v * scale;
     // The slot's reads are done (their values fed the math): refill it.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -372,12 +364,6 @@ __device__ __forceinline__ int pf_swz(int r, int c) {
   return kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
 }
 
-__device__ __forceinline__ float quad_sum(float v) {  // over lanes l%16 + 16j
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  v = __int_as_float(a[0]) + __int_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return __int_as_float(b[0]) + __int_as_float(b[1]);
-}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -516,7 +502,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x += wv[qq][mt][i] * fmaxf(acc[qq][mt][i], 0.f);
-        v[qq] = quad_sum(x);
+        v[qq] = group_sum(x);
       }
       const int s = s_begin + tile * kPfTile + nt * 16 + r16;
       if (g == 0) {

@@ -61,36 +61,6 @@ constexpr float kMhLog2e = 1.4426950408889634f;
 constexpr float kMhLn2 = 0.6931471805599453f;
 constexpr float kMhSlack = 8.f;
 
-typedef __attribute__((address_space(3))) void mh_lds_void;
-
-__device__ __forceinline__ uint32_t mh_lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((const mh_lds_void*)p);
-}
-// global_load_lds (16 bytes a lane, lane i writes M0 + 16 i) through inline
-// asm, so that the compiler does not make later reads of other ring slots
-// wait for the copy; the kernel orders each slot's reads after its copies
-// itself (vmcnt wait, then a barrier).  No register result.
-__device__ __forceinline__ void mh_copy16(const void* addr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(addr) : "m0");
-}
-__device__ __forceinline__ i16x4 mh_read_tr16(const uint8_t* p) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
-// max / sum over the 4 lanes l%16 + 16j that hold the same query.
-__device__ __forceinline__ float mh_group_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
-}
-__device__ __forceinline__ float mh_group_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  v = __int_as_float(a[0]) + __int_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return __int_as_float(b[0]) + __int_as_float(b[1]);
-}
-
 // Bitmap [B][W][Tp] uint32 (W = ceil(T/32) words per query, Tp = T rounded up
 // to 64): bit t%32 of word t/32 of query s is set when t (0 <= t < T) is in
 // s's list.  One workgroup per (sequence, 64 queries, 256 words); each thread
@@ -169,22 +139,22 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
       const int r = 8 * wv + 4 * i + (lane >> 4);
       const int t = min(t0 + r, T - 1);
       const int cn = (lane & 15) ^ (r & 15);
-      mh_copy16(kn_h + (size_t)t * (kMhHeads * 256) + cn * 16,
-                __builtin_amdgcn_readfirstlane(mh_lds_addr(base + (8 * wv + 4 * i) * 256)));
+      lds_copy16_v(kn_h + (size_t)t * (kMhHeads * 256) + cn * 16,
+                __builtin_amdgcn_readfirstlane(lds_addr(base + (8 * wv + 4 * i) * 256)));
       const int cv = (lane & 15) ^ ((r & 7) << 1);
-      mh_copy16(v_h + (size_t)t * (kMhHeads * 256) + cv * 16,
-                __builtin_amdgcn_readfirstlane(mh_lds_addr(base + kMhOffV + (8 * wv + 4 * i) * 256)));
+      lds_copy16_v(v_h + (size_t)t * (kMhHeads * 256) + cv * 16,
+                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffV + (8 * wv + 4 * i) * 256)));
     }
     {
       const int r = 8 * wv + (lane >> 3);
       const int t = min(t0 + r, T - 1);
       const int cp = (lane & 7) ^ ((r >> 1) & 7);
-      mh_copy16(kp_b + (size_t)t * 128 + cp * 16,
-                __builtin_amdgcn_readfirstlane(mh_lds_addr(base + kMhOffKp + 8 * wv * 128)));
+      lds_copy16_v(kp_b + (size_t)t * 128 + cp * 16,
+                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffKp + 8 * wv * 128)));
     }
     if (lane < 4)
-      mh_copy16(bt_b + ((size_t)kt * Tp + s0 + 16 * wv) * 4 + lane * 16,
-                __builtin_amdgcn_readfirstlane(mh_lds_addr(base + kMhOffBits + 64 * wv)));
+      lds_copy16_v(bt_b + ((size_t)kt * Tp + s0 + 16 * wv) * 4 + lane * 16,
+                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffBits + 64 * wv)));
   };
 
   float m_run = -INFINITY, l_part = 0.f;
@@ -249,7 +219,7 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
         sc[mt][i] = sel ? sc[mt][i] : -INFINITY;  // raw score, masked
         mx = fmaxf(mx, sc[mt][i]);
       }
-    mx = mh_group_max(mx) * scale_log2;
+    mx = group_max(mx) * scale_log2;
     const bool grow = mx > m_run + kMhSlack;
     if (__ballot(grow) != 0) {
       const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.f;
@@ -277,8 +247,8 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const int off = ((2 * ct + vch) ^ vsw) << 4;
-      const i16x4 lo = mh_read_tr16(vrow + off);
-      const i16x4 hi = mh_read_tr16(vrow + 16 * 256 + off);
+      const i16x4 lo = lds_read_tr16(vrow + off);
+      const i16x4 hi = lds_read_tr16(vrow + 16 * 256 + off);
       const uint4 va = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
                              (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                              (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
@@ -288,7 +258,7 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
   }
 
   // ---- finish ----
-  const float l_tot = mh_group_sum(l_part);
+  const float l_tot = group_sum(l_part);
   if (s_me < T) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = out + (((size_t)b * T + s_me) * kMhHeads + h) * kMhDv + 4 * g;
