@@ -26,7 +26,7 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxTile = 16;
 
 #ifndef DSA_IDX_TARGET_BLOCKS
-#define DSA_IDX_TARGET_BLOCKS 2048
+#define DSA_IDX_TARGET_BLOCKS 1024
 #endif
 
 // Key fragment of one 16-key tile for this lane: 64 bytes (bf16) or 32 (fp8)
@@ -536,8 +536,8 @@ int launch_index_scores(const void* q, const float* q_scale, const float* w, con
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   const long tiles_per_row = (max_end_pos + kIdxTile - 1) / kIdxTile;
-  // Enough blocks to cover all 256 CUs several times over, but at least one
-  // 16-key tile per wave and at most 16.
+  // About 1024 workgroups (four per CU), at least one 16-key tile per wave and
+  // at most 16: long key ranges per wave then take the streaming form.
   long tpw = rows * tiles_per_row / ((long)DSA_IDX_TARGET_BLOCKS * kIdxWaves);
   tpw = tpw < 1 ? 1 : (tpw > kIdxMaxTpw ? kIdxMaxTpw : tpw);
   const int keys_per_block = (int)(kIdxWaves * tpw * kIdxTile);
