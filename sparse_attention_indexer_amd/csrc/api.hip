@@ -202,8 +202,10 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   st = dsa::launch_topk(scores, end_pos, B, T, S_max, max_end_pos, k, indices, ws + L.topk_ws,
                         /*counters_clear=*/topk_ctr != nullptr, stream);
   if (st) return st;
+  // The selection fills each list's first min(k, causal bound) slots, so the
+  // attention skips the rest (whole tiles of -1 for early prefill queries).
   return dsa::launch_sparse_mla(q_nope, q_pe, kv_cache, pe_cache, indices, B, T, S_max, k,
-                                softmax_scale, out, lse, ws + L.mla_ws, stream);
+                                softmax_scale, out, lse, ws + L.mla_ws, stream, end_pos);
 }
 
 DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {

@@ -35,9 +35,13 @@ MlaPlan sparse_mla_plan(int B, int T, int k);
 MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos);
 size_t mla_workspace_bytes(int B, int T, const MlaPlan& plan);
 
+// prefix_end_pos: NULL, or the end positions when idx comes from the top-k
+// selection (kept positions in the first min(k, causal bound) slots, -1
+// after): the kernels then skip the empty tail of each list.
 int launch_sparse_mla(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
                       const int32_t* idx, int B, int T, int S_max, int k, float softmax_scale,
-                      void* out, float* lse, void* workspace, hipStream_t stream);
+                      void* out, float* lse, void* workspace, hipStream_t stream,
+                      const int32_t* prefix_end_pos = nullptr);
 int launch_dense_mla(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
                      const int32_t* end_pos, int B, int T, int S_max, int max_end_pos,
                      float softmax_scale, void* out, float* lse, void* workspace,

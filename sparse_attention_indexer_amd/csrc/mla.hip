@@ -109,10 +109,14 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   const int row = X / n_splits, split = X - row * n_splits;
   const int b = row / T, t = row - b * T;
 
-  int n_list;  // entries in this row's list
-  if constexpr (kDense) {
+  // Entries in this row's list.  Dense: the causal bound.  Sparse: k, or,
+  // when end_pos is given (a list from the top-k selection, whose kept
+  // positions fill its first min(k, bound) slots), only those slots.
+  int n_list;
+  if (kDense || end_pos != nullptr) {
     const int ep = min(max(end_pos[b], T), S_max);
     n_list = ep - T + t + 1;
+    if (!kDense) n_list = min(n_list, k);
   } else {
     n_list = k;
   }
@@ -391,10 +395,14 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   if (X >= n_items) return;
   const int row = X / n_splits, split = X - row * n_splits;
   const int b = row / T, t = row - b * T;
+  // Entries in this row's list.  Dense: the causal bound.  Sparse: k, or,
+  // when end_pos is given (a list from the top-k selection, whose kept
+  // positions fill its first min(k, bound) slots), only those slots.
   int n_list;
-  if constexpr (kDense) {
+  if (kDense || end_pos != nullptr) {
     const int ep = min(max(end_pos[b], T), S_max);
     n_list = ep - T + t + 1;
+    if (!kDense) n_list = min(n_list, k);
   } else {
     n_list = k;
   }
@@ -908,9 +916,10 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
 
 int launch_sparse_mla(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
                       const int32_t* idx, int B, int T, int S_max, int k, float softmax_scale,
-                      void* out, float* lse, void* workspace, hipStream_t stream) {
+                      void* out, float* lse, void* workspace, hipStream_t stream,
+                      const int32_t* prefix_end_pos) {
   const MlaPlan plan = sparse_mla_plan(B, T, k);
-  return launch_mla<false>(q_nope, q_pe, kv, pe, idx, nullptr, B, T, S_max, k, plan,
+  return launch_mla<false>(q_nope, q_pe, kv, pe, idx, prefix_end_pos, B, T, S_max, k, plan,
                            softmax_scale, out, lse, workspace, stream);
 }
 

@@ -488,6 +488,33 @@ def test_forward_decode_32k_normal():
     assert_out_close(out, lse, o_ref, lse_ref)
 
 
+@pytest.mark.parametrize("B,T,eps,k", [(2, 640, [640, 3000], 256), (1, 2, [2], 2048),
+                                        (1, 40, [40], 64)])
+def test_forward_skips_empty_list_tail(B, T, eps, k):
+    """dsa_forward bounds each attention list by the query's causal bound
+    (the selection fills only the first min(k, bound) slots).  Early prefill
+    queries then have short lists, ending inside a tile or a split; the
+    result must equal, bit for bit, dsa_sparse_mla over the full k slots of
+    the same selection, and match the oracle on sampled rows."""
+    m = dsa()
+    banner(f"forward list bound B={B} T={T} end_pos={eps} k={k}")
+    case = inputs.make_case("list_bound", B, T, eps, max(eps), seed=21, topk=k, device=DEV)
+    topk_out = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    out, lse, _ = m.forward_case(case, topk_out=topk_out)
+    out2, lse2 = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, topk_out,
+                              case.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert torch.equal(lse, lse2)
+    h = np_case(case)
+    n = B * T
+    rows = sorted({0, 1, 31, 32, 33, k - 1, k, T - 1, n - 1} & set(range(n)))
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale,
+                                indices=topk_out.cpu().numpy(), rows=rows)
+    assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
+
+
 def test_forward_rows_mix():
     """Four decode rows mixing the top-k's forms: candidate-list rows of 20000 and 9000
     positions (split over workgroups, finished by the second launch), one that fits a
