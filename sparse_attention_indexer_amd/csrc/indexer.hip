@@ -381,9 +381,13 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
   constexpr int kRowsPerCopy = 1024 / kRowBytes;
   __shared__ __align__(16) uint8_t s_k[2][kTileBytes];
 
+  // The query block varies fastest: workgroups go to the 8 XCDs round robin,
+  // and with the key chunk fastest XCD x would get chunk x of every query
+  // block, so the XCDs holding the early chunks (active for every causal
+  // query block) would carry most of the work.
   const int bid = blockIdx.x;
-  const int chunk = bid % n_chunks, rest = bid / n_chunks;
-  const int qblk = rest % n_qblk, b = rest / n_qblk;
+  const int qblk = bid % n_qblk, rest = bid / n_qblk;
+  const int chunk = rest % n_chunks, b = rest / n_chunks;
   const int t0 = qblk * kPfQ;
   const int ep = min(max(end_pos[b], T), S_max);
   const int t_last = min(t0 + kPfQ - 1, T - 1);
