@@ -233,7 +233,7 @@ __device__ __forceinline__ int winner_slot(const uint32_t* sure, const uint32_t*
 constexpr int kMultiRows = 1024;
 constexpr int kSplitThreads = 512;
 constexpr int kSpPerShort = 8;      // positions per thread, rows <= kSpShortMax
-constexpr int kSpPerLong = 32;      // longer rows (fewer workgroups per row)
+constexpr int kSpPerLong = 16;      // longer rows (fewer workgroups per row)
 constexpr int kSpShortMax = 32768;
 constexpr int kSpCap = 8192;        // list entries per row
 constexpr int kSpMaxN = 131072;     // longest row the bitmaps cover
