@@ -341,8 +341,14 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 // ---- Wide form: many query rows -------------------------------------------
 //
 // Eight waves (two per SIMD).  The two contractions are split differently:
-//   scores  S^T[row][head]: wave w takes heads 16w..16w+15, its query
-//           fragments in registers, exactly as in the narrow form;
+//   scores  S^T[row][head]: the wave pair 2p, 2p+1 takes heads 32p..32p+31,
+//           wave 2p+d the half d of the 576 score dims (latent 0..287, or
+//           latent 288..511 and the rope part), its query fragments of both
+//           16-head tiles in registers.  Each K fragment read from LDS then
+//           feeds two MFMAs, so a tile's K is read from LDS four times, not
+//           eight (those reads bound the kernel).  The pair swaps the partial
+//           scores of the head tile it does not keep through LDS (2 KiB a
+//           wave), and wave w finishes head tile w, as in the narrow form;
 //   values  O^T[c][head]: wave w takes latent dims 64w..64w+63 for all 128
 //           heads (4 x 8 accumulator tiles, 128 registers), so each transposed
 //           V fragment feeds 8 head tiles and V is read from LDS once per tile
@@ -372,6 +378,8 @@ constexpr int kWdTileKv = kWdRt * kWdPitch;
 constexpr int kWdTileBytes = kWdTileKv + kWdRt * 128;
 constexpr int kWdDims = kDc / kWdWaves;                 // latent dims per value wave (64)
 constexpr int kWdCt = kWdDims / 16;                     // their 16-dim tiles (4)
+constexpr int kWdSteps = (kDc + kDr) / 32 / 2;          // 32-dim score steps per dim half (9)
+static_assert(kWdSteps == 9 && kDc / 32 == 16, "dim halves: latent steps 0-8 | 9-15 and rope 0-1");
 static_assert(kWdRw == 4, "rope copies use lanes 8r..8r+7 for row r");
 
 template <bool kDense>
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   __shared__ float s_alpha[2][kHeads];                    // a tile's rescale per head
   __shared__ float s_fin[2][kHeads];                    // m, l per head
   __shared__ __align__(8) uint8_t s_vmask[kWdNbuf][kWdWaves];  // bit r: row 4w+r is valid
-  __shared__ __align__(16) uint4 s_qpe[2][kWdWaves][64];      // rope-part query fragments
+  __shared__ __align__(16) float4 s_x[kWdWaves][2][64];     // partial scores for the pair wave
   __shared__ int s_grow[2];                             // last tile (per parity) whose max moved
   __shared__ int s_idx[kDense ? 1 : kMaxSplitRows];     // the split's positions
 
@@ -433,18 +441,20 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
     return pos;
   };
 
-  // Query fragments of the wave's head tile (head 16*wave + r16): the latent
-  // part in registers, the rope part parked in LDS (each wave reads back only
-  // its own), which keeps the register budget of two waves per SIMD.
-  const int head = 16 * wave + r16;
-  uint4 qb[16];
-  {
-    const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc;
-    const uint16_t* qp = q_pe + ((size_t)row * kHeads + head) * kDr;
+  // Query fragments of the pair's two head tiles (heads 32*(wave/2) + 16*ht
+  // + r16) over this wave's dim half: step j is score step 9*dh + j, latent
+  // dims 32*step.. for steps below 16, the rope part after.
+  const int head = 16 * wave + r16;  // the head this lane finishes
+  const int dh = wv & 1;
+  uint4 qb[2][kWdSteps];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qb[kk] = ldg16(qn + kk * 32 + g * 8);
+  for (int ht = 0; ht < 2; ++ht) {
+    const int hq = 16 * ((wave & ~1) + ht) + r16;
+    const uint16_t* qn = q_nope + ((size_t)row * kHeads + hq) * kDc + 9 * 32 * dh + g * 8;
+    const uint16_t* qp = q_pe + ((size_t)row * kHeads + hq) * kDr + g * 8;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) s_qpe[kk][wave][lane] = ldg16(qp + kk * 32 + g * 8);
+    for (int j = 0; j < kWdSteps; ++j)
+      qb[ht][j] = ldg16(j < 7 || dh == 0 ? qn + j * 32 : qp + (j - 7) * 32);
   }
 
   const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
@@ -502,9 +512,9 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
 
   if (n_tiles > 0) issue(0);
 
-  // Iteration it: scores and softmax of tile it, values of tile it-1 (whose P
-  // was written in the previous iteration), so that one barrier per tile
-  // suffices and a wave's softmax arithmetic can interleave with its MFMAs.
+  // Iteration it: scores and softmax of tile it, then the values of tile it-1
+  // (whose P was written in the previous iteration): one barrier per tile, and
+  // one between the two halves of the scores.
 #pragma unroll 1
   for (int it = 0; it <= n_tiles; ++it) {
     static_assert(kWdNbuf == 3, "slots: tile it-1 (values), tile it (scores), tile it+1 (copies)");
@@ -514,67 +524,44 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
     const int lane = opaque_lane(), g = lane >> 4, r16 = lane & 15;  // recomputed addresses
     const int head = 16 * wave + r16;
 
-    // ---- scores of tile it for this wave's 16 heads: rows mt*16 + 4g + i ----
+    // ---- scores of tile it, this wave's dim half for the pair's 32 heads;
+    //      rows mt*16 + 4g + i ----
     f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     const bool have_s = it < n_tiles;
     const int slot = it % kWdNbuf;
     if (have_s) {
       const uint8_t* buf = s_ring + slot * kWdTileBytes;
+      // Rows r16 and 16 + r16 share their swizzle (r16 >> 3): latent step s
+      // of row tile mt is at the offset mt*16*pitch + 64*s from one base.
+      // The rope chunks (4j' + g) ^ (r16 & 7) differ per lane.
+      const uint8_t* kb = buf + r16 * kWdPitch + ((g ^ (r16 >> 3)) << 4) + 9 * 64 * dh;
+      const uint8_t* rb = buf + kWdTileKv + r16 * 128;
+      f32x4 sp[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                        {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
+      for (int j = 0; j < kWdSteps; ++j) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int trow = mt * 16 + r16;
-          const uint8_t* a;
-          if (kk < 16) {
-            a = buf + trow * kWdPitch + (((kk * 4 + g) ^ wd_swz(trow)) << 4);
-          } else {
-            const int chunk = ((kk - 16) * 4 + g) ^ (trow & 7);
-            a = buf + kWdTileKv + trow * 128 + chunk * 16;
-          }
-          const uint4 bq = kk < 16 ? qb[kk] : s_qpe[kk - 16][wave][lane];
-          sc[mt] = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(a)),
-                                      as_bf16x8(bq), sc[mt]);
+          const uint8_t* a = kb + mt * 16 * kWdPitch + 64 * j;
+          if (j >= 7 && dh == 1) a = rb + mt * 16 * 128 + ((((j - 7) * 4 + g) ^ (r16 & 7)) << 4);
+          const uint4 kf = *reinterpret_cast<const uint4*>(a);
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht)
+            sp[ht][mt] = mfma_bf16_16x16x32(as_bf16x8(kf), as_bf16x8(qb[ht][j]), sp[ht][mt]);
         }
       }
-    }
-
-    // ---- values of tile it-1 for this wave's 64 latent dims, all heads ----
-    if (it > 0) {
-      const int pt = it - 1, pp = pt & 1;
-      if (s_grow[pp] == pt) {  // some head's reference moved at tile it-1
+      // Keep head tile dh, hand the other one's partial to the pair wave.
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          const float al = s_alpha[pp][16 * h + r16];
-#pragma unroll
-          for (int j = 0; j < kWdCt; ++j) o[j][h] *= al;
-        }
+      for (int mt = 0; mt < 2; ++mt) {
+        sc[mt] = dh ? sp[1][mt] : sp[0][mt];
+        const f32x4 give = dh ? sp[0][mt] : sp[1][mt];
+        s_x[wv][mt][lane] = float4{give[0], give[1], give[2], give[3]};
       }
-      // Rows 4g + r16/4 (+16): their swizzle is g >> 1 for both halves.
-      const uint8_t* vrow = s_ring + (pt % kWdNbuf) * kWdTileBytes +
-                            (4 * g + (r16 >> 2)) * kWdPitch + 8 * (r16 & 1);
-      const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+      lds_barrier();  // the pair's partials are visible
 #pragma unroll
-      for (int jh = 0; jh < kWdCt; jh += 2) {
-        uint4 va[2];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int ct = kWdCt * wave + jh + jj;
-          const int off = ((2 * ct + vch) ^ vsw) << 4;  // this lane's 16-byte chunk
-          const i16x4 lo = lds_read_tr16(vrow + off);
-          const i16x4 hi = lds_read_tr16(vrow + 16 * kWdPitch + off);
-          va[jj] = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-        }
-#pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          const uint4 pb = s_p[pp][h][lane];
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            o[jh + jj][h] = mfma_bf16_16x16x32(as_bf16x8(va[jj]), as_bf16x8(pb), o[jh + jj][h]);
-        }
+      for (int mt = 0; mt < 2; ++mt) {
+        const float4 got = s_x[wv ^ 1][mt][lane];
+        sc[mt][0] += got.x, sc[mt][1] += got.y, sc[mt][2] += got.z, sc[mt][3] += got.w;
       }
     }
 
@@ -614,6 +601,45 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
       if (g == 0) s_alpha[cp][head] = alpha;
       // A head's first reference needs no rescaling (its accumulators are zero).
       if (__ballot(grow && !fresh) != 0 && lane == 0) s_grow[cp] = it;
+    }
+
+    // ---- values of tile it-1 for this wave's 64 latent dims, all heads ----
+    if (it > 0) {
+      const int pt = it - 1, pp = pt & 1;
+      if (s_grow[pp] == pt) {  // some head's reference moved at tile it-1
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const float al = s_alpha[pp][16 * h + r16];
+#pragma unroll
+          for (int j = 0; j < kWdCt; ++j) o[j][h] *= al;
+        }
+      }
+      // Rows 4g + r16/4 (+16): their swizzle is g >> 1 for both halves.
+      const uint8_t* vrow = s_ring + (pt % kWdNbuf) * kWdTileBytes +
+                            (4 * g + (r16 >> 2)) * kWdPitch + 8 * (r16 & 1);
+      const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+#pragma unroll
+      for (int jh = 0; jh < kWdCt; jh += 2) {
+        uint4 va[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ct = kWdCt * wave + jh + jj;
+          const int off = ((2 * ct + vch) ^ vsw) << 4;  // this lane's 16-byte chunk
+          const i16x4 lo = lds_read_tr16(vrow + off);
+          const i16x4 hi = lds_read_tr16(vrow + 16 * kWdPitch + off);
+          va[jj] = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint4 pb = s_p[pp][h][lane];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            o[jh + jj][h] = mfma_bf16_16x16x32(as_bf16x8(va[jj]), as_bf16x8(pb), o[jh + jj][h]);
+        }
+      }
     }
   }
 
