@@ -733,16 +733,20 @@ constexpr int kCbHeads = 4;
 constexpr int kCbThreads = 512;
 static_assert(kCbThreads == (kDc / 16) * kCbHeads * 4 && kHeads % kCbHeads == 0,
               "one thread per (16-dim tile, head, quarter of the tile)");
-template <int kBatch>
-__global__ __launch_bounds__(kCbThreads) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                                 const float4* __restrict__ part_ml,
-                                                                 int n_splits, uint16_t* __restrict__ out,
-                                                                 float* __restrict__ lse) {
+// kParts > 1 (few rows): each workgroup takes 1/kParts of the 32 dim tiles
+// with kCbThreads/kParts threads, so more workgroups share the loads (every
+// part repeats the weights of its four heads, which needs four waves).
+template <int kBatch, int kParts>
+__global__ __launch_bounds__(kCbThreads / kParts) void mla_combine_kernel(
+    const uint16_t* __restrict__ part_o, const float4* __restrict__ part_ml, int n_splits,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(kBatch % 4 == 0 && kBatch <= 32, "batches of 4 to 32 splits");
+  static_assert(kCbThreads / kParts >= 64 * kCbHeads, "a wave per head for the weights");
   constexpr int kGroups = kHeads / kCbHeads;
-  const int row = blockIdx.x / kGroups, h0 = (blockIdx.x - row * kGroups) * kCbHeads;
+  const int part = blockIdx.x % kParts, gid = blockIdx.x / kParts;
+  const int row = gid / kGroups, h0 = (gid - row * kGroups) * kCbHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ct = tid >> 4, q = (tid >> 2) & 3, quarter = tid & 3;
+  const int ct = (tid >> 4) + part * (kDc / 16 / kParts), q = (tid >> 2) & 3, quarter = tid & 3;
   const int head = h0 + q;
   const size_t item0 = (size_t)row * n_splits;
   const uint16_t* src = part_o + item0 * kHeads * kDc + ((size_t)ct * kHeads + head) * 16 + 4 * quarter;
@@ -795,7 +799,7 @@ __global__ __launch_bounds__(kCbThreads) void mla_combine_kernel(const uint16_t*
   }
   if (wave < kCbHeads && lane == 0) {
     s_inv[wave] = L > 0.f ? 1.f / L : 0.f;
-    if (lse != nullptr)
+    if (lse != nullptr && part == 0)
       lse[(size_t)row * kHeads + h0 + wave] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
@@ -808,6 +812,9 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 #ifndef DSA_MLA_TARGET_BLOCKS
 #define DSA_MLA_TARGET_BLOCKS 256
+#endif
+#ifndef DSA_CB_SPLIT_ROWS
+#define DSA_CB_SPLIT_ROWS 2
 #endif
 #ifndef DSA_MLA_SMALL_ROWS
 #define DSA_MLA_SMALL_ROWS 16
@@ -921,20 +928,32 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
   }
   if (st) return st;
   if (plan.n_splits > 1) {
-    const dim3 grid((unsigned)(rows * (kHeads / kCbHeads))), block(kCbThreads);
     uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
-    if (plan.n_splits <= 4)
-      hipLaunchKernelGGL(mla_combine_kernel<4>, grid, block, 0, stream, part_o, part_ml,
-                         plan.n_splits, o16, lse);
-    else if (plan.n_splits <= 8)
-      hipLaunchKernelGGL(mla_combine_kernel<8>, grid, block, 0, stream, part_o, part_ml,
-                         plan.n_splits, o16, lse);
-    else if (plan.n_splits <= 16)
-      hipLaunchKernelGGL(mla_combine_kernel<16>, grid, block, 0, stream, part_o, part_ml,
-                         plan.n_splits, o16, lse);
-    else
-      hipLaunchKernelGGL(mla_combine_kernel<32>, grid, block, 0, stream, part_o, part_ml,
-                         plan.n_splits, o16, lse);
+    const unsigned groups = (unsigned)(rows * (kHeads / kCbHeads));
+    if (rows <= DSA_CB_SPLIT_ROWS) {
+      // Few rows: two workgroups per head group, so twice as many CUs load.
+      const dim3 grid(2 * groups), block(kCbThreads / 2);
+      if (plan.n_splits <= 16)
+        hipLaunchKernelGGL((mla_combine_kernel<16, 2>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+      else
+        hipLaunchKernelGGL((mla_combine_kernel<32, 2>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+    } else {
+      const dim3 grid(groups), block(kCbThreads);
+      if (plan.n_splits <= 4)
+        hipLaunchKernelGGL((mla_combine_kernel<4, 1>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+      else if (plan.n_splits <= 8)
+        hipLaunchKernelGGL((mla_combine_kernel<8, 1>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+      else if (plan.n_splits <= 16)
+        hipLaunchKernelGGL((mla_combine_kernel<16, 1>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+      else
+        hipLaunchKernelGGL((mla_combine_kernel<32, 1>), grid, block, 0, stream, part_o, part_ml,
+                           plan.n_splits, o16, lse);
+    }
     if (hipGetLastError() != hipSuccess) return -5;
   }
   return 0;
