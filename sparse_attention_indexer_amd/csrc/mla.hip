@@ -138,6 +138,22 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
     return pos;
   };
 
+  // The split's positions are loaded first and the query's fragments right
+  // after them; the positions go to LDS as soon as they arrive, so the first
+  // tiles' copies start while the query loads are still in flight (the
+  // positions are a few hundred bytes, the query 36 KiB a workgroup).
+  constexpr int kIdxPer = (kNarrowMaxRows + kThreads - 1) / kThreads;
+  int pv[kIdxPer];
+  if constexpr (!kDense) {
+    const int32_t* src = idx + (size_t)row * k + j_begin;
+#pragma unroll
+    for (int u = 0; u < kIdxPer; ++u) {
+      const int j = threadIdx.x + u * kThreads;
+      pv[u] = j < n_rows ? src[j] : -1;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the position loads go out before the query's
+
   // Query fragment (B operand of S^T = KV . Q^T): head hg*16*kWaves + wave*16 + r16;
   // K-step kk holds dims kk*32 + 8g .. +7 of [q_nope | q_pe].
   const int head = hg * S::kHeadsPerBlock + wave * 16 + r16;
@@ -150,15 +166,13 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = ldg16(qp + kk * 32 + g * 8);
   }
-  // The split's positions go to LDS in one go, their loads in flight together
-  // with the query's, so no tile's copies wait on a load of its positions.
   if constexpr (!kDense) {
-    const int32_t* src = idx + (size_t)row * k + j_begin;
-    for (int j = threadIdx.x; j < n_rows; j += kThreads) {
-      const int pos = src[j];
-      s_idx[j] = (pos < 0 || pos >= S_max) ? -1 : pos;
+#pragma unroll
+    for (int u = 0; u < kIdxPer; ++u) {
+      const int j = threadIdx.x + u * kThreads;
+      if (j < n_rows) s_idx[j] = (pv[u] < 0 || pv[u] >= S_max) ? -1 : pv[u];
     }
-    __syncthreads();
+    lds_barrier();  // LDS only: the query loads stay in flight
   }
 
   const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
