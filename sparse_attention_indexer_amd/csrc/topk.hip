@@ -568,20 +568,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
 // Too short a list (the sample misjudged the row) or an overflowing region
 // sends the row to full_row_topk.
 constexpr int kLeanMaxN = kChunk;                          // 32768
-constexpr int kLeanGroups = kLeanMaxN / kWave / kTkWaves;  // 64 groups per wave
-constexpr int kLeanCap = 16384;                            // keys >= L per row
-constexpr int kLeanRegion = kLeanCap / kTkWaves;           // 2048 per wave
 constexpr int kLeanExactN = 8192;                          // histogram every position up to here
 constexpr int kLeanSample = 4;                             // else every 4th group
 
-struct LeanShared {
+// kMaxN = 32768, or 8192 when S_max <= 8192 (prefill of up to 8192 tokens):
+// then every row takes the exact histogram, no wave region can overflow
+// (region = the wave's 1024 positions) and the list always holds k keys, so
+// full_row_topk and its LDS are never needed, and the lighter registers and
+// LDS let two workgroups share a CU.
+template <int kMaxN>
+struct LeanSharedT {
+  static constexpr int kCap = kMaxN > kLeanExactN ? 16384 : kMaxN;  // keys >= L per row
+  static constexpr int kRegion = kCap / kTkWaves;                  // per wave
   uint32_t hist[kHistWords];   // round 0 (the sample), then round 1, then round 3
   uint32_t hist2[kHistWords];  // round 2
-  uint32_t ck[kLeanCap];       // keys >= L; wave w's at [2048 w, 2048 w + ncw[w])
-  uint16_t cp[kLeanCap];       // their positions
-  uint32_t sure[kLeanMaxN / 32];
-  uint32_t eq[kLeanMaxN / 32];
-  uint32_t pre[kLeanMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
+  uint32_t ck[kCap];           // keys >= L; wave w's at [kRegion w, kRegion w + ncw[w])
+  uint16_t cp[kCap];           // their positions
+  uint32_t sure[kMaxN / 32];
+  uint32_t eq[kMaxN / 32];
+  uint32_t pre[kMaxN / 32];    // per-word prefixes of sure / eq (bitmap_prefixes)
   uint32_t ncw[kTkWaves];
   uint32_t wave[2 * kTkWaves];
   uint32_t sel[2];
@@ -589,16 +594,30 @@ struct LeanShared {
   uint32_t nsmall;
 };
 
-union LeanLds {
+template <int kMaxN>
+union LeanLdsFull {
   TopkShared full;
-  LeanShared lean;
+  LeanSharedT<kMaxN> lean;
 };
+template <int kMaxN>
+struct LeanLdsOnly {
+  LeanSharedT<kMaxN> lean;
+};
+template <int kMaxN>
+using LeanLds = typename std::conditional<(kMaxN > kLeanExactN), LeanLdsFull<kMaxN>,
+                                          LeanLdsOnly<kMaxN>>::type;
 
-__global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
+template <int kMaxN>
+__global__ __launch_bounds__(kTkThreads, kMaxN > kLeanExactN ? 1 : 4) void topk_lean_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ end_pos, int T, int S_max,
     int k, int32_t* __restrict__ out) {
-  __shared__ __align__(16) LeanLds lds;
-  LeanShared& sh = lds.lean;
+  constexpr int kLeanGroups = kMaxN / kWave / kTkWaves;  // 64-position groups per wave
+  constexpr int kLeanRegion = LeanSharedT<kMaxN>::kRegion;
+  static_assert(kLeanGroups * kWave * kTkWaves == kMaxN, "row fits the registers");
+  static_assert(kMaxN > kLeanExactN || kLeanRegion >= kLeanGroups * kWave,
+                "a wave's keys always fit its region");
+  __shared__ __align__(16) LeanLds<kMaxN> lds;
+  LeanSharedT<kMaxN>& sh = lds.lean;
   const int row = blockIdx.x;
   const int n = row_len(end_pos, row, T, S_max);
   const float* x = scores + (size_t)row * S_max;
@@ -610,7 +629,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
     for (int i = tid; i < k; i += kTkThreads) o[i] = i < n ? i : -1;
     return;
   }
-  bool ok = n <= kLeanMaxN;
+  bool ok = n <= kMaxN;
   if (ok) {
     // Group i of this wave holds positions 64 (8 i + wave) + lane.
     uint32_t key[kLeanGroups];
@@ -621,7 +640,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
       sh.hist[i] = 0;
       sh.hist2[i] = 0;
     }
-    for (int i = tid; i < kLeanMaxN / 32; i += kTkThreads) {
+    for (int i = tid; i < kMaxN / 32; i += kTkThreads) {
       sh.sure[i] = 0;
       sh.eq[i] = 0;
     }
@@ -776,14 +795,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_lean_kernel(
       }
     }
   }
-  if (!ok) {
-    __syncthreads();  // the list checks' reads are done before the LDS is reused
-    full_row_topk(x, n, k, o, lds.full);
+  if constexpr (kMaxN > kLeanExactN) {
+    if (!ok) {
+      __syncthreads();  // the list checks' reads are done before the LDS is reused
+      full_row_topk(x, n, k, o, lds.full);
+    }
   }
 }
-
-static_assert(kLeanGroups * kWave * kTkWaves == kLeanMaxN, "row fits the registers");
-static_assert(kTkThreads * 2 * 32 == kLeanMaxN, "two bitmap words per thread");
 
 static_assert(kTkThreads * 4 == kBins, "one 16-byte histogram piece per thread");
 
@@ -825,9 +843,14 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
     }
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
+  if (S_max <= kLeanExactN) {  // every row is at most 8192 long
+    hipLaunchKernelGGL(topk_lean_kernel<kLeanExactN>, dim3((unsigned)rows), dim3(kTkThreads), 0,
+                       stream, scores, end_pos, T, S_max, k, out);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   if (max_end_pos <= kLeanMaxN) {
-    hipLaunchKernelGGL(topk_lean_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream,
-                       scores, end_pos, T, S_max, k, out);
+    hipLaunchKernelGGL(topk_lean_kernel<kLeanMaxN>, dim3((unsigned)rows), dim3(kTkThreads), 0,
+                       stream, scores, end_pos, T, S_max, k, out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, scores,

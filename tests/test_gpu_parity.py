@@ -283,10 +283,14 @@ def test_topk_row_longer_than_promised(max_end_pos):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("B,T,S,kind", [(1, 1100, 3000, "ties"), (2, 520, 33000, "normal")])
+@pytest.mark.parametrize("B,T,S,kind", [(1, 1100, 3000, "ties"), (2, 520, 33000, "normal"),
+                                        (1, 1100, 8192, "equal"), (1, 1030, 8192, "relu"),
+                                        (2, 520, 8193, "zeros")])
 def test_topk_many_rows(B, T, S, kind):
     """More than 1024 query rows: one workgroup per row (rows of up to 32768
-    positions held in registers, longer ones chunk by chunk)."""
+    positions held in registers, longer ones chunk by chunk; with S_max <= 8192
+    the lighter form whose list always holds k keys - an all-equal row puts
+    every position in it)."""
     m = dsa()
     banner(f"topk many rows B={B} T={T} S={S}")
     k = 2048
