@@ -151,17 +151,19 @@ def test_indexer_integer_prefill_exact():
     assert np.array_equal(gpu.cpu().numpy()[msk], ref[msk])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_indexer_prefill_ragged(dtype):
-    """The prefill form (16 queries per workgroup, 64-key LDS tiles, 1024-key
-    chunks): T not a multiple of 16, a sequence whose queries start deep in
-    its cache, and one starting at position 0."""
+@pytest.mark.parametrize("dtype,T,ep0,S", [("bf16", 37, 2300, 2300), ("fp8", 37, 2300, 2300),
+                                           ("bf16", 8, 4100, 4200), ("fp8", 15, 2049, 2100)])
+def test_indexer_prefill_ragged(dtype, T, ep0, S):
+    """The prefill form (8 queries per workgroup, 64-key LDS tiles, 2048-key
+    chunks): T not a multiple of 8 (or exactly the smallest T that takes the
+    form), a sequence whose queries start deep in its cache (ranges ending
+    just past a chunk), and one starting at position 0."""
     m = dsa()
-    banner(f"indexer prefill ragged {dtype}")
-    case = inputs.make_case("prefill_ragged", 2, 37, [2300, 37], 2300, dtype=dtype, seed=11,
+    banner(f"indexer prefill ragged {dtype} T={T} end_pos={ep0}")
+    case = inputs.make_case("prefill_ragged", 2, T, [ep0, T], S, dtype=dtype, seed=11,
                             device=DEV)
     gpu = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale,
-                         q_scale=case.q_scale, k_scale=case.k_scale, max_end_pos=2300)
+                         q_scale=case.q_scale, k_scale=case.k_scale, max_end_pos=ep0)
     h = np_case(case)
     ref = oracle_scores(case, h)
     assert_scores_close(gpu.cpu().numpy(), ref, h["end_pos"], case.T, SCORE_TOL[dtype])
