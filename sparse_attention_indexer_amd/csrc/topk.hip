@@ -313,7 +313,10 @@ __device__ __noinline__ void full_row_topk(const float* __restrict__ x, int n, i
 // positions (topk_split_kernel), and a second launch with one workgroup per
 // row finishes it (topk_finish_kernel).
 //   1. Every workgroup derives the same cut L from the same 2048 sampled
-//      positions of the row (floor(j n / 2048)): the 22-bit key prefix of the
+//      positions of the row, 128 evenly spaced runs of 16 consecutive ones
+//      (run g starts at floor(g (n - 16) / 127); one 64-byte segment per run,
+//      where single positions at a stride cost a cache line each and made
+//      the sample most of a long row's traffic): the 22-bit key prefix of the
 //      sample's T_s-th largest key, T_s being the sample's expected count of
 //      keys above the k-th largest plus four standard deviations (and 16).
 //   2. It appends its keys >= L with their positions to the row's list in the
@@ -448,9 +451,13 @@ __global__ __launch_bounds__(kTkThreads, kFallback ? 1 : 4) void topk_split_kern
   for (int u = 0; u < kSpPer; ++u)
     kv[u] = __float_as_uint(x[min(base + tid + kTkThreads * u, n - 1)]);
 #pragma unroll
-  for (int u = 0; u < kSpSamplePer; ++u)
-    ks[u] = __float_as_uint(
-        x[(int)(((uint64_t)(tid + kTkThreads * u) * (uint64_t)n) / (uint64_t)kSpSample)]);
+  for (int u = 0; u < kSpSamplePer; ++u) {
+    const int s = tid + kTkThreads * u;  // sample s: run s / 16, position s % 16 in it
+    const int pos = n >= kSpSample
+                        ? (int)(((uint64_t)(s >> 4) * (uint64_t)(n - 16)) / (kSpSample / 16 - 1)) + (s & 15)
+                        : (int)(((uint64_t)s * (uint64_t)n) / (uint64_t)kSpSample);
+    ks[u] = __float_as_uint(x[pos]);
+  }
   if (nb == 1) {
     // The whole row is in this workgroup's registers: select over it directly.
     uint32_t pv[kSpPer];

@@ -536,17 +536,20 @@ def test_forward_rows_mix():
 
 def test_forward_sample_misjudged():
     """A 32768-token row built so that the split top-k's sampled cut lets fewer than k
-    candidates through: of the sampled positions (every 16th) the even-numbered ones score
-    highest and the odd-numbered ones lowest, all other positions in between and equal.
-    The finishing launch then selects over the whole row; the answer is the 1024 high
-    positions plus the first 1024 of the middle ones (ties to the smaller position)."""
+    candidates through.  The sample is 128 evenly spaced runs of 16 consecutive positions
+    (run g starts at floor(g (n - 16) / 127)); the even-numbered runs score highest, the
+    odd-numbered ones lowest, every other position in between and equal.  The sample's
+    cut then admits only the 1024 high positions, and the finishing launch selects over the
+    whole row; the answer is those 1024 plus the first 1024 of the middle ones (ties to
+    the smaller position)."""
     banner("forward, sample misjudged")
     n = 32768
     case = inputs.make_case("fused_fallback", 1, 1, [n], n, seed=18, device=DEV)
-    pos = torch.arange(n)
+    starts = (np.arange(128) * (n - 16)) // 127
+    runs = starts[:, None] + np.arange(16)[None, :]
     c = torch.full((n,), 2.0)
-    c[pos % 32 == 0] = 3.0
-    c[pos % 32 == 16] = 1.0
+    c[torch.from_numpy(runs[0::2].ravel())] = 3.0
+    c[torch.from_numpy(runs[1::2].ravel())] = 1.0
     q = torch.zeros(1, 1, 64, 128)
     q[..., 0] = 1.0
     k_cache = torch.zeros(1, n, 128)
@@ -555,7 +558,8 @@ def test_forward_sample_misjudged():
     case.w = torch.ones(1, 1, 64, device=DEV)
     case.k_cache = k_cache.to(torch.bfloat16).to(DEV)
     out, lse, idx, ref_s, ref_idx, o_ref, lse_ref, h = _forward_and_oracle(case)
-    expect = np.sort(np.concatenate([np.arange(0, n, 32), np.flatnonzero(pos.numpy() % 16 != 0)[:1024]]))
+    cn = c.numpy()
+    expect = np.sort(np.concatenate([np.flatnonzero(cn == 3.0), np.flatnonzero(cn == 2.0)[:1024]]))
     assert np.array_equal(ref_idx[0, 0], expect)
     assert np.array_equal(idx, ref_idx)
     assert_out_close(out, lse, o_ref, lse_ref)
