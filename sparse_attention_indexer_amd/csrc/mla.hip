@@ -380,7 +380,6 @@ constexpr int kWdThreads = kWdWaves * 64;
 constexpr int kWdRt = 32;                               // rows per tile
 constexpr int kWdRw = kWdRt / kWdWaves;                 // rows each wave copies (4)
 constexpr int kWdNbuf = 3;
-constexpr int kWdLoads = 2 * kWdRw;                     // copies per wave per tile
 // Latent rows sit 1056 bytes apart (8 banks), and the 16-byte chunks of rows
 // 8..15 and 24..31 of a tile are XOR-swizzled by 1: chunk c of row r is at
 // position c ^ ((r >> 3) & 1).  The score reads (16 rows, one chunk each per
