@@ -748,13 +748,16 @@ static_assert(kCbThreads == (kDc / 16) * kCbHeads * 4 && kHeads % kCbHeads == 0,
               "one thread per (16-dim tile, head, quarter of the tile)");
 // kParts > 1 (few rows): each workgroup takes 1/kParts of the 32 dim tiles
 // with kCbThreads/kParts threads, so more workgroups share the loads (every
-// part repeats the weights of its four heads, which needs four waves).
+// part repeats the weights of its four heads; with fewer than four waves a
+// wave makes the weights of several heads).
 template <int kBatch, int kParts>
 __global__ __launch_bounds__(kCbThreads / kParts) void mla_combine_kernel(
     const uint16_t* __restrict__ part_o, const float4* __restrict__ part_ml, int n_splits,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(kBatch % 4 == 0 && kBatch <= 32, "batches of 4 to 32 splits");
-  static_assert(kCbThreads / kParts >= 64 * kCbHeads, "a wave per head for the weights");
+  constexpr int kWavesB = kCbThreads / kParts / 64;
+  constexpr int kHpw = kCbHeads > kWavesB ? kCbHeads / kWavesB : 1;  // heads whose weights a wave makes
+  static_assert(kHpw * kWavesB >= kCbHeads, "every head's weights have a wave");
   constexpr int kGroups = kHeads / kCbHeads;
   const int part = blockIdx.x % kParts, gid = blockIdx.x / kParts;
   const int row = gid / kGroups, h0 = (gid - row * kGroups) * kCbHeads;
@@ -768,25 +771,31 @@ __global__ __launch_bounds__(kCbThreads / kParts) void mla_combine_kernel(
   __shared__ float s_alpha[2][kCbHeads];
   __shared__ float s_inv[kCbHeads];
   float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f, M = -INFINITY;  // kept by wave q < 4 for head h0 + q
+  float L[kHpw], M[kHpw];  // kept by wave q for heads h0 + q + kWavesB * i
+#pragma unroll
+  for (int i = 0; i < kHpw; ++i) L[i] = 0.f, M[i] = -INFINITY;
   int par = 0;
   for (int s0 = 0; s0 < n_splits; s0 += kBatch, par ^= 1) {
     uint2 a[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
       a[u] = *reinterpret_cast<const uint2*>(src + (size_t)min(s0 + u, n_splits - 1) * stride);
-    if (wave < kCbHeads) {
-      const int s = min(s0 + min(lane, kBatch - 1), n_splits - 1);
-      const float4 v = part_ml[(item0 + s) * kHeads + h0 + wave];
-      const bool valid = lane < kBatch && s0 + lane < n_splits && v.y > 0.f;
-      const float mb = fmaxf(M, wave_max_f(valid ? v.x : -INFINITY));
-      // Nothing was accumulated while M was -inf, so the factor is then moot.
-      const float alpha = M == -INFINITY ? 0.f : exp2f(M - mb);
-      const float w = valid ? exp2f(v.x - mb) : 0.f;
-      L = L * alpha + wave_sum_f(w * v.y);
-      M = mb;
-      if (lane < kBatch) s_w[par][wave][lane] = w;
-      if (lane == 0) s_alpha[par][wave] = alpha;
+#pragma unroll
+    for (int i = 0; i < kHpw; ++i) {
+      const int hq = wave + kWavesB * i;
+      if (hq < kCbHeads) {
+        const int s = min(s0 + min(lane, kBatch - 1), n_splits - 1);
+        const float4 v = part_ml[(item0 + s) * kHeads + h0 + hq];
+        const bool valid = lane < kBatch && s0 + lane < n_splits && v.y > 0.f;
+        const float mb = fmaxf(M[i], wave_max_f(valid ? v.x : -INFINITY));
+        // Nothing was accumulated while M was -inf, so the factor is then moot.
+        const float alpha = M[i] == -INFINITY ? 0.f : exp2f(M[i] - mb);
+        const float w = valid ? exp2f(v.x - mb) : 0.f;
+        L[i] = L[i] * alpha + wave_sum_f(w * v.y);
+        M[i] = mb;
+        if (lane < kBatch) s_w[par][hq][lane] = w;
+        if (lane == 0) s_alpha[par][hq] = alpha;
+      }
     }
     // One barrier per batch: a wave can only refill this parity's weights
     // after every wave has passed the next batch's barrier.
@@ -810,10 +819,14 @@ __global__ __launch_bounds__(kCbThreads / kParts) void mla_combine_kernel(
       }
     }
   }
-  if (wave < kCbHeads && lane == 0) {
-    s_inv[wave] = L > 0.f ? 1.f / L : 0.f;
-    if (lse != nullptr && part == 0)
-      lse[(size_t)row * kHeads + h0 + wave] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kHpw; ++i) {
+    const int hq = wave + kWavesB * i;
+    if (hq < kCbHeads && lane == 0) {
+      s_inv[hq] = L[i] > 0.f ? 1.f / L[i] : 0.f;
+      if (lse != nullptr && part == 0)
+        lse[(size_t)row * kHeads + h0 + hq] = L[i] > 0.f ? (M[i] + log2f(L[i])) * kLn2 : -INFINITY;
+    }
   }
   __syncthreads();
   const float inv = s_inv[q];
@@ -944,13 +957,13 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
     uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
     const unsigned groups = (unsigned)(rows * (kHeads / kCbHeads));
     if (rows <= DSA_CB_SPLIT_ROWS) {
-      // Few rows: two workgroups per head group, so twice as many CUs load.
-      const dim3 grid(2 * groups), block(kCbThreads / 2);
+      // Few rows: four workgroups per head group, so four times as many CUs load.
+      const dim3 grid(4 * groups), block(kCbThreads / 4);
       if (plan.n_splits <= 16)
-        hipLaunchKernelGGL((mla_combine_kernel<16, 2>), grid, block, 0, stream, part_o, part_ml,
+        hipLaunchKernelGGL((mla_combine_kernel<16, 4>), grid, block, 0, stream, part_o, part_ml,
                            plan.n_splits, o16, lse);
       else
-        hipLaunchKernelGGL((mla_combine_kernel<32, 2>), grid, block, 0, stream, part_o, part_ml,
+        hipLaunchKernelGGL((mla_combine_kernel<32, 4>), grid, block, 0, stream, part_o, part_ml,
                            plan.n_splits, o16, lse);
     } else {
       const dim3 grid(groups), block(kCbThreads);
