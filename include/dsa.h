@@ -117,13 +117,11 @@ int dsa_index_scores(const void* q, const float* q_scale, const float* weights,
  * Integer-only selection (order-preserving 32-bit keys): the result is
  * exact.  1 <= k <= 2048.
  * Workspace: dsa_topk_workspace_size bytes, 256-byte aligned (0 bytes, and
- * NULL allowed, when S_max <= 32768 or B*T > 1024).  Part of it carries a
- * per-row histogram from one call to the next; the call leaves it zeroed.
- * Zero-fill the workspace once after allocating it to get the fast path from
- * the first call; with any other content the result is still exact (the call
- * detects that its candidate set cannot be trusted and selects over the
- * whole row), only slower for that call.  Calls that overlap in time must not
- * share a workspace. */
+ * NULL allowed, when B*T > 1024; otherwise 64 KiB per row when S_max <= 4096
+ * and 256 KiB per row above that).  It holds the per-row candidate lists of
+ * one call; its contents on entry do not matter (the call clears whatever it
+ * needs cleared) and are unspecified afterwards.  Calls that overlap in time
+ * must not share a workspace. */
 size_t dsa_topk_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k);
 int dsa_topk(const float* index_score, const int32_t* end_pos, int32_t B, int32_t T,
              int32_t S_max, int32_t max_end_pos, int32_t k, int32_t* topk_indices,
@@ -155,8 +153,9 @@ int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* kv_cache,
 
 /* (a)+(b)+(c) on one stream: the decode step of "DeepSeek-V3.2-Exp - Apply
  * sparse mask" with the indexer of "Keep top-k positions".  Arguments are
- * those of the three calls; index_score, the indices and the top-k
- * workspace (see dsa_topk: zero-fill once) live in the workspace.  topk_indices_out [B,T,k] receives a copy of the selection if
+ * those of the three calls; index_score, the indices, the top-k lists and
+ * the attention's split partials live in the workspace, whose contents on
+ * entry do not matter.  topk_indices_out [B,T,k] receives the selection if
  * not NULL.  When every query has at most k valid positions every position
  * is kept, which equals dense attention (the short-context case). */
 size_t dsa_forward_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k);

@@ -12,6 +12,12 @@ Stages (same names as the C ABI, without the ``dsa_`` prefix):
   sparse_mla    absorbed MLA (128 heads, 512 latent + 64 rope) over the selected rows
   forward       the three stages on one stream
   dense_mla     the same attention over every valid position (baseline)
+
+Defaults that matter for capture and latency: without ``max_end_pos`` the
+calls use S_max as the bound on end_pos (no device->host sync); without
+``workspace`` (or ``out``) they take one from torch's caching allocator on
+every call.  Passing both keeps a call free of syncs and allocations, so it
+can be captured into a HIP graph.
 """
 from __future__ import annotations
 
@@ -116,20 +122,21 @@ def _need(t, name, dtype, shape=None, device=None):
     return t
 
 
-def _max_end_pos(end_pos, max_end_pos):
-    # end_pos lives on the device; the host bound is needed for the grid.  Passing
-    # it avoids a device->host sync.
-    return int(end_pos.max().item()) if max_end_pos is None else int(max_end_pos)
+def _max_end_pos(max_end_pos, S_max):
+    # end_pos lives on the device and the grid needs a host bound.  Without the
+    # caller's bound S_max serves (always valid, as end_pos <= S_max): no
+    # device->host sync, only more workgroups that find nothing to do.
+    return int(S_max) if max_end_pos is None else int(max_end_pos)
 
 
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        # Zero-filled: the top-k stage keeps a per-row histogram in its workspace
-        # between calls and expects zeros the first time (any other content is
-        # still correct, only slower once).
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        # The kernels need nothing in particular in it on entry.  This comes from
+        # torch's caching allocator (a hipMalloc only when its pool is short);
+        # pass a workspace to keep allocation out of the call altogether.
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace of {workspace.numel()} bytes < required {nbytes}")
     return workspace, workspace.numel() * workspace.element_size()
@@ -154,7 +161,7 @@ def index_scores(q, weights, k_cache, end_pos, scale, q_scale=None, k_scale=None
     _need(out, "out", torch.float32, (B, T, S_max), dev)
     st = lib().dsa_index_scores(_ptr(q), _ptr(q_scale) if fp8 else None, _ptr(weights),
                                 _ptr(k_cache), _ptr(k_scale) if fp8 else None, _ptr(end_pos),
-                                B, T, S_max, _max_end_pos(end_pos, max_end_pos), float(scale),
+                                B, T, S_max, _max_end_pos(max_end_pos, S_max), float(scale),
                                 FP8_E4M3 if fp8 else BF16, _ptr(out), _stream(stream))
     _check(st, "dsa_index_scores")
     return out
@@ -172,7 +179,7 @@ def topk(index_score, end_pos, k=MAX_TOPK, max_end_pos=None, out=None, workspace
     _need(out, "out", torch.int32, (B, T, k), dev)
     ws, nb = _workspace(lib().dsa_topk_workspace_size(B, T, S_max, k), dev, workspace)
     st = lib().dsa_topk(_ptr(index_score), _ptr(end_pos), B, T, S_max,
-                        _max_end_pos(end_pos, max_end_pos), int(k), _ptr(out), _ptr(ws), nb,
+                        _max_end_pos(max_end_pos, S_max), int(k), _ptr(out), _ptr(ws), nb,
                         _stream(stream))
     _check(st, "dsa_topk")
     return out
@@ -223,7 +230,7 @@ def dense_mla(q_nope, q_pe, kv_cache, pe_cache, end_pos, softmax_scale, max_end_
     out, lse = _mla_outputs(B, T, dev, out, lse, want_lse)
     ws, nb = _workspace(lib().dsa_dense_mla_workspace_size(B, T, S_max), dev, workspace)
     st = lib().dsa_dense_mla(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
-                             _ptr(end_pos), B, T, S_max, _max_end_pos(end_pos, max_end_pos),
+                             _ptr(end_pos), B, T, S_max, _max_end_pos(max_end_pos, S_max),
                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), nb,
                              _stream(stream))
     _check(st, "dsa_dense_mla")
@@ -352,7 +359,7 @@ def forward(q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cache, inde
     st = lib().dsa_forward(_ptr(q), _ptr(q_scale) if fp8 else None, _ptr(weights),
                            _ptr(k_cache), _ptr(k_scale) if fp8 else None, _ptr(end_pos),
                            _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache), B, T, S_max,
-                           _max_end_pos(end_pos, max_end_pos), int(k), float(index_scale),
+                           _max_end_pos(max_end_pos, S_max), int(k), float(index_scale),
                            float(softmax_scale), FP8_E4M3 if fp8 else BF16, _ptr(out),
                            _ptr(lse), _ptr(topk_out), _ptr(ws), nb, _stream(stream))
     _check(st, "dsa_forward")

@@ -194,8 +194,8 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   int32_t* indices =
       topk_indices_out ? topk_indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
-  // The indexer also clears the top-k's per-row counters.
-  uint32_t* topk_ctr = dsa::topk_counters(ws + L.topk_ws, B, T);
+  // The indexer also clears the top-k's per-row counters (when that path has them).
+  uint32_t* topk_ctr = dsa::topk_counters(ws + L.topk_ws, B, T, max_end_pos);
   st = dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
                                 max_end_pos, index_scale, dtype, scores, topk_ctr, stream);
   if (st) return st;

@@ -19,8 +19,8 @@ int launch_index_scores(const void* q, const float* q_scale, const float* w, con
 
 size_t topk_workspace_bytes(int B, int T, int S_max, int k);
 // The per-row counters at the start of the top-k workspace, or nullptr when
-// B*T rows take a path without them.
-uint32_t* topk_counters(void* workspace, int B, int T);
+// B*T rows of at most max_end_pos positions take a path without them.
+uint32_t* topk_counters(void* workspace, int B, int T, int max_end_pos);
 int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S_max,
                 int max_end_pos, int k, int32_t* out, void* workspace, bool counters_clear,
                 hipStream_t stream);
@@ -30,6 +30,7 @@ struct MlaPlan {
   int rows_per_split;
   int n_splits;
   int waves;  // 2 or 4 (16 heads per wave, 32 or 64 per block) or 8 (all 128 heads per block)
+  bool tile = false;  // the 4-wave, 32-head form with one 64-row tile per block
 };
 MlaPlan sparse_mla_plan(int B, int T, int k);
 MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos);

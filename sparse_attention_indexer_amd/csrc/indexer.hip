@@ -17,6 +17,7 @@
 // in registers, and two cross-lane adds finish the sum over 64 heads.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "select.h"
 
 namespace dsa {
 

@@ -352,6 +352,256 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
   }
 }
 
+// ---- Tile form: few query rows, one 64-row tile per workgroup -------------
+//
+// Four waves (one per SIMD) and 32 heads (a head group) per workgroup, and one
+// tile of 64 rows of the list per workgroup, so a decode query spreads over
+// (k / 64) * 4 workgroups with every SIMD of a CU busy.  The two contractions
+// are split differently between the waves:
+//   scores  S^T[row][head]: wave w takes rows 16w..16w+15 of the tile for all
+//           32 heads, so every K fragment read from LDS feeds two MFMAs (the
+//           query fragments of both 16-head tiles, 36 x 16 bytes a lane, come
+//           from an LDS copy of the head group's query);
+//   values  O^T[c][head]: wave w takes latent dims 128w..128w+127 for all 32
+//           heads (8 x 2 accumulator tiles), each transposed V fragment
+//           feeding two MFMAs.
+// The probabilities cross through LDS: value K-step s covers tile rows
+// 32s..32s+31 in the order rows 32s+4g+i then 32s+16+4g+i (i < 4) for lane
+// group g, so score wave 2s+h's lane holds exactly half (h) of the B fragment
+// that the same lane of every value wave needs.  The tile's maximum per head
+// (over the four score waves, through LDS) is the softmax reference, so there
+// is no rescaling.  Latent rows sit 1056 bytes apart with chunk c of row r at
+// c ^ ((r >> 3) & 1), as in the wide form; rope parts are 128-byte rows with
+// chunk c at c ^ (r & 7).
+constexpr int kTfWaves = 4;
+constexpr int kTfThreads = kTfWaves * 64;
+constexpr int kTfHeads = 32;
+constexpr int kTfRows = 64;
+constexpr int kTfPitch = 1056;
+constexpr int kTfGroups = kHeads / kTfHeads;  // 4 head groups
+constexpr int kTfQPitch = kDc * 2 + 16;       // q_nope rows in LDS, 16 bytes apart in bank
+
+template <bool kDense>
+__global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
+    int k, int n_splits, int n_items, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ part_o, float4* __restrict__ part_ml) {
+  __shared__ __align__(16) uint8_t s_qn[kTfHeads * kTfQPitch];  // the head group's q_nope rows
+  __shared__ __align__(16) uint8_t s_qp[kTfHeads * kDr * 2];   // and q_pe rows
+  __shared__ __align__(16) uint8_t s_kv[kTfRows * kTfPitch];   // the tile's latent rows
+  __shared__ __align__(16) uint8_t s_pe[kTfRows * kDr * 2];    // and rope parts
+  __shared__ __align__(16) uint4 s_p[2][2][64];               // P fragments [K-step][head tile][lane]
+  __shared__ float s_red[2][kTfWaves][kTfHeads];              // per-wave max, then sum, per head
+  __shared__ int s_pos[kTfRows];
+
+  // Block -> (item, head group): the head groups of one item get ids 8 apart
+  // (the same XCD under round-robin dispatch), so they share its L2.
+  const int bid = blockIdx.x;
+  const int X = (bid / (8 * kTfGroups)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % kTfGroups;
+  if (X >= n_items) return;
+  const int row = X / n_splits, split = X - row * n_splits;
+  const int b = row / T, t = row - b * T;
+  int n_list;
+  if (kDense || end_pos != nullptr) {
+    const int ep = min(max(end_pos[b], T), S_max);
+    n_list = ep - T + t + 1;
+    if (!kDense) n_list = min(n_list, k);
+  } else {
+    n_list = k;
+  }
+  const int j_begin = split * kTfRows;
+  const int n_rows = max(min(kTfRows, n_list - j_begin), 0);
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // The tile's positions first (they address the gathers), then the query.
+  int pos = -1;
+  if (tid < kTfRows && tid < n_rows) {
+    if constexpr (kDense) pos = j_begin + tid;
+    else {
+      pos = idx[(size_t)row * k + j_begin + tid];
+      if (pos < 0 || pos >= S_max) pos = -1;
+    }
+  }
+  {
+    // Query: 32 rows of 1 KiB (one per head) and 4 KiB of rope parts, 36
+    // copies of 1 KiB, nine a wave.
+    const int ln = opaque_lane();
+    const size_t h0 = (size_t)row * kHeads + hg * kTfHeads;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const int cc = wv * 9 + c;
+      if (cc < kTfHeads) {
+        lds_copy16_v(reinterpret_cast<const uint8_t*>(q_nope + (h0 + cc) * kDc) + ln * 16,
+                     __builtin_amdgcn_readfirstlane(lds_addr(s_qn + cc * kTfQPitch)));
+      } else {
+        const int c4 = cc - kTfHeads;  // 8 heads' rope parts
+        lds_copy16_v(reinterpret_cast<const uint8_t*>(q_pe + (h0 + 8 * c4) * kDr) + ln * 16,
+                     __builtin_amdgcn_readfirstlane(lds_addr(s_qp + c4 * 1024)));
+      }
+    }
+  }
+  if (tid < kTfRows) s_pos[tid] = pos;
+  lds_barrier();  // positions visible; the query copies stay in flight
+
+  // Gathers: wave w copies rows 16w..16w+15 (one instruction per latent row,
+  // two for the sixteen rope parts).
+  const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
+  const uint8_t* pe_b = reinterpret_cast<const uint8_t*>(pe) + (size_t)b * S_max * kDr * 2;
+  {
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int trow = 16 * wv + r;
+      const int pu = max(__builtin_amdgcn_readfirstlane(s_pos[trow]), 0);
+      lds_copy16(kv_b + (size_t)pu * (kDc * 2), (ln ^ ((trow >> 3) & 1)) * 16,
+                 __builtin_amdgcn_readfirstlane(lds_addr(s_kv + trow * kTfPitch)));
+    }
+#pragma unroll
+    for (int q8 = 0; q8 < 2; ++q8) {
+      const int trow = 16 * wv + 8 * q8 + (ln >> 3);
+      const int pu = max(s_pos[trow], 0);
+      const int chunk = (ln & 7) ^ (trow & 7);
+      lds_copy16_v(pe_b + (size_t)pu * (kDr * 2) + chunk * 16,
+                   __builtin_amdgcn_readfirstlane(lds_addr(s_pe + (16 * wv + 8 * q8) * 128)));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  lds_barrier();  // every wave's copies have landed
+
+  // Query fragments (B operand): head 16 ht + r16 of the group, K-step kk
+  // holds dims 32 kk + 8g .. +7 of [q_nope | q_pe].
+  uint4 qb[2][18];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = 16 * ht + r16;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      qb[ht][kk] = *reinterpret_cast<const uint4*>(s_qn + h * kTfQPitch + kk * 64 + g * 16);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      qb[ht][16 + kk] = *reinterpret_cast<const uint4*>(s_qp + h * kDr * 2 + kk * 64 + g * 16);
+  }
+
+  // ---- scores S^T[row][head] for rows 16w + 4g + i ----
+  f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  {
+    const int trow = 16 * wv + r16;
+    const uint8_t* kb = s_kv + trow * kTfPitch;
+    const int sw = (trow >> 3) & 1;
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const uint8_t* a = kk < 16 ? kb + (((4 * kk + g) ^ sw) << 4)
+                                 : s_pe + trow * 128 + ((((kk - 16) * 4 + g) ^ (trow & 7)) << 4);
+      const uint4 kf = *reinterpret_cast<const uint4*>(a);
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) sc[ht] = mfma_bf16_16x16x32(as_bf16x8(kf), as_bf16x8(qb[ht][kk]), sc[ht]);
+    }
+  }
+  // Mask the empty rows, then the tile's maximum per head.
+  float mx[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    mx[ht] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = s_pos[16 * wv + 4 * g + i] >= 0;
+      sc[ht][i] = valid ? sc[ht][i] * scale_log2 : -INFINITY;  // log2-domain score
+      mx[ht] = fmaxf(mx[ht], sc[ht][i]);
+    }
+    mx[ht] = group_max(mx[ht]);
+    if (g == 0) s_red[0][wv][16 * ht + r16] = mx[ht];
+  }
+  lds_barrier();
+  float m_ref[2], psum[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    float m = s_red[0][0][16 * ht + r16];
+#pragma unroll
+    for (int w = 1; w < kTfWaves; ++w) m = fmaxf(m, s_red[0][w][16 * ht + r16]);
+    m_ref[ht] = m;
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float p[4];
+    psum[ht] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2f(sc[ht][i] - m_use);
+      psum[ht] += p[i];
+    }
+    // Half (wv & 1) of K-step wv / 2's B fragment for this head tile.
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&s_p[wv >> 1][ht][lane]) + 2 * (wv & 1);
+    *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+    psum[ht] = group_sum(psum[ht]);
+    if (g == 0) s_red[1][wv][16 * ht + r16] = psum[ht];
+  }
+  lds_barrier();  // P fragments and the per-wave sums are visible
+
+  // ---- values O^T[c][head] for dims 128w .. 128w + 127 ----
+  f32x4 o[8][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j][0] = o[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* vrow = s_kv + (4 * g + (r16 >> 2)) * kTfPitch + 8 * (r16 & 1);
+    const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 pb0 = s_p[ks][0][lane], pb1 = s_p[ks][1][lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ct = 8 * wv + j;
+        const int off = ((2 * ct + vch) ^ vsw) << 4;
+        const uint8_t* base = vrow + 32 * ks * kTfPitch + off;
+        const i16x4 lo = lds_read_tr16(base);
+        const i16x4 hi = lds_read_tr16(base + 16 * kTfPitch);
+        const uint4 va = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        o[j][0] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb0), o[j][0]);
+        o[j][1] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb1), o[j][1]);
+      }
+    }
+  }
+
+  // ---- finish ----
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int hl = 16 * ht + r16;  // head within the group
+    const int head = hg * kTfHeads + hl;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kTfWaves; ++w) l += s_red[1][w][hl];
+    const float m = m_ref[ht];
+    if (n_splits == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* orow = out + ((size_t)row * kHeads + head) * kDc + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ct = 8 * wv + j;
+        *reinterpret_cast<uint2*>(orow + ct * 16) =
+            uint2{pack_bf16(o[j][ht][0] * inv, o[j][ht][1] * inv),
+                  pack_bf16(o[j][ht][2] * inv, o[j][ht][3] * inv)};
+      }
+      if (lse != nullptr && wv == 0 && g == 0)
+        lse[(size_t)row * kHeads + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      // Partial: the accumulator relative to 2^m, bf16, [item][tile][head][16].
+      uint16_t* prow = part_o + (size_t)X * kHeads * kDc + head * 16 + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ct = 8 * wv + j;
+        *reinterpret_cast<uint2*>(prow + ct * kHeads * 16) =
+            uint2{pack_bf16(o[j][ht][0], o[j][ht][1]), pack_bf16(o[j][ht][2], o[j][ht][3])};
+      }
+      if (wv == 0 && g == 0) part_ml[(size_t)X * kHeads + head] = float4{m, l, 0.f, 0.f};
+    }
+  }
+}
+
 // ---- Wide form: many query rows -------------------------------------------
 //
 // Eight waves (two per SIMD).  The two contractions are split differently:
@@ -861,8 +1111,14 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // about one block per CU.
 static int narrow_waves(long rows) { return rows <= 2 ? 2 : 4; }
 
+#ifndef DSA_MLA_TILE_ROWS
+#define DSA_MLA_TILE_ROWS 16
+#endif
+
 MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
+  if (rows <= DSA_MLA_TILE_ROWS)  // one 64-row tile per workgroup of 32 heads
+    return MlaPlan{kTfRows, (k + kTfRows - 1) / kTfRows, kTfWaves, true};
   if (rows <= DSA_MLA_SMALL_ROWS) {
     // Splits of k*rows/128 rows (a power of two, at least DSA_MLA_SMALL_SPLIT_MIN):
     // about 128 items of 2 head groups each.
@@ -885,6 +1141,8 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   // computed from S_max always covers the launch.
   // Few rows over a short context: the small-batch shape, as on the sparse
   // path; otherwise 8-wave blocks, which gather every row once for all heads.
+  if (rows <= DSA_MLA_TILE_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK)
+    return MlaPlan{kTfRows, (ext + kTfRows - 1) / kTfRows, kTfWaves, true};
   if (rows <= DSA_MLA_SMALL_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK) {
     int rps = DSA_MLA_SMALL_SPLIT_MIN;
     while (rps < kMaxSplitRows && (long)rps * 128 < (long)S_max * rows) rps *= 2;
@@ -936,7 +1194,16 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
     part_ml = reinterpret_cast<float4*>(part_o + (size_t)n_items * kHeads * kDc);
   }
   int st;
-  if (plan.waves == 8) {
+  if (plan.tile) {
+    const unsigned grid = (unsigned)(((n_items + 7) / 8) * 8 * kTfGroups);
+    hipLaunchKernelGGL((mla_tile_kernel<kDense>), dim3(grid), dim3(kTfThreads), 0, stream,
+                       reinterpret_cast<const uint16_t*>(q_nope),
+                       reinterpret_cast<const uint16_t*>(q_pe),
+                       reinterpret_cast<const uint16_t*>(kv), reinterpret_cast<const uint16_t*>(pe),
+                       idx, end_pos, T, S_max, k, plan.n_splits, n_items, softmax_scale * kLog2e,
+                       reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
+    st = hipGetLastError() == hipSuccess ? 0 : -5;
+  } else if (plan.waves == 8) {
     hipLaunchKernelGGL((mla_wide_kernel<kDense>), dim3((unsigned)n_items), dim3(kWdThreads), 0,
                        stream, reinterpret_cast<const uint16_t*>(q_nope),
                        reinterpret_cast<const uint16_t*>(q_pe),

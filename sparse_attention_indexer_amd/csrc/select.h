@@ -165,12 +165,25 @@ __device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
   const int lane = threadIdx.x & 63;
   const bool valid = lane < (int)m;
   const uint32_t mine = s_small[min(lane, (int)m - 1)];
-  uint32_t gt = 0, ge = 0;
-  for (int j = 0; j < (int)m; ++j) {
-    const uint32_t other = s_small[j];
-    gt += other > mine ? 1u : 0u;
-    ge += other >= mine ? 1u : 0u;
+  // All 64 slots in 16-byte reads issued together (the same address in every
+  // lane: broadcast reads); slots past m are skipped.  Four counters per
+  // relation keep the dependent adds in four short chains rather than one long
+  // one (a single wave pays the full latency of every dependent instruction).
+  const uint4* s4 = reinterpret_cast<const uint4*>(s_small);
+  uint32_t gt4[4] = {0u, 0u, 0u, 0u}, ge4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < kWave / 4; ++q) {
+    const uint4 o4 = s4[q];
+    const uint32_t other[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = 4 * q + i < (int)m;
+      gt4[i] += in && other[i] > mine ? 1u : 0u;
+      ge4[i] += in && other[i] >= mine ? 1u : 0u;
+    }
   }
+  const uint32_t gt = (gt4[0] + gt4[1]) + (gt4[2] + gt4[3]);
+  const uint32_t ge = (ge4[0] + ge4[1]) + (ge4[2] + ge4[3]);
   // Fewer than `remaining` keys above it, at least `remaining` at or above it.
   const bool hit = valid && gt < remaining && remaining <= ge;
   const uint64_t who = __builtin_amdgcn_ballot_w64(hit);
@@ -285,9 +298,9 @@ struct SelectSharedT {
   uint32_t sure[kMaxN / 32];
   uint32_t eq[kMaxN / 32];
   uint32_t pre[kMaxN / 32];  // per-word prefixes of sure / eq (bitmap_prefixes)
-  uint32_t wave[2 * 8];
+  uint32_t wave[2 * 16];
   uint32_t sel[2];
-  uint32_t small[kWave];
+  alignas(16) uint32_t small[kWave];
   uint32_t nsmall;
 };
 using SelectShared = SelectSharedT<kSpMaxN>;
@@ -308,38 +321,39 @@ struct RegCandidates {
   }
 };
 
-// Exact selection of the k largest among the candidates (at least k of them,
-// positions < n <= Sh::kMaxPositions), by a workgroup of kThreads threads.  Returns the
-// threshold D value and need_eq; on return the bitmaps and their prefixes are
-// complete (the workgroup is synchronised), so that
-//   winner_slot(sh.sure, sh.eq, sh.pre, p, d > thr, need_eq)
-// gives the output slot of every candidate (d, p) with d >= thr.
+// Threshold of the k largest among the candidates (at least k of them), by a
+// workgroup of kThreads threads: the D value thr of the k-th largest and the
+// number need_eq of candidates equal to it that are kept (the others equal to
+// it are dropped, the larger positions first).  dmax is an upper bound of
+// every D when known (known_dmax), else the rounds find the largest D first.
+// Ends with the workgroup synchronised on LDS.
 template <int kThreads, class Cand, class Sh>
-__device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh& sh,
-                                             uint32_t& thr, uint32_t& need_eq) {
+__device__ __forceinline__ void block_threshold(const Cand& cand, int k, Sh& sh, bool known_dmax,
+                                                uint32_t dmax, uint32_t& thr,
+                                                uint32_t& need_eq) {
   constexpr int kWaves = kThreads / kWave;
-  static_assert(kThreads % kWave == 0 && kWaves <= 8, "up to 8 waves");
+  static_assert(kThreads % kWave == 0 && kWaves <= 16, "up to 16 waves");
   const int tid = threadIdx.x;
-  const int nwords = (n + 31) >> 5;
   for (int i = tid; i < kHistWords; i += kThreads) {
     sh.hist[i] = 0;
     sh.hist2[i] = 0;
-  }
-  for (int i = tid; i < nwords; i += kThreads) {
-    sh.sure[i] = 0;
-    sh.eq[i] = 0;
   }
   if (tid == 0) sh.nsmall = 0;
   // The rounds work on D, whose range is known from the largest one, so the
   // first digit spreads the keys over the histogram instead of piling them
   // into the few top-bit bins they share.
-  uint32_t mx = 0;
-  cand.each([&](uint32_t d, uint32_t) { mx = max(mx, d); });
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) sh.wave[tid >> 6] = mx;
+  uint32_t mx = dmax;
+  if (!known_dmax) {
+    mx = 0;
+    cand.each([&](uint32_t d, uint32_t) { mx = max(mx, d); });
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) sh.wave[tid >> 6] = mx;
+  }
   lds_barrier();  // also orders the clearing above before the rounds
+  if (!known_dmax) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) mx = max(mx, sh.wave[w]);
+    for (int w = 0; w < kWaves; ++w) mx = max(mx, sh.wave[w]);
+  }
   const int bits = 32 - __clz((int)mx);      // D < 2^bits
   const int s1 = bits > 11 ? bits - 11 : 0;  // round 1: D >> s1 (< 2048)
   const int s2 = s1 > 11 ? s1 - 11 : 0;      // round 2: bits s2.. of D
@@ -391,6 +405,111 @@ __device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh&
       need_eq = remaining;
     }
   }
+}
+
+// The same threshold with 12-bit digits and a block-parallel bin search, for
+// candidate sets whose largest D is known (dmax): a first digit of 4096 bins
+// usually leaves at most 64 keys in the threshold's bin, which one wave then
+// ranks directly, so one histogram round and one rank suffice.  Each round:
+// the bins are cleared, the matching keys counted (LDS atomics), every thread
+// sums its kThreads-th share of the bins (top bins first), and one block scan
+// of those sums finds the thread whose bins hold the k-th largest; that thread
+// finds the bin.  h12 is 4096 words of LDS.  Ends synchronised on LDS.
+constexpr int kBins12 = 4096;
+
+template <int kThreads, class Cand, class Sh>
+__device__ __forceinline__ void block_threshold12(const Cand& cand, int k, Sh& sh, uint32_t* h12,
+                                                  uint32_t dmax, uint32_t& thr,
+                                                  uint32_t& need_eq) {
+  constexpr int kWaves = kThreads / kWave;
+  constexpr int kPer = kBins12 / kThreads;  // bins per thread
+  static_assert(kPer % 4 == 0 && kWaves <= 16, "16-byte bin reads, up to 16 waves");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) sh.nsmall = 0;
+  uint32_t pre = 0, remaining = (uint32_t)k;
+  int shift = 32 - __clz((int)dmax);  // every D < 2^shift
+#pragma unroll 1
+  for (;;) {
+    const int s_new = shift > 12 ? shift - 12 : 0;
+    uint4* h4 = reinterpret_cast<uint4*>(h12);
+    for (int i = tid; i < kBins12 / 4; i += kThreads) h4[i] = uint4{0u, 0u, 0u, 0u};
+    lds_barrier();
+    const uint32_t p0 = pre, sh0 = (uint32_t)shift, sn = (uint32_t)s_new;
+    cand.each([&](uint32_t d, uint32_t) {
+      if (sh0 >= 32 || (d >> sh0) == p0) atomicAdd(&h12[(d >> sn) & (kBins12 - 1)], 1u);
+    });
+    lds_barrier();
+    // Thread t owns bins [4096 - kPer (t + 1), 4096 - kPer t): the top bins first.
+    const int lo = kBins12 - kPer * (tid + 1);
+    uint32_t c[kPer], sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const uint4 v = h4[lo / 4 + q];
+      c[4 * q] = v.x, c[4 * q + 1] = v.y, c[4 * q + 2] = v.z, c[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sum += c[j];
+    const uint32_t wincl = wave_incl_scan(sum);
+    if (lane == 63) sh.wave[wave] = wincl;
+    lds_barrier();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) before += w < wave ? sh.wave[w] : 0u;
+    const uint32_t incl = before + wincl, excl = incl - sum;
+    if (excl < remaining && remaining <= incl) {
+      uint32_t above = excl;
+#pragma unroll
+      for (int j = kPer - 1; j >= 0; --j) {
+        if (above < remaining && remaining <= above + c[j]) {
+          sh.sel[0] = (uint32_t)(lo + j);
+          sh.sel[1] = remaining - above;
+          sh.small[0] = c[j];  // keys in the bin; read before the gather below
+        }
+        above += c[j];
+      }
+    }
+    lds_barrier();
+    const uint32_t digit = sh.sel[0], m = sh.small[0];
+    remaining = sh.sel[1];
+    pre = (shift >= 32 ? 0u : (pre << (shift - s_new))) | digit;
+    shift = s_new;
+    if (shift == 0) {
+      thr = pre;
+      need_eq = remaining;
+      return;
+    }
+    if (m <= (uint32_t)kWave) {
+      lds_barrier();  // every thread has read sel and small[0]
+      const uint32_t p1 = pre, s1 = (uint32_t)shift;
+      cand.each([&](uint32_t d, uint32_t) {
+        if ((d >> s1) == p1) sh.small[atomicAdd(&sh.nsmall, 1u)] = d;
+      });
+      lds_barrier();
+      if (tid < kWave) rank_small(sh.small, m, remaining, sh.sel);
+      lds_barrier();
+      thr = sh.sel[0];
+      need_eq = sh.sel[1];
+      return;
+    }
+  }
+}
+
+// Exact selection of the k largest among the candidates (at least k of them,
+// positions < n <= Sh::kMaxPositions), by a workgroup of kThreads threads.  Returns the
+// threshold D value and need_eq; on return the bitmaps and their prefixes are
+// complete (the workgroup is synchronised), so that
+//   winner_slot(sh.sure, sh.eq, sh.pre, p, d > thr, need_eq)
+// gives the output slot of every candidate (d, p) with d >= thr.
+template <int kThreads, class Cand, class Sh>
+__device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh& sh,
+                                             uint32_t& thr, uint32_t& need_eq) {
+  const int tid = threadIdx.x;
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kThreads) {
+    sh.sure[i] = 0;
+    sh.eq[i] = 0;
+  }
+  block_threshold<kThreads>(cand, k, sh, false, 0u, thr, need_eq);
   const uint32_t t = thr;
   cand.each([&](uint32_t d, uint32_t p) {
     if (d > t) atomicOr(&sh.sure[p >> 5], 1u << (p & 31));

@@ -10,22 +10,31 @@
 // in ascending position order, so ties go to the smaller position and the
 // result is unique.
 //
-// Three ways to run it, chosen on the host:
-//  * up to 1024 rows: topk_split_kernel spreads each row over workgroups of
-//    4096 positions; they cut the row down to a short list of candidates and
-//    the row's last workgroup finishes the selection (one launch);
-//  * more rows, each of at most 32768 positions: topk_lean_kernel, one
-//    512-thread workgroup per row holding the whole row in registers;
+// Four ways to run it, chosen on the host from the row count and the
+// longest row:
+//  * up to 1024 rows of 4097..131072 positions (decode): topk_cut_kernel
+//    spreads each row over workgroups of 2048 or 8192 positions that cut it
+//    down to position-ordered candidate regions, and topk_pick_kernel, one
+//    workgroup per row, selects among them (two launches);
+//  * other rows when there are at most 1024: topk_split_kernel spreads each
+//    row over workgroups that append their candidates to one list per row,
+//    and topk_finish_kernel selects among them (one launch when a row fits
+//    one workgroup, else two);
+//  * more rows, each of at most 32768 positions (prefill): topk_lean_kernel,
+//    one 512-thread workgroup per row holding the whole row in registers;
 //  * otherwise: full_row_topk, one workgroup per row, chunk by chunk
 //    (topk_row_kernel).
-// The first two build bitmaps of the certain winners and of the ties and read
-// the ordered output off them; full_row_topk (also their fallback when the
-// candidate list misses or overflows) compacts keys held in LDS.  None of them
-// needs the workspace to hold anything in particular beforehand.
+// The candidate paths fall back to full_row_topk for a row whose candidates
+// cannot be trusted (fewer than k of them, or more than the lists hold), so
+// the result is exact whatever the sample says.  Only the split path needs
+// anything in the workspace beforehand: its per-row list counters must be
+// zero when it starts (dsa_forward has the indexer clear them, dsa_topk
+// launches a small clearing kernel).
 #include "dsa_device.h"
 #include "dsa_launch.h"
 #include "select.h"
 
+#include <cstddef>
 #include <type_traits>
 
 namespace dsa {
@@ -292,26 +301,9 @@ __device__ __noinline__ void full_row_topk(const float* __restrict__ x, int n, i
 }
 
 // ---------------------------------------------------------------------------
-// Candidate path.  A row is cut into blocks of kBlk positions processed by
-// separate workgroups:
-//   topk_hist_kernel  counts the top 11 key bits of each block into the row's
-//                     histogram (LDS, then one global atomic per non-empty bin);
-//   topk_cand_kernel  reads the histogram, takes the lower edge L of the bin
-//                     holding the k-th largest key, and writes the (key,
-//                     position) of every element >= L of its block, in
-//                     position order, to the block's slot (or marks overflow);
-//   topk_kernel       concatenates the slots (ascending positions), checks that
-//                     they hold every element >= L and at least k of them, and
-//                     then selects exactly among them.  Otherwise it falls back
-//                     to full_row_topk.  It leaves the row's histogram zeroed.
-// The histogram only chooses L: whatever it contains, the selection is exact
-// (a candidate set holding every element >= L with at least k elements
-// contains the top k).  A zero-filled workspace gets the fast path at once.
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// Up to 1024 rows: each row is spread over workgroups of 512 * kSpPer
-// positions (topk_split_kernel), and a second launch with one workgroup per
-// row finishes it (topk_finish_kernel).
+// Up to 1024 rows of at most 4096 (or more than 131072) positions: each row
+// is spread over workgroups of 512 * kSpPer positions (topk_split_kernel), and
+// a second launch with one workgroup per row finishes it (topk_finish_kernel).
 //   1. Every workgroup derives the same cut L from the same 2048 sampled
 //      positions of the row, 128 evenly spaced runs of 16 consecutive ones
 //      (run g starts at floor(g (n - 16) / 127); one 64-byte segment per run,
@@ -337,15 +329,6 @@ constexpr int kSpSample = 2048;                       // sampled positions per r
 constexpr int kSpSamplePer = kSpSample / kTkThreads;  // 4 per thread
 constexpr int kSpListPer = kSpCap / kTkThreads;       // 16 per thread
 
-size_t topk_workspace_bytes(int B, int T, int, int) {
-  const size_t rows = (size_t)B * T;
-  if (rows > (size_t)kMultiRows) return 0;
-  return align256(rows * kCtrWords * 4) + rows * kSpCap * 8;
-}
-
-uint32_t* topk_counters(void* workspace, int B, int T) {
-  return B * T > kMultiRows ? nullptr : reinterpret_cast<uint32_t*>(workspace);
-}
 
 union SplitLds {
   TopkShared full;
@@ -535,6 +518,323 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
                ws.list + (size_t)row * kSpCap, ws.ctr[kCtrWords * row + 2], lds);
 }
 
+// Candidates held in registers as entries tid + kThreads u with a validity
+// bit each.  (The loops over u are fully unrolled and predicated: a loop exit
+// on a run-time bound would leave the arrays indexed at run time, which puts
+// them in scratch memory.)
+template <int kThreads, int kEnt>
+struct MaskedCandidates {
+  uint32_t d[kEnt], p[kEnt];
+  uint32_t valid;  // bit u: entry u is a candidate
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u)
+      if ((valid >> u) & 1u) f(d[u], p[u]);
+  }
+};
+
+// Writes every candidate with d > thr, and the first need_eq with d == thr,
+// at its slot in ascending staging order (which is position order).  Entry
+// tid + kThreads u of the order is held by thread tid as entry u.
+template <int kEnt, class Cand, int kRows>
+__device__ __forceinline__ void ordered_output(const Cand& cand, uint32_t thr, uint32_t need_eq,
+                                               int k, int32_t* __restrict__ o,
+                                               uint32_t (&tab)[2][kRows][kTkWaves]) {
+  static_assert(kEnt <= kRows, "a table row per entry block");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The ballots are taken twice (counts first, ranks after the scan) rather
+  // than kept: 32 masks would not fit the scalar registers.
+  auto sure = [&](int u) { return ((cand.valid >> u) & 1u) && cand.d[u] > thr; };
+  auto tie = [&](int u) { return ((cand.valid >> u) & 1u) && cand.d[u] == thr; };
+#pragma unroll
+  for (int u = 0; u < kRows; ++u) {
+    const uint32_t cs = u < kEnt ? (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(sure(u))) : 0u;
+    const uint32_t ce = u < kEnt ? (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(tie(u))) : 0u;
+    if (lane == 0) {
+      tab[0][u][wave] = cs;
+      tab[1][u][wave] = ce;
+    }
+  }
+  lds_barrier();
+  if (wave == 0) {
+    // Exclusive scan of the (block, wave) counts in staging order: lane l
+    // holds entries 2l and 2l + 1 of each table (rows past kEnt: never read).
+    constexpr int kN = kRows * kTkWaves;  // 128
+    static_assert(kN == 2 * kWave, "two table entries per lane");
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint32_t* flat = &tab[t][0][0];
+      const uint32_t a0 = flat[2 * lane], a1 = flat[2 * lane + 1];
+      const uint32_t incl = wave_incl_scan(a0 + a1);
+      flat[2 * lane] = incl - a0 - a1;
+      flat[2 * lane + 1] = incl - a1;
+    }
+  }
+  lds_barrier();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < kEnt; ++u) {
+    const bool is_s = sure(u), is_e = tie(u);
+    const uint64_t ms = __builtin_amdgcn_ballot_w64(is_s);
+    const uint64_t me = __builtin_amdgcn_ballot_w64(is_e);
+    const uint32_t sb = tab[0][u][wave] + (uint32_t)__popcll(ms & below);
+    const uint32_t eb = tab[1][u][wave] + (uint32_t)__popcll(me & below);
+    if (is_s) {
+      const uint32_t slot = sb + min(eb, need_eq);
+      if (slot < (uint32_t)k) o[slot] = (int32_t)cand.p[u];
+    } else if (is_e && eb < need_eq && sb + eb < (uint32_t)k) {
+      o[sb + eb] = (int32_t)cand.p[u];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode rows (up to 1024 rows of at most 131072 positions), two launches.
+//   topk_cut_kernel: a row is spread over workgroups of 512 * kPer positions
+//     (2048 for rows up to 32768, 8192 for longer ones; wave w of a workgroup
+//     owns its 64 * kPer consecutive positions, so every load instruction
+//     reads 256 contiguous bytes).  Every workgroup derives the same cut L
+//     from the row's 2048-position sample (as the split top-k) and writes its
+//     keys >= L with their positions to its own region of the row's list, in
+//     position order (waves in order, a wave's entries by ballot rank), and a
+//     header (count, largest key, L).  No atomics, nothing to clear.
+//   topk_pick_kernel: one workgroup per row copies the regions into LDS (their
+//     concatenation is in position order), takes them into registers (entry
+//     tid + 512 u of the list is thread tid's entry u: 8 per thread for rows
+//     up to 32768, 16 for longer ones), finds the threshold among them
+//     (block_threshold12: 12-bit histogram rounds over the keys' offsets from
+//     L, the largest offset taken from the headers) and writes each winner at
+//     its slot, the number of winners before it in the list (ordered_output:
+//     ballot counts per wave and per register entry, one scan over them).
+// When the list misses (fewer than k keys, a region over its capacity, more
+// entries than the pick holds, or a row longer than promised) the pick
+// workgroup selects the row from scratch (full_row_topk), which is exact
+// whatever the sample said.
+constexpr int kCutCap = 2048;                    // list entries per region
+constexpr int kCutMaxRegions = 16;
+constexpr int kPickCap = 8192;                   // entries the pick workgroup selects over
+constexpr int kPickEnt = kPickCap / kTkThreads;  // per thread
+constexpr int kCutShortPer = 4;                  // positions per thread, rows <= 32768
+constexpr int kCutLongPer = 16;                  // rows <= 131072
+constexpr int kCutMaxN = kCutMaxRegions * kTkThreads * kCutLongPer;
+
+struct CutHdr {
+  uint32_t count, maxkey, L, pad;
+};
+struct CutWs {
+  CutHdr* hdr;  // [rows][kCutMaxRegions]
+  uint2* list;  // [rows][kCutMaxRegions][kCutCap]: (key, position)
+  int n_reg;    // regions (workgroups) per row
+};
+
+__host__ inline int cut_per_thread(int max_end_pos) {
+  return max_end_pos <= kCutMaxRegions * kTkThreads * kCutShortPer ? kCutShortPer : kCutLongPer;
+}
+__host__ inline bool cut_path(int rows, int max_end_pos) {
+  return rows <= kMultiRows && max_end_pos > kSplitThreads * kSpPerShort && max_end_pos <= kCutMaxN;
+}
+__host__ inline size_t cut_ws_bytes(int rows) {
+  return align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)) +
+         (size_t)rows * kCutMaxRegions * kCutCap * sizeof(uint2);
+}
+__host__ inline CutWs carve_cut_ws(void* ws, int rows, int max_end_pos) {
+  CutWs w;
+  char* p = reinterpret_cast<char*>(ws);
+  w.hdr = reinterpret_cast<CutHdr*>(p);
+  w.list = reinterpret_cast<uint2*>(p + align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)));
+  const int blk = kTkThreads * cut_per_thread(max_end_pos);
+  w.n_reg = (max_end_pos + blk - 1) / blk;
+  return w;
+}
+
+template <int kPer>
+__global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __restrict__ scores,
+                                                              const int32_t* __restrict__ end_pos,
+                                                              int T, int S_max, int k,
+                                                              int32_t* __restrict__ out, CutWs ws) {
+  constexpr int kBlk = kTkThreads * kPer;
+  __shared__ uint32_t s_hist[kHistWords];
+  __shared__ uint32_t s_hist2[kHistWords];
+  __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_cnt[kTkWaves], s_mx[kTkWaves];
+  const int row = blockIdx.x / ws.n_reg, blk = blockIdx.x - row * ws.n_reg;
+  const int n = row_len(end_pos, row, T, S_max);
+  const float* x = scores + (size_t)row * S_max;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (n <= k) {  // every valid position is kept
+    if (blk == 0) {
+      int32_t* o = out + (size_t)row * k;
+      for (int i = tid; i < k; i += kTkThreads) o[i] = i < n ? i : -1;
+    }
+    return;
+  }
+  if (n > ws.n_reg * kBlk) return;  // longer than max_end_pos promised: the pick launch selects it
+  const int base = blk * kBlk;
+  if (base >= n) return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wbase = base + wave * kWave * kPer;  // this wave's first position
+
+  uint32_t kv[kPer], ks[kSpSamplePer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) kv[u] = __float_as_uint(x[min(wbase + kWave * u + lane, n - 1)]);
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u) {
+    const int s = tid + kTkThreads * u;  // sample s: run s / 16, position s % 16 in it
+    const int pos = n >= kSpSample
+                        ? (int)(((uint64_t)(s >> 4) * (uint64_t)(n - 16)) / (kSpSample / 16 - 1)) + (s & 15)
+                        : (int)(((uint64_t)s * (uint64_t)n) / (uint64_t)kSpSample);
+    ks[u] = __float_as_uint(x[pos]);
+  }
+  for (int i = tid; i < kHistWords; i += kTkThreads) {
+    s_hist[i] = 0;
+    s_hist2[i] = 0;
+  }
+  lds_barrier();
+
+  // The cut L: the 22-bit key prefix of the sample's T_s-th largest key.
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u) {
+    ks[u] = score_key(__uint_as_float(ks[u]));
+    atomicAdd(&s_hist[hpad(ks[u] >> 21)], 1u);
+  }
+  const float mean = (float)k * (float)kSpSample / (float)n;
+  uint32_t rem = min((uint32_t)kSpSample, (uint32_t)(mean + 4.0f * sqrtf(mean) + 16.0f));
+  const uint32_t c0 = sel_select_bin(s_hist, kBins, rem, s_sel);
+#pragma unroll
+  for (int u = 0; u < kSpSamplePer; ++u)
+    if ((ks[u] >> 21) == c0) atomicAdd(&s_hist2[hpad((ks[u] >> 10) & (kBins - 1))], 1u);
+  const uint32_t c1 = sel_select_bin(s_hist2, kBins, rem, s_sel);
+  const uint32_t L = (c0 << 21) | (c1 << 10);
+
+  // Keys >= L: this wave's count and largest key, then the workgroup's.
+  uint64_t mk[kPer];
+  uint32_t cnt = 0, mx = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    kv[u] = score_key(__uint_as_float(kv[u]));
+    const bool ge = wbase + kWave * u + lane < n && kv[u] >= L;
+    mk[u] = __builtin_amdgcn_ballot_w64(ge);
+    cnt += (uint32_t)__popcll(mk[u]);
+    mx = max(mx, ge ? kv[u] : 0u);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) {
+    s_cnt[wave] = cnt;
+    s_mx[wave] = mx;
+  }
+  lds_barrier();
+  uint32_t at = 0, total = 0, maxkey = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint32_t c = s_cnt[w];
+    at += w < wave ? c : 0u;
+    total += c;
+    maxkey = max(maxkey, s_mx[w]);
+  }
+  if (total <= (uint32_t)kCutCap) {
+    uint2* reg = ws.list + ((size_t)row * kCutMaxRegions + blk) * kCutCap;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint64_t m = mk[u];
+      if ((m >> lane) & 1ull) {
+        const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        reg[at + r] = uint2{kv[u], (uint32_t)(wbase + kWave * u + lane)};
+      }
+      at += (uint32_t)__popcll(m);
+    }
+  }
+  if (tid == 0) ws.hdr[(size_t)row * kCutMaxRegions + blk] = CutHdr{total, maxkey, L, 0u};
+}
+
+struct PickShared {
+  alignas(16) uint32_t hist[kHistWords];  // with hist2: the 4096 bins of block_threshold12
+  uint32_t hist2[kHistWords];
+  uint32_t wave[2 * kTkWaves];
+  uint32_t sel[2];
+  alignas(16) uint32_t small[kWave];
+  uint32_t nsmall;
+  uint32_t tab[2][kPickEnt][kTkWaves];  // ordered_output's (block, wave) counts
+  uint2 list[kPickCap];  // the regions' entries, concatenated (position order)
+};
+static_assert(offsetof(PickShared, hist2) == offsetof(PickShared, hist) + sizeof(uint32_t) * kHistWords &&
+                  2 * kHistWords >= kBins12,
+              "hist and hist2 together hold the 4096 bins");
+union PickLds {
+  TopkShared full;
+  PickShared pick;
+};
+
+template <int kPer, int kEnt>
+__global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __restrict__ scores,
+                                                               const int32_t* __restrict__ end_pos,
+                                                               int T, int S_max, int k,
+                                                               int32_t* __restrict__ out, CutWs ws) {
+  constexpr int kBlk = kTkThreads * kPer;
+  constexpr int kSpec = 8;  // entries per thread loaded before the counts are known
+  static_assert(kTkThreads == kCutMaxRegions * 32 && 32 * kSpec <= kCutCap, "32 threads per region");
+  __shared__ __align__(16) PickLds lds;
+  PickShared& sh = lds.pick;
+  const int row = blockIdx.x;
+  const int n = row_len(end_pos, row, T, S_max);
+  if (n <= k) return;  // done by the cut launch
+  const float* x = scores + (size_t)row * S_max;
+  int32_t* o = out + (size_t)row * k;
+  if (n > ws.n_reg * kBlk) {  // longer than max_end_pos promised
+    full_row_topk(x, n, k, o, lds.full);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int nr = (n + kBlk - 1) / kBlk;  // regions holding positions of this row
+  const CutHdr* hdr = ws.hdr + (size_t)row * kCutMaxRegions;
+  const uint2* list = ws.list + (size_t)row * kCutMaxRegions * kCutCap;
+  // Thread (w, r) = (tid / 32, tid % 32) copies entries r + 32 j of region w.
+  // The first kSpec of them are loaded together with the headers.
+  const int w = tid >> 5, r = tid & 31;
+  uint2 e[kSpec];
+#pragma unroll
+  for (int j = 0; j < kSpec; ++j) e[j] = list[(size_t)w * kCutCap + r + 32 * j];
+  uint32_t cnt[kCutMaxRegions], M = 0, maxkey = 0, ok = 1, P = 0, cw = 0;
+  const uint32_t L = hdr[0].L;
+#pragma unroll
+  for (int i = 0; i < kCutMaxRegions; ++i) {
+    const CutHdr h = i < nr ? hdr[i] : CutHdr{0u, 0u, 0u, 0u};
+    cnt[i] = h.count;
+    ok &= h.count <= (uint32_t)kCutCap ? 1u : 0u;
+    P += i < w ? h.count : 0u;
+    cw = i == w ? h.count : cw;
+    M += h.count;
+    maxkey = h.count != 0 ? max(maxkey, h.maxkey) : maxkey;
+  }
+  if (!ok || M < (uint32_t)k || M > (uint32_t)(kEnt * kTkThreads)) {
+    full_row_topk(x, n, k, o, lds.full);
+    return;
+  }
+  // Stage the list in LDS, in position order.
+  if (w < nr) {
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j)
+      if ((uint32_t)(r + 32 * j) < cw) sh.list[P + r + 32 * j] = e[j];
+    for (int j = kSpec; (uint32_t)(r + 32 * j) < cw; ++j)
+      sh.list[P + r + 32 * j] = list[(size_t)w * kCutCap + r + 32 * j];
+  }
+  lds_barrier();
+  MaskedCandidates<kTkThreads, kEnt> cand;
+  cand.valid = 0u;
+#pragma unroll
+  for (int u = 0; u < kEnt; ++u) {
+    const int i = tid + kTkThreads * u;
+    const uint2 v = sh.list[min(i, (int)M - 1)];
+    cand.d[u] = v.x - L;
+    cand.p[u] = v.y;
+    cand.valid |= (i < (int)M ? 1u : 0u) << u;
+  }
+  uint32_t thr, need_eq;
+  block_threshold12<kTkThreads>(cand, k, sh, sh.hist, maxkey - L, thr, need_eq);
+  ordered_output<kEnt>(cand, thr, need_eq, k, o, sh.tab);
+}
+
 __global__ __launch_bounds__(256) void topk_reset_kernel(uint32_t* __restrict__ ctr, int words) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < words) ctr[i] = 0u;
@@ -597,7 +897,7 @@ struct LeanSharedT {
   uint32_t ncw[kTkWaves];
   uint32_t wave[2 * kTkWaves];
   uint32_t sel[2];
-  uint32_t small[kWave];
+  alignas(16) uint32_t small[kWave];
   uint32_t nsmall;
 };
 
@@ -810,12 +1110,44 @@ __global__ __launch_bounds__(kTkThreads, kMaxN > kLeanExactN ? 1 : 4) void topk_
   }
 }
 
+size_t topk_workspace_bytes(int B, int T, int S_max, int) {
+  const size_t rows = (size_t)B * T;
+  if (rows > (size_t)kMultiRows) return 0;
+  const size_t split = align256(rows * kCtrWords * 4) + rows * kSpCap * 8;
+  if (S_max <= kSplitThreads * kSpPerShort) return split;
+  return max(split, cut_ws_bytes((int)rows));
+}
+
+uint32_t* topk_counters(void* workspace, int B, int T, int max_end_pos) {
+  const int rows = B * T;
+  if (rows > kMultiRows || cut_path(rows, max_end_pos)) return nullptr;
+  return reinterpret_cast<uint32_t*>(workspace);
+}
+
 static_assert(kTkThreads * 4 == kBins, "one 16-byte histogram piece per thread");
 
 int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S_max,
                 int max_end_pos, int k, int32_t* out, void* workspace, bool counters_clear,
                 hipStream_t stream) {
   const int rows = B * T;
+  if (cut_path(rows, max_end_pos)) {
+    const CutWs ws = carve_cut_ws(workspace, rows, max_end_pos);
+    const dim3 grid((unsigned)((long)rows * ws.n_reg)), block(kTkThreads);
+    if (cut_per_thread(max_end_pos) == kCutShortPer) {
+      hipLaunchKernelGGL(topk_cut_kernel<kCutShortPer>, grid, block, 0, stream, scores, end_pos, T,
+                         S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL((topk_pick_kernel<kCutShortPer, kPickEnt / 2>), dim3((unsigned)rows), block,
+                         0, stream, scores, end_pos, T, S_max, k, out, ws);
+    } else {
+      hipLaunchKernelGGL(topk_cut_kernel<kCutLongPer>, grid, block, 0, stream, scores, end_pos, T,
+                         S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL((topk_pick_kernel<kCutLongPer, kPickEnt>), dim3((unsigned)rows), block, 0,
+                         stream, scores, end_pos, T, S_max, k, out, ws);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   if (rows <= kMultiRows) {
     const SplitWs ws = carve_split_ws(workspace, rows, max_end_pos);
     if (!counters_clear && ws.n_blk > 1) {  // the lists are only used with several workgroups
