@@ -168,15 +168,15 @@ DSA_EXPORT size_t dsa_forward_workspace_size(int32_t B, int32_t T, int32_t S_max
   return forward_layout(B, T, S_max, k).total;
 }
 
-DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* weights,
-                           const void* k_cache, const float* k_scale, const int32_t* end_pos,
-                           const void* q_nope, const void* q_pe, const void* kv_cache,
-                           const void* pe_cache, int32_t B, int32_t T, int32_t S_max,
-                           int32_t max_end_pos, int32_t k, float index_scale,
-                           float softmax_scale, int32_t dtype, void* out, float* lse,
-                           int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  // Validate everything before the first launch.
+namespace {
+
+// Everything dsa_forward checks before its first launch.
+int check_forward(const void* q, const float* q_scale, const float* weights, const void* k_cache,
+                  const float* k_scale, const int32_t* end_pos, const void* q_nope,
+                  const void* q_pe, const void* kv_cache, const void* pe_cache, int32_t B,
+                  int32_t T, int32_t S_max, int32_t max_end_pos, int32_t k, float softmax_scale,
+                  int32_t dtype, const void* out, const float* lse,
+                  const int32_t* topk_indices_out) {
   int st = check_indexer(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
                          max_end_pos, dtype);
   if (st) return st;
@@ -186,18 +186,24 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   if (k < 1) return kErrInvalid;
   if (k > kMaxTopk) return kErrUnsupported;
   if (topk_indices_out && !aligned4(topk_indices_out)) return kErrMisaligned;
-  const ForwardLayout L = forward_layout(B, T, S_max, k);
-  st = check_workspace(workspace, workspace_bytes, L.total);
-  if (st) return st;
+  return kOk;
+}
 
-  char* ws = reinterpret_cast<char*>(workspace);
+// The three stages on `stream` over a checked workspace.
+int run_forward(const void* q, const float* q_scale, const float* weights, const void* k_cache,
+                const float* k_scale, const int32_t* end_pos, const void* q_nope,
+                const void* q_pe, const void* kv_cache, const void* pe_cache, int32_t B,
+                int32_t T, int32_t S_max, int32_t max_end_pos, int32_t k, float index_scale,
+                float softmax_scale, int32_t dtype, void* out, float* lse,
+                int32_t* topk_indices_out, char* ws, const ForwardLayout& L,
+                hipStream_t stream) {
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   int32_t* indices =
       topk_indices_out ? topk_indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
   // The indexer also clears the top-k's per-row counters (when that path has them).
   uint32_t* topk_ctr = dsa::topk_counters(ws + L.topk_ws, B, T, max_end_pos);
-  st = dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
-                                max_end_pos, index_scale, dtype, scores, topk_ctr, stream);
+  int st = dsa::launch_index_scores(q, q_scale, weights, k_cache, k_scale, end_pos, B, T, S_max,
+                                    max_end_pos, index_scale, dtype, scores, topk_ctr, stream);
   if (st) return st;
   st = dsa::launch_topk(scores, end_pos, B, T, S_max, max_end_pos, k, indices, ws + L.topk_ws,
                         /*counters_clear=*/topk_ctr != nullptr, stream);
@@ -206,6 +212,29 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   // attention skips the rest (whole tiles of -1 for early prefill queries).
   return dsa::launch_sparse_mla(q_nope, q_pe, kv_cache, pe_cache, indices, B, T, S_max, k,
                                 softmax_scale, out, lse, ws + L.mla_ws, stream, end_pos);
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* weights,
+                           const void* k_cache, const float* k_scale, const int32_t* end_pos,
+                           const void* q_nope, const void* q_pe, const void* kv_cache,
+                           const void* pe_cache, int32_t B, int32_t T, int32_t S_max,
+                           int32_t max_end_pos, int32_t k, float index_scale,
+                           float softmax_scale, int32_t dtype, void* out, float* lse,
+                           int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  // Validate everything before the first launch.
+  int st = check_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                         pe_cache, B, T, S_max, max_end_pos, k, softmax_scale, dtype, out, lse,
+                         topk_indices_out);
+  if (st) return st;
+  const ForwardLayout L = forward_layout(B, T, S_max, k);
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st) return st;
+  return run_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                     pe_cache, B, T, S_max, max_end_pos, k, index_scale, softmax_scale, dtype,
+                     out, lse, topk_indices_out, reinterpret_cast<char*>(workspace), L, stream);
 }
 
 DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {
