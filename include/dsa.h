@@ -167,6 +167,29 @@ int dsa_forward(const void* q, const float* q_scale, const float* weights, const
                 int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* dsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, which lives instead in a device
+ * array held by the library, DSA_FORWARD_SCRATCH_BYTES on every GPU it runs
+ * on, from the library's load until the process ends.  Returns
+ * DSA_ERR_WORKSPACE_TOO_SMALL, launching nothing, when
+ * dsa_forward_workspace_size(B, T, S_max, k) exceeds that (96 MiB holds batch
+ * 64 at 131072 positions, or one 4096-query prefill); the other errors are
+ * dsa_forward's.  The call makes no allocation of any kind.  The current
+ * device must be the one `stream` runs on; the array's address on it is
+ * looked up on the first call there (DSA_ERR_HIP if that fails).  Every call
+ * on one GPU uses the same array and nothing in it needs clearing: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller. */
+#define DSA_FORWARD_SCRATCH_BYTES ((size_t)96 << 20)
+int dsa_forward_noalloc(const void* q, const float* q_scale, const float* weights,
+                        const void* k_cache, const float* k_scale, const int32_t* end_pos,
+                        const void* q_nope, const void* q_pe, const void* kv_cache,
+                        const void* pe_cache, int32_t B, int32_t T, int32_t S_max,
+                        int32_t max_end_pos, int32_t k, float index_scale, float softmax_scale,
+                        int32_t dtype, void* out, float* lse, int32_t* topk_indices_out,
+                        hipStream_t stream);
+
 /* Dense baseline: (c) over every causally valid position 0..bound, no index
  * list (the unmasked form of the same decode branch).  Same tensors and
  * arithmetic as dsa_sparse_mla.  Used to measure where sparse wins. */

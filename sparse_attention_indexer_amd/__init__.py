@@ -11,6 +11,7 @@ Stages (same names as the C ABI, without the ``dsa_`` prefix):
   topk          per-query top-k positions (ascending, ties to the smaller position, -1 pad)
   sparse_mla    absorbed MLA (128 heads, 512 latent + 64 rope) over the selected rows
   forward       the three stages on one stream
+  forward_noalloc  the same with the workspace in the library's per-device scratch
   dense_mla     the same attention over every valid position (baseline)
 
 Defaults that matter for capture and latency: without ``max_end_pos`` the
@@ -34,6 +35,7 @@ FP8_E4M3 = 1
 INDEX_HEADS, INDEX_DIM = 64, 128
 MLA_HEADS, LATENT_DIM, ROPE_DIM = 128, 512, 64
 MAX_TOPK = 2048
+SCRATCH_BYTES = 96 << 20  # DSA_FORWARD_SCRATCH_BYTES: dsa_forward_noalloc's per-device workspace
 
 _lib = None
 
@@ -69,6 +71,8 @@ def _bind(L):
         "dsa_forward_workspace_size": ([i32, i32, i32, i32], sz),
         "dsa_forward": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                          f32, i32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "dsa_forward_noalloc": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                 f32, f32, i32, vp, vp, vp, vp], ctypes.c_int),
         "dsa_dense_mla_workspace_size": ([i32, i32, i32], sz),
         "dsa_dense_mla": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp],
                           ctypes.c_int),
@@ -363,6 +367,40 @@ def forward(q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cache, inde
                            float(softmax_scale), FP8_E4M3 if fp8 else BF16, _ptr(out),
                            _ptr(lse), _ptr(topk_out), _ptr(ws), nb, _stream(stream))
     _check(st, "dsa_forward")
+    return out, lse, topk_out
+
+
+def forward_noalloc(q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cache, index_scale,
+                    softmax_scale, k=MAX_TOPK, q_scale=None, k_scale=None, max_end_pos=None,
+                    out=None, lse=None, want_lse=True, topk_out=None, stream=None):
+    """forward() through dsa_forward_noalloc: the workspace is the library's
+    per-device scratch (at most SCRATCH_BYTES), so with ``out`` (and ``lse``)
+    given the call allocates nothing.  Calls that overlap on one GPU race."""
+    fp8 = q.dtype == torch.float8_e4m3fn
+    B, T = q.shape[:2]
+    S_max = k_cache.shape[1]
+    dev = q.device
+    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), (B, T, INDEX_HEADS, INDEX_DIM))
+    _need(weights, "weights", torch.float32, (B, T, INDEX_HEADS), dev)
+    _need(k_cache, "k_cache", q.dtype, (B, S_max, INDEX_DIM), dev)
+    _need(end_pos, "end_pos", torch.int32, (B,), dev)
+    if fp8:
+        _need(q_scale, "q_scale", torch.float32, (B, T, INDEX_HEADS), dev)
+        _need(k_scale, "k_scale", torch.float32, (B, S_max), dev)
+    Bm, Tm, S_kv, _ = _mla_checks(q_nope, q_pe, kv_cache, pe_cache)
+    if (Bm, Tm, S_kv) != (B, T, S_max):
+        raise ValueError("indexer and attention tensors disagree on B, T or S_max")
+    out, lse = _mla_outputs(B, T, dev, out, lse, want_lse)
+    if topk_out is not None:
+        _need(topk_out, "topk_out", torch.int32, (B, T, k), dev)
+    with torch.cuda.device(dev):
+        st = lib().dsa_forward_noalloc(
+            _ptr(q), _ptr(q_scale) if fp8 else None, _ptr(weights), _ptr(k_cache),
+            _ptr(k_scale) if fp8 else None, _ptr(end_pos), _ptr(q_nope), _ptr(q_pe),
+            _ptr(kv_cache), _ptr(pe_cache), B, T, S_max, _max_end_pos(max_end_pos, S_max),
+            int(k), float(index_scale), float(softmax_scale), FP8_E4M3 if fp8 else BF16,
+            _ptr(out), _ptr(lse), _ptr(topk_out), _stream(stream))
+    _check(st, "dsa_forward_noalloc")
     return out, lse, topk_out
 
 

@@ -1,8 +1,13 @@
 // C ABI of libdsa.so (declared in include/dsa.h): argument validation on the
 // host, workspace carving, and kernel launches on the caller's stream.  No
-// allocation, no synchronisation, no global mutable state.
+// allocation and no synchronisation.  The only global state is the device
+// scratch of dsa_forward_noalloc and the table of its per-device addresses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
+
+#include "dsa.h"
 
 #include "dsa_launch.h"
 
@@ -235,6 +240,60 @@ DSA_EXPORT int dsa_forward(const void* q, const float* q_scale, const float* wei
   return run_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
                      pe_cache, B, T, S_max, max_end_pos, k, index_scale, softmax_scale, dtype,
                      out, lse, topk_indices_out, reinterpret_cast<char*>(workspace), L, stream);
+}
+
+// ---- dsa_forward_noalloc: dsa_forward's workspace in a library-held array ----
+// Every GPU the library runs on holds its own copy of `scratch` from module
+// load until the process ends.  In host code the name only stands for the
+// symbol: its device address on the current device comes from
+// hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[DSA_FORWARD_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once known
+
+// The address of the current device's scratch (looked up on its first use).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return kErrHip;
+  if (dev < 0 || dev >= kMaxDevices) return kErrUnsupported;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return kErrHip;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return kOk;
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_forward_noalloc(const void* q, const float* q_scale, const float* weights,
+                                   const void* k_cache, const float* k_scale,
+                                   const int32_t* end_pos, const void* q_nope, const void* q_pe,
+                                   const void* kv_cache, const void* pe_cache, int32_t B,
+                                   int32_t T, int32_t S_max, int32_t max_end_pos, int32_t k,
+                                   float index_scale, float softmax_scale, int32_t dtype,
+                                   void* out, float* lse, int32_t* topk_indices_out,
+                                   hipStream_t stream) {
+  int st = check_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                         pe_cache, B, T, S_max, max_end_pos, k, softmax_scale, dtype, out, lse,
+                         topk_indices_out);
+  if (st) return st;
+  const ForwardLayout L = forward_layout(B, T, S_max, k);
+  if (L.total > DSA_FORWARD_SCRATCH_BYTES) return kErrWorkspace;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  // Nothing in the workspace has to start at any particular value (the
+  // indexer clears the top-k counters that need it), so no clearing here.
+  return run_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                     pe_cache, B, T, S_max, max_end_pos, k, index_scale, softmax_scale, dtype,
+                     out, lse, topk_indices_out, reinterpret_cast<char*>(ws), L, stream);
 }
 
 DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {

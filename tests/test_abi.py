@@ -102,6 +102,27 @@ def test_forward_validation(L):
     assert L.dsa_forward(*bad, P, need, None) == -1
 
 
+def test_forward_noalloc_validation(L):
+    # Same checks as dsa_forward, then the workspace must fit the library's
+    # scratch (96 MiB): refused before any HIP call, so this runs without a GPU.
+    scratch = 96 << 20
+    base = [P, None, P, P, None, P, P, P, P, P, 2, 1, 1000, 1000, 2048, 1.0, 1.0, 0, P, None,
+            None]
+    bad = list(base)
+    bad[14] = 4096
+    assert L.dsa_forward_noalloc(*bad, None) == -2
+    bad = list(base)
+    bad[6] = None
+    assert L.dsa_forward_noalloc(*bad, None) == -1
+    S = 1 << 24  # batch 2 at 2^24 positions: 64 MiB of scores per row alone
+    assert L.dsa_forward_workspace_size(2, 1, S, 2048) > scratch
+    big = list(base)
+    big[12] = big[13] = S
+    assert L.dsa_forward_noalloc(*big, None) == -4
+    # A 4096-query prefill fits exactly.
+    assert L.dsa_forward_workspace_size(1, 4096, 4096, 2048) <= scratch
+
+
 def test_workspace_sizes_monotone(L):
     a = L.dsa_dense_mla_workspace_size(8, 1, 131072)
     b = L.dsa_dense_mla_workspace_size(8, 1, 262144)
