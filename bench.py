@@ -86,7 +86,7 @@ def stage_work(case):
 # between them).
 STAGE_KERNELS = {
     "index_scores": ["indexer_kernel<false>"],
-    "topk": ["topk_cut_kernel<4>", "topk_pick_kernel<4, 8>"],
+    "topk": ["topk_cut_kernel<4>", "topk_pick_kernel<4>"],
     "sparse_mla": ["mla_tile_kernel<false>", "mla_combine_kernel<32, 4>"],
 }
 

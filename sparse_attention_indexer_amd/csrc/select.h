@@ -407,93 +407,6 @@ __device__ __forceinline__ void block_threshold(const Cand& cand, int k, Sh& sh,
   }
 }
 
-// The same threshold with 12-bit digits and a block-parallel bin search, for
-// candidate sets whose largest D is known (dmax): a first digit of 4096 bins
-// usually leaves at most 64 keys in the threshold's bin, which one wave then
-// ranks directly, so one histogram round and one rank suffice.  Each round:
-// the bins are cleared, the matching keys counted (LDS atomics), every thread
-// sums its kThreads-th share of the bins (top bins first), and one block scan
-// of those sums finds the thread whose bins hold the k-th largest; that thread
-// finds the bin.  h12 is 4096 words of LDS.  Ends synchronised on LDS.
-constexpr int kBins12 = 4096;
-
-template <int kThreads, class Cand, class Sh>
-__device__ __forceinline__ void block_threshold12(const Cand& cand, int k, Sh& sh, uint32_t* h12,
-                                                  uint32_t dmax, uint32_t& thr,
-                                                  uint32_t& need_eq) {
-  constexpr int kWaves = kThreads / kWave;
-  constexpr int kPer = kBins12 / kThreads;  // bins per thread
-  static_assert(kPer % 4 == 0 && kWaves <= 16, "16-byte bin reads, up to 16 waves");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) sh.nsmall = 0;
-  uint32_t pre = 0, remaining = (uint32_t)k;
-  int shift = 32 - __clz((int)dmax);  // every D < 2^shift
-#pragma unroll 1
-  for (;;) {
-    const int s_new = shift > 12 ? shift - 12 : 0;
-    uint4* h4 = reinterpret_cast<uint4*>(h12);
-    for (int i = tid; i < kBins12 / 4; i += kThreads) h4[i] = uint4{0u, 0u, 0u, 0u};
-    lds_barrier();
-    const uint32_t p0 = pre, sh0 = (uint32_t)shift, sn = (uint32_t)s_new;
-    cand.each([&](uint32_t d, uint32_t) {
-      if (sh0 >= 32 || (d >> sh0) == p0) atomicAdd(&h12[(d >> sn) & (kBins12 - 1)], 1u);
-    });
-    lds_barrier();
-    // Thread t owns bins [4096 - kPer (t + 1), 4096 - kPer t): the top bins first.
-    const int lo = kBins12 - kPer * (tid + 1);
-    uint32_t c[kPer], sum = 0;
-#pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const uint4 v = h4[lo / 4 + q];
-      c[4 * q] = v.x, c[4 * q + 1] = v.y, c[4 * q + 2] = v.z, c[4 * q + 3] = v.w;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) sum += c[j];
-    const uint32_t wincl = wave_incl_scan(sum);
-    if (lane == 63) sh.wave[wave] = wincl;
-    lds_barrier();
-    uint32_t before = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) before += w < wave ? sh.wave[w] : 0u;
-    const uint32_t incl = before + wincl, excl = incl - sum;
-    if (excl < remaining && remaining <= incl) {
-      uint32_t above = excl;
-#pragma unroll
-      for (int j = kPer - 1; j >= 0; --j) {
-        if (above < remaining && remaining <= above + c[j]) {
-          sh.sel[0] = (uint32_t)(lo + j);
-          sh.sel[1] = remaining - above;
-          sh.small[0] = c[j];  // keys in the bin; read before the gather below
-        }
-        above += c[j];
-      }
-    }
-    lds_barrier();
-    const uint32_t digit = sh.sel[0], m = sh.small[0];
-    remaining = sh.sel[1];
-    pre = (shift >= 32 ? 0u : (pre << (shift - s_new))) | digit;
-    shift = s_new;
-    if (shift == 0) {
-      thr = pre;
-      need_eq = remaining;
-      return;
-    }
-    if (m <= (uint32_t)kWave) {
-      lds_barrier();  // every thread has read sel and small[0]
-      const uint32_t p1 = pre, s1 = (uint32_t)shift;
-      cand.each([&](uint32_t d, uint32_t) {
-        if ((d >> s1) == p1) sh.small[atomicAdd(&sh.nsmall, 1u)] = d;
-      });
-      lds_barrier();
-      if (tid < kWave) rank_small(sh.small, m, remaining, sh.sel);
-      lds_barrier();
-      thr = sh.sel[0];
-      need_eq = sh.sel[1];
-      return;
-    }
-  }
-}
-
 // Exact selection of the k largest among the candidates (at least k of them,
 // positions < n <= Sh::kMaxPositions), by a workgroup of kThreads threads.  Returns the
 // threshold D value and need_eq; on return the bitmaps and their prefixes are

@@ -12,10 +12,10 @@
 //
 // Four ways to run it, chosen on the host from the row count and the
 // longest row:
-//  * up to 1024 rows of 4097..131072 positions (decode): topk_cut_kernel
-//    spreads each row over workgroups of 2048 or 8192 positions that cut it
-//    down to position-ordered candidate regions, and topk_pick_kernel, one
-//    workgroup per row, selects among them (two launches);
+//  * up to 1024 rows of 4097..32768 positions (decode): topk_cut_kernel
+//    spreads each row over workgroups of 2048 positions that cut it down to
+//    position-ordered candidate regions, and topk_pick_kernel, one workgroup
+//    per row, selects among them (two launches);
 //  * other rows when there are at most 1024: topk_split_kernel spreads each
 //    row over workgroups that append their candidates to one list per row,
 //    and topk_finish_kernel selects among them (one launch when a row fits
@@ -518,109 +518,34 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
                ws.list + (size_t)row * kSpCap, ws.ctr[kCtrWords * row + 2], lds);
 }
 
-// Candidates held in registers as entries tid + kThreads u with a validity
-// bit each.  (The loops over u are fully unrolled and predicated: a loop exit
-// on a run-time bound would leave the arrays indexed at run time, which puts
-// them in scratch memory.)
-template <int kThreads, int kEnt>
-struct MaskedCandidates {
-  uint32_t d[kEnt], p[kEnt];
-  uint32_t valid;  // bit u: entry u is a candidate
-  template <class F>
-  __device__ __forceinline__ void each(F&& f) const {
-#pragma unroll
-    for (int u = 0; u < kEnt; ++u)
-      if ((valid >> u) & 1u) f(d[u], p[u]);
-  }
-};
-
-// Writes every candidate with d > thr, and the first need_eq with d == thr,
-// at its slot in ascending staging order (which is position order).  Entry
-// tid + kThreads u of the order is held by thread tid as entry u.
-template <int kEnt, class Cand, int kRows>
-__device__ __forceinline__ void ordered_output(const Cand& cand, uint32_t thr, uint32_t need_eq,
-                                               int k, int32_t* __restrict__ o,
-                                               uint32_t (&tab)[2][kRows][kTkWaves]) {
-  static_assert(kEnt <= kRows, "a table row per entry block");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // The ballots are taken twice (counts first, ranks after the scan) rather
-  // than kept: 32 masks would not fit the scalar registers.
-  auto sure = [&](int u) { return ((cand.valid >> u) & 1u) && cand.d[u] > thr; };
-  auto tie = [&](int u) { return ((cand.valid >> u) & 1u) && cand.d[u] == thr; };
-#pragma unroll
-  for (int u = 0; u < kRows; ++u) {
-    const uint32_t cs = u < kEnt ? (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(sure(u))) : 0u;
-    const uint32_t ce = u < kEnt ? (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(tie(u))) : 0u;
-    if (lane == 0) {
-      tab[0][u][wave] = cs;
-      tab[1][u][wave] = ce;
-    }
-  }
-  lds_barrier();
-  if (wave == 0) {
-    // Exclusive scan of the (block, wave) counts in staging order: lane l
-    // holds entries 2l and 2l + 1 of each table (rows past kEnt: never read).
-    constexpr int kN = kRows * kTkWaves;  // 128
-    static_assert(kN == 2 * kWave, "two table entries per lane");
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t* flat = &tab[t][0][0];
-      const uint32_t a0 = flat[2 * lane], a1 = flat[2 * lane + 1];
-      const uint32_t incl = wave_incl_scan(a0 + a1);
-      flat[2 * lane] = incl - a0 - a1;
-      flat[2 * lane + 1] = incl - a1;
-    }
-  }
-  lds_barrier();
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int u = 0; u < kEnt; ++u) {
-    const bool is_s = sure(u), is_e = tie(u);
-    const uint64_t ms = __builtin_amdgcn_ballot_w64(is_s);
-    const uint64_t me = __builtin_amdgcn_ballot_w64(is_e);
-    const uint32_t sb = tab[0][u][wave] + (uint32_t)__popcll(ms & below);
-    const uint32_t eb = tab[1][u][wave] + (uint32_t)__popcll(me & below);
-    if (is_s) {
-      const uint32_t slot = sb + min(eb, need_eq);
-      if (slot < (uint32_t)k) o[slot] = (int32_t)cand.p[u];
-    } else if (is_e && eb < need_eq && sb + eb < (uint32_t)k) {
-      o[sb + eb] = (int32_t)cand.p[u];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Decode rows (up to 1024 rows of at most 131072 positions), two launches.
-//   topk_cut_kernel: a row is spread over workgroups of 512 * kPer positions
-//     (2048 for rows up to 32768, 8192 for longer ones; wave w of a workgroup
-//     owns its 64 * kPer consecutive positions, so every load instruction
-//     reads 256 contiguous bytes).  Every workgroup derives the same cut L
+// Decode rows (up to 1024 rows of 4097..32768 positions), two launches.
+//   topk_cut_kernel: a row is spread over workgroups of 512 * kPer = 2048
+//     positions (wave w of a workgroup owns its 64 * kPer consecutive
+//     positions, so every load instruction reads 256 contiguous bytes).  Every workgroup derives the same cut L
 //     from the row's 2048-position sample (as the split top-k) and writes its
 //     keys >= L with their positions to its own region of the row's list, in
 //     position order (waves in order, a wave's entries by ballot rank), and a
-//     header (count, largest key, L).  No atomics, nothing to clear.
-//   topk_pick_kernel: one workgroup per row copies the regions into LDS (their
-//     concatenation is in position order), takes them into registers (entry
-//     tid + 512 u of the list is thread tid's entry u: 8 per thread for rows
-//     up to 32768, 16 for longer ones), finds the threshold among them
-//     (block_threshold12: 12-bit histogram rounds over the keys' offsets from
-//     L, the largest offset taken from the headers) and writes each winner at
-//     its slot, the number of winners before it in the list (ordered_output:
-//     ballot counts per wave and per register entry, one scan over them).
+//     header (count, L).  No atomics, nothing to clear.
+//   topk_pick_kernel: one workgroup per row copies the regions into LDS,
+//     takes them into registers (entry tid + 512 u of their concatenation is
+//     thread tid's entry u, 8 per thread) and selects among them as the
+//     finishing launch of the split path does (split_select: radix rounds
+//     over key - L, winner and tie bitmaps, each winner's slot from the
+//     bitmaps' prefix counts).
 // When the list misses (fewer than k keys, a region over its capacity, more
 // entries than the pick holds, or a row longer than promised) the pick
 // workgroup selects the row from scratch (full_row_topk), which is exact
 // whatever the sample said.
 constexpr int kCutCap = 2048;                    // list entries per region
 constexpr int kCutMaxRegions = 16;
-constexpr int kPickCap = 8192;                   // entries the pick workgroup selects over
-constexpr int kPickEnt = kPickCap / kTkThreads;  // per thread
-constexpr int kCutShortPer = 4;                  // positions per thread, rows <= 32768
-constexpr int kCutLongPer = 16;                  // rows <= 131072
-constexpr int kCutMaxN = kCutMaxRegions * kTkThreads * kCutLongPer;
+constexpr int kPickCap = 4096;                   // entries the pick workgroup selects over
+constexpr int kPickEnt = kPickCap / kTkThreads;  // per thread (8)
+constexpr int kCutPer = 4;                       // positions per thread of a cut workgroup
+constexpr int kCutMaxN = kCutMaxRegions * kTkThreads * kCutPer;  // 32768
 
 struct CutHdr {
-  uint32_t count, maxkey, L, pad;
+  uint32_t count, L, pad0, pad1;
 };
 struct CutWs {
   CutHdr* hdr;  // [rows][kCutMaxRegions]
@@ -628,9 +553,6 @@ struct CutWs {
   int n_reg;    // regions (workgroups) per row
 };
 
-__host__ inline int cut_per_thread(int max_end_pos) {
-  return max_end_pos <= kCutMaxRegions * kTkThreads * kCutShortPer ? kCutShortPer : kCutLongPer;
-}
 __host__ inline bool cut_path(int rows, int max_end_pos) {
   return rows <= kMultiRows && max_end_pos > kSplitThreads * kSpPerShort && max_end_pos <= kCutMaxN;
 }
@@ -643,7 +565,7 @@ __host__ inline CutWs carve_cut_ws(void* ws, int rows, int max_end_pos) {
   char* p = reinterpret_cast<char*>(ws);
   w.hdr = reinterpret_cast<CutHdr*>(p);
   w.list = reinterpret_cast<uint2*>(p + align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)));
-  const int blk = kTkThreads * cut_per_thread(max_end_pos);
+  const int blk = kTkThreads * kCutPer;
   w.n_reg = (max_end_pos + blk - 1) / blk;
   return w;
 }
@@ -657,7 +579,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __res
   __shared__ uint32_t s_hist[kHistWords];
   __shared__ uint32_t s_hist2[kHistWords];
   __shared__ uint32_t s_sel[2];
-  __shared__ uint32_t s_cnt[kTkWaves], s_mx[kTkWaves];
+  __shared__ uint32_t s_cnt[kTkWaves];
   const int row = blockIdx.x / ws.n_reg, blk = blockIdx.x - row * ws.n_reg;
   const int n = row_len(end_pos, row, T, S_max);
   const float* x = scores + (size_t)row * S_max;
@@ -707,30 +629,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __res
   const uint32_t c1 = sel_select_bin(s_hist2, kBins, rem, s_sel);
   const uint32_t L = (c0 << 21) | (c1 << 10);
 
-  // Keys >= L: this wave's count and largest key, then the workgroup's.
+  // Keys >= L: this wave's count, then the workgroup's.
   uint64_t mk[kPer];
-  uint32_t cnt = 0, mx = 0;
+  uint32_t cnt = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     kv[u] = score_key(__uint_as_float(kv[u]));
     const bool ge = wbase + kWave * u + lane < n && kv[u] >= L;
     mk[u] = __builtin_amdgcn_ballot_w64(ge);
     cnt += (uint32_t)__popcll(mk[u]);
-    mx = max(mx, ge ? kv[u] : 0u);
   }
-  mx = wave_max(mx);
-  if (lane == 0) {
-    s_cnt[wave] = cnt;
-    s_mx[wave] = mx;
-  }
+  if (lane == 0) s_cnt[wave] = cnt;
   lds_barrier();
-  uint32_t at = 0, total = 0, maxkey = 0;
+  uint32_t at = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < kTkWaves; ++w) {
     const uint32_t c = s_cnt[w];
     at += w < wave ? c : 0u;
     total += c;
-    maxkey = max(maxkey, s_mx[w]);
   }
   if (total <= (uint32_t)kCutCap) {
     uint2* reg = ws.list + ((size_t)row * kCutMaxRegions + blk) * kCutCap;
@@ -745,28 +661,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __res
       at += (uint32_t)__popcll(m);
     }
   }
-  if (tid == 0) ws.hdr[(size_t)row * kCutMaxRegions + blk] = CutHdr{total, maxkey, L, 0u};
+  if (tid == 0) ws.hdr[(size_t)row * kCutMaxRegions + blk] = CutHdr{total, L, 0u, 0u};
 }
 
-struct PickShared {
-  alignas(16) uint32_t hist[kHistWords];  // with hist2: the 4096 bins of block_threshold12
-  uint32_t hist2[kHistWords];
-  uint32_t wave[2 * kTkWaves];
-  uint32_t sel[2];
-  alignas(16) uint32_t small[kWave];
-  uint32_t nsmall;
-  uint32_t tab[2][kPickEnt][kTkWaves];  // ordered_output's (block, wave) counts
-  uint2 list[kPickCap];  // the regions' entries, concatenated (position order)
-};
-static_assert(offsetof(PickShared, hist2) == offsetof(PickShared, hist) + sizeof(uint32_t) * kHistWords &&
-                  2 * kHistWords >= kBins12,
-              "hist and hist2 together hold the 4096 bins");
 union PickLds {
-  TopkShared full;
-  PickShared pick;
+  TopkShared full;                 // full_row_topk (the fallback)
+  uint2 list[kPickCap];            // the regions' entries, concatenated (position order)
+  SelectSharedT<kCutMaxN> sel;     // the selection, once the list is in registers
 };
 
-template <int kPer, int kEnt>
+template <int kPer>
 __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ end_pos,
                                                                int T, int S_max, int k,
@@ -775,7 +679,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
   constexpr int kSpec = 8;  // entries per thread loaded before the counts are known
   static_assert(kTkThreads == kCutMaxRegions * 32 && 32 * kSpec <= kCutCap, "32 threads per region");
   __shared__ __align__(16) PickLds lds;
-  PickShared& sh = lds.pick;
   const int row = blockIdx.x;
   const int n = row_len(end_pos, row, T, S_max);
   if (n <= k) return;  // done by the cut launch
@@ -795,19 +698,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
   uint2 e[kSpec];
 #pragma unroll
   for (int j = 0; j < kSpec; ++j) e[j] = list[(size_t)w * kCutCap + r + 32 * j];
-  uint32_t cnt[kCutMaxRegions], M = 0, maxkey = 0, ok = 1, P = 0, cw = 0;
+  uint32_t M = 0, ok = 1, P = 0, cw = 0;
   const uint32_t L = hdr[0].L;
 #pragma unroll
   for (int i = 0; i < kCutMaxRegions; ++i) {
     const CutHdr h = i < nr ? hdr[i] : CutHdr{0u, 0u, 0u, 0u};
-    cnt[i] = h.count;
     ok &= h.count <= (uint32_t)kCutCap ? 1u : 0u;
     P += i < w ? h.count : 0u;
     cw = i == w ? h.count : cw;
     M += h.count;
-    maxkey = h.count != 0 ? max(maxkey, h.maxkey) : maxkey;
   }
-  if (!ok || M < (uint32_t)k || M > (uint32_t)(kEnt * kTkThreads)) {
+  if (!ok || M < (uint32_t)k || M > (uint32_t)kPickCap) {
     full_row_topk(x, n, k, o, lds.full);
     return;
   }
@@ -815,24 +716,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
   if (w < nr) {
 #pragma unroll
     for (int j = 0; j < kSpec; ++j)
-      if ((uint32_t)(r + 32 * j) < cw) sh.list[P + r + 32 * j] = e[j];
+      if ((uint32_t)(r + 32 * j) < cw) lds.list[P + r + 32 * j] = e[j];
     for (int j = kSpec; (uint32_t)(r + 32 * j) < cw; ++j)
-      sh.list[P + r + 32 * j] = list[(size_t)w * kCutCap + r + 32 * j];
+      lds.list[P + r + 32 * j] = list[(size_t)w * kCutCap + r + 32 * j];
   }
   lds_barrier();
-  MaskedCandidates<kTkThreads, kEnt> cand;
-  cand.valid = 0u;
+  uint32_t ek[kPickEnt], ep[kPickEnt];
 #pragma unroll
-  for (int u = 0; u < kEnt; ++u) {
-    const int i = tid + kTkThreads * u;
-    const uint2 v = sh.list[min(i, (int)M - 1)];
-    cand.d[u] = v.x - L;
-    cand.p[u] = v.y;
-    cand.valid |= (i < (int)M ? 1u : 0u) << u;
+  for (int u = 0; u < kPickEnt; ++u) {
+    const uint2 v = lds.list[min(tid + kTkThreads * u, (int)M - 1)];
+    ek[u] = v.x;
+    ep[u] = v.y;
   }
-  uint32_t thr, need_eq;
-  block_threshold12<kTkThreads>(cand, k, sh, sh.hist, maxkey - L, thr, need_eq);
-  ordered_output<kEnt>(cand, thr, need_eq, k, o, sh.tab);
+  lds_barrier();  // the selection's LDS overlaps the staged list
+  split_select<kPickEnt>(ek, ep, (int)M, n, k, o, L, lds.sel);
 }
 
 __global__ __launch_bounds__(256) void topk_reset_kernel(uint32_t* __restrict__ ctr, int words) {
@@ -1133,19 +1030,11 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
   if (cut_path(rows, max_end_pos)) {
     const CutWs ws = carve_cut_ws(workspace, rows, max_end_pos);
     const dim3 grid((unsigned)((long)rows * ws.n_reg)), block(kTkThreads);
-    if (cut_per_thread(max_end_pos) == kCutShortPer) {
-      hipLaunchKernelGGL(topk_cut_kernel<kCutShortPer>, grid, block, 0, stream, scores, end_pos, T,
-                         S_max, k, out, ws);
-      if (hipGetLastError() != hipSuccess) return -5;
-      hipLaunchKernelGGL((topk_pick_kernel<kCutShortPer, kPickEnt / 2>), dim3((unsigned)rows), block,
-                         0, stream, scores, end_pos, T, S_max, k, out, ws);
-    } else {
-      hipLaunchKernelGGL(topk_cut_kernel<kCutLongPer>, grid, block, 0, stream, scores, end_pos, T,
-                         S_max, k, out, ws);
-      if (hipGetLastError() != hipSuccess) return -5;
-      hipLaunchKernelGGL((topk_pick_kernel<kCutLongPer, kPickEnt>), dim3((unsigned)rows), block, 0,
-                         stream, scores, end_pos, T, S_max, k, out, ws);
-    }
+    hipLaunchKernelGGL(topk_cut_kernel<kCutPer>, grid, block, 0, stream, scores, end_pos, T, S_max,
+                       k, out, ws);
+    if (hipGetLastError() != hipSuccess) return -5;
+    hipLaunchKernelGGL(topk_pick_kernel<kCutPer>, dim3((unsigned)rows), block, 0, stream, scores,
+                       end_pos, T, S_max, k, out, ws);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   if (rows <= kMultiRows) {
