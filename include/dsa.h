@@ -30,10 +30,15 @@
  *   to [0, S_max) and never read out of bounds, whatever end_pos holds.
  * - bf16 is bfloat16; fp8 is OCP FP8 E4M3 ("e4m3fn", max 448), the native
  *   fp8 of gfx950.
+ * - A call covers at most 2^24 query rows (B*T) and caches of at most 2^28
+ *   positions (S_max); more give DSA_ERR_UNSUPPORTED, and the
+ *   *_workspace_size functions return 0 for them (as for non-positive
+ *   sizes).
  * - Every call returns DSA_OK (0) or a negative status.  Arguments are
  *   validated on the host before anything is launched; on failure nothing
  *   is enqueued.  DSA_ERR_HIP reports a failed launch (hipGetLastError).
- *   No global mutable state: calls are re-entrant and thread-safe.
+ *   Calls are re-entrant and thread-safe; the one global state is the
+ *   per-device scratch of dsa_forward_noalloc.
  *
  * Sources of the definitions (web pages on DeepSeek-V3.2's sparse
  * attention): the indexer score and its output shape follow kernelpool's

@@ -34,9 +34,19 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool good_softmax_scale(float s) { return s > 0.f && __builtin_isfinite(s); }
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Query rows (B*T) a call may cover, and cache positions per sequence: grids,
+// row indices and position arithmetic (rounding up to whole tiles included)
+// stay well inside 32-bit integers.  2^28 positions of one sequence's latent
+// cache alone would be 309 GB.
+constexpr long kMaxRows = 1L << 24;
+constexpr int32_t kMaxPositions = 1 << 28;
+bool rows_ok(int32_t B, int32_t T) { return B >= 1 && T >= 1 && (long)B * T <= kMaxRows; }
+bool positions_ok(int32_t S_max) { return S_max >= 1 && S_max <= kMaxPositions; }
+
 // Shared checks of the (B, T, S_max, max_end_pos) geometry.
 int check_geometry(int32_t B, int32_t T, int32_t S_max, int32_t max_end_pos) {
   if (B < 1 || T < 1 || S_max < 1) return kErrInvalid;
+  if (!rows_ok(B, T) || !positions_ok(S_max)) return kErrUnsupported;
   if (max_end_pos < T || max_end_pos > S_max) return kErrInvalid;
   return kOk;
 }
@@ -130,7 +140,7 @@ DSA_EXPORT int dsa_index_scores(const void* q, const float* q_scale, const float
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k) {
-  if (B < 1 || T < 1 || S_max < 1 || k < 1) return 0;
+  if (!rows_ok(B, T) || !positions_ok(S_max) || k < 1) return 0;
   return dsa::topk_workspace_bytes(B, T, S_max, k);
 }
 
@@ -146,7 +156,7 @@ DSA_EXPORT int dsa_topk(const float* index_score, const int32_t* end_pos, int32_
 }
 
 DSA_EXPORT size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t T, int32_t k) {
-  if (B < 1 || T < 1 || k < 1) return 0;
+  if (!rows_ok(B, T) || k < 1) return 0;
   return sparse_mla_ws(B, T, k);
 }
 
@@ -159,6 +169,7 @@ DSA_EXPORT int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* 
   if (st) return st;
   if (!topk_indices) return kErrInvalid;
   if (B < 1 || T < 1 || S_max < 1 || k < 1) return kErrInvalid;
+  if (!rows_ok(B, T) || !positions_ok(S_max)) return kErrUnsupported;
   if (!good_softmax_scale(softmax_scale)) return kErrInvalid;
   if (k > kMaxTopk) return kErrUnsupported;
   if (!aligned4(topk_indices)) return kErrMisaligned;
@@ -169,7 +180,7 @@ DSA_EXPORT int dsa_sparse_mla(const void* q_nope, const void* q_pe, const void* 
 }
 
 DSA_EXPORT size_t dsa_forward_workspace_size(int32_t B, int32_t T, int32_t S_max, int32_t k) {
-  if (B < 1 || T < 1 || S_max < 1 || k < 1) return 0;
+  if (!rows_ok(B, T) || !positions_ok(S_max) || k < 1) return 0;
   return forward_layout(B, T, S_max, k).total;
 }
 
@@ -297,7 +308,7 @@ DSA_EXPORT int dsa_forward_noalloc(const void* q, const float* q_scale, const fl
 }
 
 DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {
-  if (B < 1 || T < 1 || S_max < 1) return 0;
+  if (!rows_ok(B, T) || !positions_ok(S_max)) return 0;
   return dsa::mla_workspace_bytes(B, T, dsa::dense_mla_plan(B, T, S_max, S_max));
 }
 
@@ -344,6 +355,7 @@ DSA_EXPORT int dsa_indexer_prep(const void* q_in, const void* k_in, const float*
   if (!q_in || !k_in || !rope_cos || !rope_sin || !end_pos || !q_out || !k_cache)
     return kErrInvalid;
   if (B < 1 || T < 1 || S_max < T || (long)B * T > (1L << 24)) return kErrInvalid;
+  if (!positions_ok(S_max)) return kErrUnsupported;
   if (dtype != 0 && dtype != 1) return kErrUnsupported;
   if (dtype == 1 && (!q_scale || !k_scale)) return kErrInvalid;
   if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(rope_cos) || !aligned16(rope_sin) ||
