@@ -358,7 +358,7 @@ def check_mla_closed_forms(lib):
 
 # --- query absorption and output up-projection -------------------------------
 
-def check_proj_identity(lib):
+def check_proj_identity(lib, mod=oracle):
     """Selector weights: the absorption's first 128 rows per head as the identity
     (q_abs = [q_nope, 0]); the up-projection's rows picking latent dims 256..383."""
     rng = np.random.default_rng(51)
@@ -370,12 +370,12 @@ def check_proj_identity(lib):
     wb = bf16(w)
     qn = bf16(rng.standard_normal((2, 1, H, 128)))
     x = bf16(rng.standard_normal((2, 1, H, 512)))
-    qa = oracle.q_absorb(qn, wb)
+    qa = mod.q_absorb(qn, wb)
     assert np.array_equal(qa[..., :128], bf16_val(qn)) and not qa[..., 128:].any()
-    assert np.array_equal(oracle.out_proj(x, wb), bf16_val(x)[..., 256:384])
+    assert np.array_equal(mod.out_proj(x, wb), bf16_val(x)[..., 256:384])
 
 
-def check_absorbed_equals_mha(lib):
+def check_absorbed_equals_mha(lib, mod=oracle):
     """The decode branch's absorbed form (query absorbed into the latent space,
     attention over the latent cache, output up-projected) against the prefill
     branch's MHA form (keys and values up-projected from the latent first, then
@@ -393,10 +393,10 @@ def check_absorbed_equals_mha(lib):
     kv = bf16(rng.standard_normal((1, n, 512)))
     pe = bf16(rng.standard_normal((1, n, Dr)))
     # Absorbed: oracle.q_absorb -> oracle.mla over all n rows -> oracle.out_proj.
-    qa = oracle.q_absorb(qn, wb)
+    qa = mod.q_absorb(qn, wb)
     assert np.abs(qa).max() <= 256 and np.array_equal(qa, np.round(qa))  # exact in bf16
     x, _ = oracle.mla(bf16(qa), qp, kv, pe, np.array([n], np.int32), scale, lib=lib)
-    y = oracle.out_proj(x, wb)[0, 0]
+    y = mod.out_proj(x, wb)[0, 0]
     # MHA: per-head keys [k_nope, k_pe] and values from the latent rows.
     W = torch.from_numpy(bf16_val(wb))                       # [H, 256, 512]
     C = torch.from_numpy(bf16_val(kv[0]))                    # [n, 512]
@@ -672,4 +672,5 @@ PREP_CHECKS = [
     check_prep_positions, check_prep_relative_position, check_prep_quantised_pipeline,
 ]
 MHA_CHECKS = [check_mha_sdpa, check_mha_closed_forms, check_mha_equals_absorbed]
+PROJ_CHECKS = [check_proj_identity, check_absorbed_equals_mha]
 ALL_CHECKS += PREP_CHECKS + MHA_CHECKS

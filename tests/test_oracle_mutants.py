@@ -74,9 +74,9 @@ def test_mutant_is_caught(name, old, new, tmp_path):
 
 
 # Planted mistakes in the Python part of the oracle (indexer input preparation,
-# MHA-form prefill attention):
+# MHA-form prefill attention, query absorption and output up-projection):
 # (name, text in oracle/__init__.py, replacement).  Each patched copy is loaded as
-# a module of its own and run against the preparation and MHA pins.
+# a module of its own and run against the preparation, MHA and projection pins.
 PY_SRC = os.path.join(pinlib.ROOT, "oracle", "__init__.py")
 PY_MUTANTS = [
     ("rope_sign", "x1 * cos - x2 * sin", "x1 * cos + x2 * sin"),
@@ -103,6 +103,19 @@ PY_MUTANTS = [
     ("mha_lse_without_max", "lse[b, s] = (m + np.log(l))[:, 0]", "lse[b, s] = np.log(l)[:, 0]"),
     ("mha_value_of_wrong_key", 'np.einsum("hn,nhd->hd", p, vf[b, sel])',
      'np.einsum("hn,nhd->hd", p, vf[b, np.roll(sel, 1)])'),
+    # query absorption and output up-projection
+    ("absorb_uses_value_rows", "w = _as_f64(wkv_b)[:, :QK_NOPE, :]",
+     "w = _as_f64(wkv_b)[:, -QK_NOPE:, :]"),
+    ("absorb_wrong_head", 'return np.einsum("bthd,hdc->bthc", q, w)',
+     'return np.einsum("bthd,hdc->bthc", q, np.roll(w, 1, axis=0))'),
+    ("absorb_rows_reversed", 'return np.einsum("bthd,hdc->bthc", q, w)',
+     'return np.einsum("bthd,hdc->bthc", q, w[:, ::-1, :])'),
+    ("outproj_uses_key_rows", "w = _as_f64(wkv_b)[:, -V_HEAD:, :]",
+     "w = _as_f64(wkv_b)[:, :V_HEAD, :]"),
+    ("outproj_wrong_head", 'return np.einsum("bthc,hdc->bthd", xx, w)',
+     'return np.einsum("bthc,hdc->bthd", xx, np.roll(w, 1, axis=0))'),
+    ("outproj_latent_reversed", 'return np.einsum("bthc,hdc->bthd", xx, w)',
+     'return np.einsum("bthc,hdc->bthd", xx[..., ::-1], w)'),
 ]
 
 
@@ -117,9 +130,10 @@ def test_python_mutant_is_caught(name, old, new, tmp_path):
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     failures = []
-    for check in pinlib.PREP_CHECKS + pinlib.MHA_CHECKS:
+    lib = oracle._load()
+    for check in pinlib.PREP_CHECKS + pinlib.MHA_CHECKS + pinlib.PROJ_CHECKS:
         try:
-            check(None, mod=mod)
+            check(lib, mod=mod)
         except (AssertionError, ValueError, IndexError) as e:
             failures.append(check.__name__)
     assert failures, f"mutant {name} passed every pin"
