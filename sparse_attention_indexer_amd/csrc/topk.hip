@@ -312,7 +312,7 @@ __device__ __noinline__ void full_row_topk(const float* __restrict__ x, int n, i
 //      sample's T_s-th largest key, T_s being the sample's expected count of
 //      keys above the k-th largest plus four standard deviations (and 16).
 //   2. It appends its keys >= L with their positions to the row's list in the
-//      workspace (one device-scope atomic per wave reserves the slots).
+//      workspace (one device-scope atomic per workgroup reserves the slots).
 //   3. The finishing workgroup loads the list into registers, runs up to
 //      three radix rounds over it (the last one a direct rank when at most 64
 //      keys are left), marks the keys above the threshold in a winner bitmap
@@ -482,10 +482,21 @@ __global__ __launch_bounds__(kTkThreads, kFallback ? 1 : 4) void topk_split_kern
     ge[u] = base + tid + kTkThreads * u < n && kv[u] >= L;
     cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(ge[u]));
   }
-  uint32_t at = 0;
-  if (lane == 0 && cnt != 0) at = atomicAdd(&ws.ctr[kCtrWords * row + 1], cnt);
-  if (blk == 0 && tid == 0) ws.ctr[kCtrWords * row + 2] = L;
-  at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
+  // One device-scope atomic per workgroup reserves the slots of all its waves.
+  const int wave = tid >> 6;
+  if (lane == 0) sh.wave[wave] = cnt;
+  lds_barrier();
+  if (tid == 0) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) tot += sh.wave[w];
+    sh.wave[kTkWaves] = tot != 0 ? atomicAdd(&ws.ctr[kCtrWords * row + 1], tot) : 0u;
+    if (blk == 0) ws.ctr[kCtrWords * row + 2] = L;
+  }
+  lds_barrier();
+  uint32_t at = sh.wave[kTkWaves];
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) at += w < wave ? sh.wave[w] : 0u;
   uint2* list = ws.list + (size_t)row * kSpCap;
 #pragma unroll
   for (int u = 0; u < kSpPer; ++u) {
