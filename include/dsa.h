@@ -236,7 +236,7 @@ int dsa_out_proj(const void* x, const void* wkv_b, int32_t B, int32_t T, void* y
  *   out    [B,T,128,128] bf16 (fp32 accumulation, round to nearest even)
  *   lse    [B,T,128] fp32 natural-log sum of exp(z) over the kept keys, or NULL
  * A query that keeps no key gets out = 0 and lse = -inf.  The workspace holds
- * the selection as a bitmap (B * ceil(T/32) * roundup(T,64) words).
+ * the selection as a bitmap (B * ceil(T/32) * roundup(T,256) words).
  * Arithmetic: bf16 MFMA with fp32 accumulation, fp32 online softmax, the
  * probabilities enter the value product as bf16.  1 <= B*T <= 2^24;
  * softmax_scale positive and finite. */

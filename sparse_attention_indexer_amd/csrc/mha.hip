@@ -13,15 +13,16 @@
 // Two kernels.
 //   mha_select_bitmap_kernel turns the index lists into a bitmap, bit t of
 //     row s meaning "t is selected for s" (a set, like the excerpt's scatter),
-//     stored key-word-major: word w of queries s0..s0+63 are 256 contiguous
-//     bytes, exactly what the attention kernel copies per key tile.
-//   mha_prefill_kernel: one workgroup per (sequence, head, block of 64
-//     queries), 4 waves of 16 queries.  Rather than gathering each query's
-//     2048 selected positions (64 KiB per position over all heads), it walks
-//     the contiguous key tiles of 32 positions up to the block's causal limit,
-//     so each key and value row is read once per 64 queries, and masks with
-//     the bitmap; a wave skips the MFMAs of a tile none of its queries
-//     selected from.  Tiles come from HBM straight into a 3-slot LDS ring
+//     stored key-word-major: word w of queries s0..s0+255 are 1 KiB of
+//     contiguous bytes, exactly what the attention kernel copies per key tile.
+//   mha_prefill_kernel: one workgroup per (sequence, head, block of 256
+//     queries), 8 waves of 32 queries (two groups of 16).  Rather than
+//     gathering each query's 2048 selected positions (64 KiB per position over
+//     all heads), it walks the contiguous key tiles of 32 positions up to the
+//     block's causal limit, so each key and value row is read once per 256
+//     queries, and masks with the bitmap; every key and value fragment read
+//     from LDS feeds the MFMAs of both query groups of a wave, and a wave
+//     skips a tile none of its queries selected from.  Tiles come from HBM straight into a 3-slot LDS ring
 //     (global_load_lds through inline asm, see mh_copy16); the math is
 //     transposed as in the latent attention kernel: S^T[key][query] =
 //     K . Q^T with the query fragments in registers, the online softmax per
@@ -35,7 +36,7 @@
 //   k_nope 32 rows x 256 B, chunk c of row r at c ^ (r & 15);
 //   k_pe   32 rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7);
 //   v      32 rows x 256 B, chunk c of row r at c ^ ((r & 7) << 1);
-//   bits   64 words: the tile's bitmap word of each query of the block.
+//   bits   256 words: the tile's bitmap word of each query of the block.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -46,23 +47,28 @@ constexpr int kMhDn = 128;                 // non-rotary key / query dims
 constexpr int kMhDr = 64;                  // rotary dims
 constexpr int kMhDq = kMhDn + kMhDr;       // 192
 constexpr int kMhDv = 128;
-constexpr int kMhQb = 64;                  // queries per workgroup
+constexpr int kMhWaves = 8;
+constexpr int kMhQg = 2;                   // 16-query groups per wave
+constexpr int kMhQw = 16 * kMhQg;          // queries per wave (32)
+constexpr int kMhQb = kMhWaves * kMhQw;    // queries per workgroup (256)
 constexpr int kMhKt = 32;                  // keys per tile (one bitmap word)
 constexpr int kMhNbuf = 3;
-constexpr int kMhThreads = 256;
+constexpr int kMhThreads = 256;            // the bitmap kernel
+constexpr int kMhPfThreads = kMhWaves * 64;
 // Byte offsets of the regions inside a slot: k_nope at 0.
 constexpr int kMhOffKp = kMhKt * 256;              // k_pe
 constexpr int kMhOffV = kMhOffKp + kMhKt * 128;    // v
 constexpr int kMhOffBits = kMhOffV + kMhKt * 256;  // bitmap words
 constexpr int kMhSlot = kMhOffBits + kMhQb * 4;
-static_assert(kMhSlot == 20736, "slot layout");
-constexpr int kMhLoads = 6;                // copies per wave per tile
+static_assert(kMhSlot == 21504, "slot layout");
+static_assert(kMhKt == 4 * kMhWaves, "each wave copies 4 rows of a tile");
+constexpr int kMhLoads = 4;                // copies per wave per tile
 constexpr float kMhLog2e = 1.4426950408889634f;
 constexpr float kMhLn2 = 0.6931471805599453f;
 constexpr float kMhSlack = 8.f;
 
 // Bitmap [B][W][Tp] uint32 (W = ceil(T/32) words per query, Tp = T rounded up
-// to 64): bit t%32 of word t/32 of query s is set when t (0 <= t < T) is in
+// to the 256-query block): bit t%32 of word t/32 of query s is set when t (0 <= t < T) is in
 // s's list.  One workgroup per (sequence, 64 queries, 256 words); each thread
 // keeps 16 index loads in flight (16 rows at one column) before its atomics.
 constexpr int kBmQ = 64, kBmW = 256, kBmRows = 16;
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(kMhThreads) void mha_select_bitmap_kernel(
   }
 }
 
-__global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
+__global__ __launch_bounds__(kMhPfThreads) void mha_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_nope,
     const uint16_t* __restrict__ k_pe, const uint16_t* __restrict__ v,
     const uint32_t* __restrict__ bits, int B, int T, int W, int Tp, float scale_log2,
@@ -120,47 +126,51 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int s_me = s0 + 16 * wave + r16;  // this lane's query (may be >= T in the tail)
-
+  // This lane's queries (may be >= T in the tail): group qq holds s_me + 16 qq.
+  const int s_me = s0 + kMhQw * wave + r16;
 
   const uint8_t* kn_h = reinterpret_cast<const uint8_t*>(k_nope) + ((size_t)b * T * kMhHeads + h) * 256;
   const uint8_t* kp_b = reinterpret_cast<const uint8_t*>(k_pe) + (size_t)b * T * 128;
   const uint8_t* v_h = reinterpret_cast<const uint8_t*>(v) + ((size_t)b * T * kMhHeads + h) * 256;
   const uint8_t* bt_b = reinterpret_cast<const uint8_t*>(bits + (size_t)b * W * Tp);
 
-  // This wave's share of tile `kt`: k_nope and v rows 8w + 4i + L/16 (2 copies
-  // each), k_pe rows 8w + L/8 (1 copy), its 16 queries' bitmap words (1 copy
-  // by 4 lanes).  Rows past T read row T-1: no query selects them.
+  // This wave's share of tile `kt`: k_nope, v and k_pe rows 4w .. 4w+3 (one
+  // copy each: 16, 16 and 8 lanes a row) and its 32 queries' bitmap words
+  // (8 lanes).  Rows past T read row T-1: no query selects them.
   auto issue = [&](int kt) {
     uint8_t* base = s_ring + (kt % kMhNbuf) * kMhSlot;
     const int t0 = kt * kMhKt;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * wv + 4 * i + (lane >> 4);
+    {
+      const int r = 4 * wv + (lane >> 4);
       const int t = min(t0 + r, T - 1);
       const int cn = (lane & 15) ^ (r & 15);
       lds_copy16_v(kn_h + (size_t)t * (kMhHeads * 256) + cn * 16,
-                __builtin_amdgcn_readfirstlane(lds_addr(base + (8 * wv + 4 * i) * 256)));
+                   __builtin_amdgcn_readfirstlane(lds_addr(base + 4 * wv * 256)));
       const int cv = (lane & 15) ^ ((r & 7) << 1);
       lds_copy16_v(v_h + (size_t)t * (kMhHeads * 256) + cv * 16,
-                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffV + (8 * wv + 4 * i) * 256)));
+                   __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffV + 4 * wv * 256)));
     }
-    {
-      const int r = 8 * wv + (lane >> 3);
+    if (lane < 32) {
+      const int r = 4 * wv + (lane >> 3);
       const int t = min(t0 + r, T - 1);
       const int cp = (lane & 7) ^ ((r >> 1) & 7);
       lds_copy16_v(kp_b + (size_t)t * 128 + cp * 16,
-                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffKp + 8 * wv * 128)));
+                   __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffKp + 4 * wv * 128)));
     }
-    if (lane < 4)
-      lds_copy16_v(bt_b + ((size_t)kt * Tp + s0 + 16 * wv) * 4 + lane * 16,
-                __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffBits + 64 * wv)));
+    if (lane < 8)
+      lds_copy16_v(bt_b + ((size_t)kt * Tp + s0 + kMhQw * wv) * 4 + lane * 16,
+                   __builtin_amdgcn_readfirstlane(lds_addr(base + kMhOffBits + 4 * kMhQw * wv)));
   };
 
-  float m_run = -INFINITY, l_part = 0.f;
-  f32x4 o[8];  // O^T: dims 16ct + 4g + i of this lane's query
+  float m_run[kMhQg], l_part[kMhQg];
+  f32x4 o[kMhQg][8];  // O^T: dims 16ct + 4g + i of this lane's query of group qq
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qq = 0; qq < kMhQg; ++qq) {
+    m_run[qq] = -INFINITY;
+    l_part[qq] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[qq][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   issue(0);
   if (n_tiles > 1) issue(1);
@@ -168,11 +178,12 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
   // loaded behind the first copies and waited for here, once: the compiler
   // does not see the copies, and a wait it placed at the first use inside the
   // loop would drain every tile's copies.
-  uint4 qf[6];
-  {
-    const uint16_t* qs = q + (((size_t)b * T + min(s_me, T - 1)) * kMhHeads + h) * kMhDq;
+  uint4 qf[kMhQg][6];
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) qf[kk] = ldg16(qs + kk * 32 + g * 8);
+  for (int qq = 0; qq < kMhQg; ++qq) {
+    const uint16_t* qs = q + (((size_t)b * T + min(s_me + 16 * qq, T - 1)) * kMhHeads + h) * kMhDq;
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) qf[qq][kk] = ldg16(qs + kk * 32 + g * 8);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
@@ -188,15 +199,25 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
 
     const uint8_t* buf = s_ring + (kt % kMhNbuf) * kMhSlot;
     const int t0 = kt * kMhKt;
-    // This lane's query's selections in the tile, restricted to t <= s.
-    uint32_t word = reinterpret_cast<const uint32_t*>(buf + kMhOffBits)[16 * wave + r16];
-    const int lim = s_me - t0;  // keys t0 + j with j <= lim are causal for this query
-    word = lim >= 31 ? word : (lim < 0 ? 0u : word & ((2u << lim) - 1u));
-    if (s_me >= T) word = 0u;
-    if (__ballot(word != 0u) == 0) continue;  // no query of this wave looks at this tile
+    // Each query's selections in the tile, restricted to t <= s.
+    uint32_t word[kMhQg];
+    bool any = false;
+#pragma unroll
+    for (int qq = 0; qq < kMhQg; ++qq) {
+      const int s = s_me + 16 * qq;
+      uint32_t w = reinterpret_cast<const uint32_t*>(buf + kMhOffBits)[kMhQw * wave + 16 * qq + r16];
+      const int lim = s - t0;  // keys t0 + j with j <= lim are causal for this query
+      w = lim >= 31 ? w : (lim < 0 ? 0u : w & ((2u << lim) - 1u));
+      word[qq] = s >= T ? 0u : w;
+      any |= word[qq] != 0u;
+    }
+    if (__ballot(any) == 0) continue;  // no query of this wave looks at this tile
 
-    // ---- scores S^T[key][query]: keys 16mt + 4g + i ----
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // ---- scores S^T[key][query]: keys 16mt + 4g + i; each K fragment read
+    //      from LDS feeds both query groups ----
+    f32x4 sc[kMhQg][2];
+#pragma unroll
+    for (int qq = 0; qq < kMhQg; ++qq) sc[qq][0] = sc[qq][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 6; ++kk) {
 #pragma unroll
@@ -205,42 +226,50 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
         const uint8_t* a;
         if (kk < 4) a = buf + r * 256 + (((4 * kk + g) ^ (r & 15)) << 4);
         else a = buf + kMhOffKp + r * 128 + (((4 * (kk - 4) + g) ^ ((r >> 1) & 7)) << 4);
-        sc[mt] = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(a)),
-                                    as_bf16x8(qf[kk]), sc[mt]);
+        const uint4 kf = *reinterpret_cast<const uint4*>(a);
+#pragma unroll
+        for (int qq = 0; qq < kMhQg; ++qq)
+          sc[qq][mt] = mfma_bf16_16x16x32(as_bf16x8(kf), as_bf16x8(qf[qq][kk]), sc[qq][mt]);
       }
     }
-    // ---- online softmax for this lane's query ----
-    float mx = -INFINITY;
+    // ---- online softmax for each of this lane's queries ----
+    uint4 pb[kMhQg];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int qq = 0; qq < kMhQg; ++qq) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool sel = (word >> (16 * mt + 4 * g + i)) & 1u;
-        sc[mt][i] = sel ? sc[mt][i] : -INFINITY;  // raw score, masked
-        mx = fmaxf(mx, sc[mt][i]);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool sel = (word[qq] >> (16 * mt + 4 * g + i)) & 1u;
+          sc[qq][mt][i] = sel ? sc[qq][mt][i] : -INFINITY;  // raw score, masked
+          mx = fmaxf(mx, sc[qq][mt][i]);
+        }
+      mx = group_max(mx) * scale_log2;
+      const bool grow = mx > m_run[qq] + kMhSlack;
+      if (__ballot(grow) != 0) {
+        const float alpha =
+            grow ? (m_run[qq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - mx)) : 1.f;
+        m_run[qq] = grow ? mx : m_run[qq];
+        l_part[qq] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[qq][c] *= alpha;
       }
-    mx = group_max(mx) * scale_log2;
-    const bool grow = mx > m_run + kMhSlack;
-    if (__ballot(grow) != 0) {
-      const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.f;
-      m_run = grow ? mx : m_run;
-      l_part *= alpha;
+      const float m_use = m_run[qq] == -INFINITY ? 0.f : m_run[qq];
+      float p[2][4], psum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] *= alpha;
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[mt][i] = __builtin_amdgcn_exp2f(fmaf(sc[qq][mt][i], scale_log2, -m_use));
+          psum += p[mt][i];
+        }
+      l_part[qq] += psum;
+      pb[qq] = uint4{pack2_bf16(p[0][0], p[0][1]), pack2_bf16(p[0][2], p[0][3]),
+                     pack2_bf16(p[1][0], p[1][1]), pack2_bf16(p[1][2], p[1][3])};
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float p[2][4], psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[mt][i] = __builtin_amdgcn_exp2f(fmaf(sc[mt][i], scale_log2, -m_use));
-        psum += p[mt][i];
-      }
-    l_part += psum;
-    const uint4 pb = uint4{pack2_bf16(p[0][0], p[0][1]), pack2_bf16(p[0][2], p[0][3]),
-                           pack2_bf16(p[1][0], p[1][1]), pack2_bf16(p[1][2], p[1][3])};
-    // ---- values O^T[d][query] += V^T . P: rows {4g + j, 16 + 4g + j} ----
+    // ---- values O^T[d][query] += V^T . P: rows {4g + j, 16 + 4g + j}; each
+    //      V fragment feeds both query groups ----
     const int vr = 4 * g + (r16 >> 2);  // row of this lane's 8-byte read (and vr + 16)
     const uint8_t* vrow = buf + kMhOffV + vr * 256 + 8 * (r16 & 1);
     const int vsw = (vr & 7) << 1, vch = (r16 & 3) >> 1;
@@ -253,22 +282,29 @@ __global__ __launch_bounds__(kMhThreads, 2) void mha_prefill_kernel(
                              (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                              (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
                              (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-      o[ct] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb), o[ct]);
+#pragma unroll
+      for (int qq = 0; qq < kMhQg; ++qq)
+        o[qq][ct] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb[qq]), o[qq][ct]);
     }
   }
 
   // ---- finish ----
-  const float l_tot = group_sum(l_part);
-  if (s_me < T) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = out + (((size_t)b * T + s_me) * kMhHeads + h) * kMhDv + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      *reinterpret_cast<uint2*>(orow + ct * 16) =
-          uint2{pack2_bf16(o[ct][0] * inv, o[ct][1] * inv), pack2_bf16(o[ct][2] * inv, o[ct][3] * inv)};
-    if (lse != nullptr && g == 0)
-      lse[((size_t)b * T + s_me) * kMhHeads + h] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kMhLn2 : -INFINITY;
+  for (int qq = 0; qq < kMhQg; ++qq) {
+    const int s = s_me + 16 * qq;
+    const float l_tot = group_sum(l_part[qq]);
+    if (s < T) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = out + (((size_t)b * T + s) * kMhHeads + h) * kMhDv + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+        *reinterpret_cast<uint2*>(orow + ct * 16) =
+            uint2{pack2_bf16(o[qq][ct][0] * inv, o[qq][ct][1] * inv),
+                  pack2_bf16(o[qq][ct][2] * inv, o[qq][ct][3] * inv)};
+      if (lse != nullptr && g == 0)
+        lse[((size_t)b * T + s) * kMhHeads + h] =
+            l_tot > 0.f ? (m_run[qq] + log2f(l_tot)) * kMhLn2 : -INFINITY;
+    }
   }
 }
 
@@ -288,7 +324,7 @@ int launch_mha_prefill(const void* q, const void* k_nope, const void* k_pe, cons
   if (hipGetLastError() != hipSuccess) return -5;
   const int nqb = (T + kMhQb - 1) / kMhQb;
   const unsigned grid = (unsigned)B * kMhHeads * nqb;
-  hipLaunchKernelGGL(mha_prefill_kernel, dim3(grid), dim3(kMhThreads), 0, stream,
+  hipLaunchKernelGGL(mha_prefill_kernel, dim3(grid), dim3(kMhPfThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_nope),
                      static_cast<const uint16_t*>(k_pe), static_cast<const uint16_t*>(v), bits, B,
                      T, W, Tp, softmax_scale * kMhLog2e, static_cast<uint16_t*>(out), lse);

@@ -1010,6 +1010,8 @@ def _mha_check(B, T, k, kind, seed, rows=None):
     (1, 37, 64, "last"),      # fewer tokens than one query block
     (1, 200, 2048, "random"), # k >= T: every causal position selected (dense causal)
     (2, 130, 24, "random"),   # causal random selections, two sequences
+    (1, 700, 300, "random"),  # three 256-query blocks, the last one ragged
+    (2, 520, 40, "messy"),    # two sequences of just over two query blocks
 ])
 def test_mha_prefill_vs_oracle(B, T, k, kind):
     """MHA-form prefill (selection bitmap + masked tiles) against the oracle on
