@@ -189,7 +189,7 @@ def test_mha_prefill_validation(L):
     L.dsa_sparse_mha_prefill_workspace_size.restype = ctypes.c_size_t
     L.dsa_sparse_mha_prefill_workspace_size.argtypes = [i32, i32]
     need = L.dsa_sparse_mha_prefill_workspace_size(1, 100)
-    assert need == 4 * 4 * 128          # ceil(100/32) words x 128 padded queries
+    assert need == 4 * 4 * 256          # ceil(100/32) words x 256 padded queries
     assert L.dsa_sparse_mha_prefill_workspace_size(0, 100) == 0
 
     def call(**over):
