@@ -114,6 +114,16 @@ __device__ __forceinline__ void lds_copy16_v(const uint8_t* addr, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m0), "v"(addr) : "m0");
 }
+// The same with the non-temporal hint, for data read once (a streamed key
+// cache): a single pass over a large buffer runs closer to the HBM peak.
+__device__ __forceinline__ void lds_copy16_v_nt(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(m0), "v"(addr) : "m0");
+}
+__device__ __forceinline__ void lds_copy4_v_nt(const uint8_t* addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off nt"
+               :: "s"(m0), "v"(addr) : "m0");
+}
 // 4 bytes a lane (lane i writes at M0 + 4 i).
 __device__ __forceinline__ void lds_copy4_v(const uint8_t* addr, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"

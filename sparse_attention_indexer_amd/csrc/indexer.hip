@@ -168,7 +168,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 // Streaming form of the decode kernel, for long key ranges per wave (at least
 // 4 tiles): the same products, but each wave copies its key tiles straight
 // from HBM into its own LDS ring (global_load_lds, 16 bytes a lane, issued
-// through inline asm so that the compiler's waits never cover them) and keeps
+// through inline asm so that the compiler's waits never cover them, with the
+// non-temporal hint: each key is read once, and a single pass over a large
+// buffer runs closer to the HBM peak that way) and keeps
 // kDepth tiles in flight; a tile's wait is a fixed vmcnt (every copy is
 // issued, clamped to the workgroup's last key), and no barrier is needed since
 // a wave reads only the slots it filled.  The 16-byte chunks of key row r sit
@@ -256,13 +258,13 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
       const int key = c * kKeysPerCopy + ln / kLanesPerKey;
       const int chunk = (ln % kLanesPerKey) ^ (key & 7);
       const int s = min(s0 + key, last);
-      lds_copy16_v(kbase + (size_t)s * kRowBytes + chunk * 16,
-                   __builtin_amdgcn_readfirstlane(lds_addr(slot + c * 1024)));
+      lds_copy16_v_nt(kbase + (size_t)s * kRowBytes + chunk * 16,
+                      __builtin_amdgcn_readfirstlane(lds_addr(slot + c * 1024)));
     }
     if constexpr (kFp8) {
       if (ln < kIdxTile)
-        lds_copy4_v(reinterpret_cast<const uint8_t*>(ksrow + min(s0 + ln, last)),
-                    __builtin_amdgcn_readfirstlane(lds_addr(slot + kIdxTile * kRowBytes)));
+        lds_copy4_v_nt(reinterpret_cast<const uint8_t*>(ksrow + min(s0 + ln, last)),
+                       __builtin_amdgcn_readfirstlane(lds_addr(slot + kIdxTile * kRowBytes)));
     }
   };
 #pragma unroll
