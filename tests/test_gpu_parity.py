@@ -705,6 +705,23 @@ def test_forward_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(idx, ref[2]), rep
+    # The replayed step against the oracle: its selection equals the oracle's
+    # top-k of the GPU's own scores, its attention the oracle's over that selection.
+    gs = m.index_scores(case.q, case.w, case.k_cache, case.end_pos, case.scale, max_end_pos=S)
+    torch.cuda.synchronize()
+    h = np_case(case)
+    ep = h["end_pos"]
+    ref_s = oracle_scores(case, h)
+    g_np = gs.cpu().numpy()
+    for b in range(B):
+        n = int(ep[b])
+        assert_scores_close(g_np[b:b + 1, :, :n], ref_s[b:b + 1, :, :n], ep[b:b + 1], 1,
+                            SCORE_TOL[case.dtype])
+    g_np = np.where(np.isfinite(g_np), g_np, 0.0).astype(np.float32)
+    assert np.array_equal(idx.cpu().numpy(), oracle.topk(g_np, ep, k))
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"], ep,
+                                case.softmax_scale, indices=idx.cpu().numpy())
+    assert_out_close(out, lse, o_ref, lse_ref)
 
 
 @pytest.mark.parametrize("fill", [0x00, 0xFF, 0x3C, "random"])

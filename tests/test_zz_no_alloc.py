@@ -58,3 +58,37 @@ def test_noalloc_repeat_is_identical():
     _, b1 = _both(c)
     _, b2 = _both(c)
     _same(b1, b2)
+
+
+def test_noalloc_captured_in_a_graph():
+    # The callers this entry point is for capture it: each replay, with other
+    # no-allocation calls on other inputs in between (which reuse the same
+    # scratch), gives the eager result bit for bit.
+    case = inputs.make_case("noalloc_graph", 2, 1, [6000, 3500], 6000, seed=31, device=DEV)
+    other = inputs.make_case("noalloc_other", 2, 1, [6000, 5200], 6000, seed=32, device=DEV)
+    B, T, k = case.B, case.T, case.topk
+    out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, 128), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+
+    def run(c):
+        dsa.forward_noalloc(c.q, c.w, c.k_cache, c.end_pos, c.q_nope, c.q_pe, c.kv_cache,
+                            c.pe_cache, c.scale, c.softmax_scale, k=k, max_end_pos=c.S_max,
+                            out=out, lse=lse, topk_out=idx)
+
+    run(case)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), idx.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(case)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        run(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(ref, (out, lse, idx))
