@@ -165,14 +165,14 @@ __device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
   const int lane = threadIdx.x & 63;
   const bool valid = lane < (int)m;
   const uint32_t mine = s_small[min(lane, (int)m - 1)];
-  // All 64 slots in 16-byte reads issued together (the same address in every
-  // lane: broadcast reads); slots past m are skipped.  Four counters per
-  // relation keep the dependent adds in four short chains rather than one long
-  // one (a single wave pays the full latency of every dependent instruction).
+  // Only the m gathered keys are compared (m is uniform and usually a handful:
+  // a single wave pays the full latency of every instruction, so a loop over
+  // all 64 slots cost more than the rest of the selection), four per 16-byte
+  // broadcast read, with four counters per relation.
   const uint4* s4 = reinterpret_cast<const uint4*>(s_small);
   uint32_t gt4[4] = {0u, 0u, 0u, 0u}, ge4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < kWave / 4; ++q) {
+  const int groups = ((int)m + 3) >> 2;
+  for (int q = 0; q < groups; ++q) {
     const uint4 o4 = s4[q];
     const uint32_t other[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
@@ -319,6 +319,41 @@ struct RegCandidates {
       if ((int)threadIdx.x + kThreads * u < M) f(d[u], p[u]);
     }
   }
+  // f(d, p, valid) for every slot some thread holds, with no branch on the
+  // lane's own slot (so the LDS operations of successive slots are issued
+  // together rather than each behind its own branch); the entries of
+  // invalid slots are other candidates' and must not be counted.
+  template <class F>
+  __device__ __forceinline__ void each_all(F&& f) const {
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u) {
+      if (kThreads * u >= M) break;  // uniform
+      f(d[u], p[u], (int)threadIdx.x + kThreads * u < M);
+    }
+  }
+};
+
+// Candidates held in registers in list order: thread tid holds entries
+// kEnt*tid .. kEnt*tid + kEnt - 1 (those below M are valid).
+template <int kThreads, int kEnt>
+struct BlockedCandidates {
+  uint32_t d[kEnt], p[kEnt];
+  int M;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int first = kEnt * (int)threadIdx.x;
+    if (first >= M) return;
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u)
+      if (first + u < M) f(d[u], p[u]);
+  }
+  template <class F>
+  __device__ __forceinline__ void each_all(F&& f) const {
+    const int first = kEnt * (int)threadIdx.x;
+    if (first >= M) return;  // whole waves past the list skip
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u) f(d[u], p[u], first + u < M);
+  }
 };
 
 // Threshold of the k largest among the candidates (at least k of them), by a
@@ -345,7 +380,7 @@ __device__ __forceinline__ void block_threshold(const Cand& cand, int k, Sh& sh,
   uint32_t mx = dmax;
   if (!known_dmax) {
     mx = 0;
-    cand.each([&](uint32_t d, uint32_t) { mx = max(mx, d); });
+    cand.each_all([&](uint32_t d, uint32_t, bool v) { mx = max(mx, v ? d : 0u); });
     mx = wave_max(mx);
     if ((tid & 63) == 0) sh.wave[tid >> 6] = mx;
   }
@@ -358,15 +393,23 @@ __device__ __forceinline__ void block_threshold(const Cand& cand, int k, Sh& sh,
   const int s1 = bits > 11 ? bits - 11 : 0;  // round 1: D >> s1 (< 2048)
   const int s2 = s1 > 11 ? s1 - 11 : 0;      // round 2: bits s2.. of D
   // Round 1.
-  cand.each([&](uint32_t d, uint32_t) { atomicAdd(&sh.hist[hpad(d >> s1)], 1u); });
+  cand.each_all([&](uint32_t d, uint32_t, bool v) {
+    atomicAdd(&sh.hist[hpad(min(d >> s1, (uint32_t)kBins - 1u))], v ? 1u : 0u);
+  });
   uint32_t remaining = (uint32_t)k;
   const uint32_t d1 = sel_select_bin(sh.hist, kBins, remaining, sh.sel);
   const uint32_t m1 = sh.hist[hpad(d1)];  // keys left in the running
   // The keys whose D >> shift equals pre are gathered and ranked directly.
   auto rank_direct = [&](int shift, uint32_t pre, uint32_t m) {
-    cand.each([&](uint32_t d, uint32_t) {
-      if ((d >> shift) == pre) sh.small[atomicAdd(&sh.nsmall, 1u)] = d;
-    });
+    // One LDS atomic per thread that holds any of the few matching keys.
+    uint32_t cnt = 0;
+    cand.each_all([&](uint32_t d, uint32_t, bool v) { cnt += v && (d >> shift) == pre ? 1u : 0u; });
+    if (cnt != 0) {
+      uint32_t at = atomicAdd(&sh.nsmall, cnt);
+      cand.each_all([&](uint32_t d, uint32_t, bool v) {
+        if (v && (d >> shift) == pre) sh.small[min(at++, (uint32_t)kWave - 1u)] = d;
+      });
+    }
     lds_barrier();
     if (tid < kWave) rank_small(sh.small, m, remaining, sh.sel);
     lds_barrier();
@@ -431,6 +474,44 @@ __device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh&
   lds_barrier();
   bitmap_prefixes<kThreads>(sh.sure, sh.eq, sh.pre, nwords, sh.wave);
   lds_barrier();
+}
+
+// Exact selection of the k largest among M >= k candidates that are held in
+// position order (BlockedCandidates: thread tid holds list entries kEnt*tid
+// ..), all with D >= 0.  A winner's output slot is the number of winners
+// before it in the list, so one block scan of two per-thread counts (keys
+// above the threshold, keys equal to it) replaces the position bitmaps: the
+// slot of an entry above is gt_before + min(eq_before, need_eq), an equal
+// entry is kept when eq_before < need_eq, at slot gt_before + eq_before.
+template <int kThreads, int kEnt, class Sh>
+__device__ __forceinline__ void ordered_select(const BlockedCandidates<kThreads, kEnt>& cand,
+                                               int k, int32_t* __restrict__ o, Sh& sh) {
+  uint32_t thr, need_eq;
+  block_threshold<kThreads>(cand, k, sh, false, 0u, thr, need_eq);
+  const int first = kEnt * (int)threadIdx.x;
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < kEnt; ++u) {
+    const bool v = first + u < cand.M;
+    n_gt += v && cand.d[u] > thr ? 1u : 0u;
+    n_eq += v && cand.d[u] == thr ? 1u : 0u;
+  }
+  uint32_t gt, eq, tot_gt, tot_eq;
+  block_exclusive_scan2<true, kThreads / kWave>(n_gt, n_eq, sh.wave, gt, eq, tot_gt, tot_eq);
+  if (n_gt + n_eq == 0) return;
+#pragma unroll
+  for (int u = 0; u < kEnt; ++u) {
+    if (first + u >= cand.M) break;
+    const uint32_t d = cand.d[u];
+    if (d > thr) {
+      const uint32_t at = gt + min(eq, need_eq);
+      if (at < (uint32_t)k) o[at] = (int32_t)cand.p[u];
+      ++gt;
+    } else if (d == thr) {
+      if (eq < need_eq && gt + eq < (uint32_t)k) o[gt + eq] = (int32_t)cand.p[u];
+      ++eq;
+    }
+  }
 }
 
 }  // namespace dsa

@@ -732,15 +732,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
       lds.list[P + r + 32 * j] = list[(size_t)w * kCutCap + r + 32 * j];
   }
   lds_barrier();
-  uint32_t ek[kPickEnt], ep[kPickEnt];
+  // Thread tid takes entries 8 tid .. 8 tid + 7 of the position-ordered list,
+  // so the winners' slots come from one scan of per-thread counts.
+  BlockedCandidates<kTkThreads, kPickEnt> cand;
+  cand.M = (int)M;
 #pragma unroll
-  for (int u = 0; u < kPickEnt; ++u) {
-    const uint2 v = lds.list[min(tid + kTkThreads * u, (int)M - 1)];
-    ek[u] = v.x;
-    ep[u] = v.y;
+  for (int u = 0; u < kPickEnt; ++u) cand.d[u] = cand.p[u] = 0u;
+  if (kPickEnt * tid < (int)M) {
+    const uint4* src = reinterpret_cast<const uint4*>(lds.list + kPickEnt * tid);
+#pragma unroll
+    for (int u = 0; u < kPickEnt / 2; ++u) {
+      const uint4 v = src[u];
+      cand.d[2 * u] = v.x - L;
+      cand.p[2 * u] = v.y;
+      cand.d[2 * u + 1] = v.z - L;
+      cand.p[2 * u + 1] = v.w;
+    }
   }
   lds_barrier();  // the selection's LDS overlaps the staged list
-  split_select<kPickEnt>(ek, ep, (int)M, n, k, o, L, lds.sel);
+  ordered_select(cand, k, o, lds.sel);
 }
 
 __global__ __launch_bounds__(256) void topk_reset_kernel(uint32_t* __restrict__ ctr, int words) {
