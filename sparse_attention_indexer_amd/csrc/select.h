@@ -204,23 +204,33 @@ __device__ __forceinline__ void rank_small(const uint32_t* s_small, uint32_t m,
 // compared with k <= 2048); thread t owns a run of consecutive words.  The
 // caller synchronises before reading `pre`.  A winner then finds its output
 // slot from three LDS words, with no loop over set bits.
-template <int kThreads = 512>
+template <int kThreads, int kMaxWords>
 __device__ __forceinline__ void bitmap_prefixes(const uint32_t* sure, const uint32_t* eq,
                                                 uint32_t* pre, int nwords, uint32_t* s_wave) {
+  // A thread's words are read once into registers: the second pass would
+  // otherwise read them again behind its own stores to `pre`, one LDS round
+  // trip per word.
+  constexpr int kWpt = (kMaxWords + kThreads - 1) / kThreads;
   const int tid = threadIdx.x;
   const int wpt = (nwords + kThreads - 1) / kThreads;
   const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
+  uint32_t cs[kWpt], ce[kWpt];
   uint32_t n_gt = 0, n_eq = 0;
-  for (int w = w0; w < w1; ++w) {
-    n_gt += (uint32_t)__popc(sure[w]);
-    n_eq += (uint32_t)__popc(eq[w]);
+#pragma unroll
+  for (int i = 0; i < kWpt; ++i) {
+    const bool in = w0 + i < w1;
+    cs[i] = in ? (uint32_t)__popc(sure[w0 + i]) : 0u;
+    ce[i] = in ? (uint32_t)__popc(eq[w0 + i]) : 0u;
+    n_gt += cs[i];
+    n_eq += ce[i];
   }
   uint32_t gt, eqb, tot_gt, tot_eq;
   block_exclusive_scan2<true, kThreads / kWave>(n_gt, n_eq, s_wave, gt, eqb, tot_gt, tot_eq);
-  for (int w = w0; w < w1; ++w) {
-    pre[w] = min(gt, 0xFFFFu) | (min(eqb, 0xFFFFu) << 16);
-    gt += (uint32_t)__popc(sure[w]);
-    eqb += (uint32_t)__popc(eq[w]);
+#pragma unroll
+  for (int i = 0; i < kWpt; ++i) {
+    if (w0 + i < w1) pre[w0 + i] = min(gt, 0xFFFFu) | (min(eqb, 0xFFFFu) << 16);
+    gt += cs[i];
+    eqb += ce[i];
   }
 }
 
@@ -472,7 +482,7 @@ __device__ __forceinline__ void block_select(const Cand& cand, int n, int k, Sh&
     else if (d == t) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
   });
   lds_barrier();
-  bitmap_prefixes<kThreads>(sh.sure, sh.eq, sh.pre, nwords, sh.wave);
+  bitmap_prefixes<kThreads, Sh::kMaxPositions / 32>(sh.sure, sh.eq, sh.pre, nwords, sh.wave);
   lds_barrier();
 }
 

@@ -1009,7 +1009,7 @@ __global__ __launch_bounds__(kTkThreads, kMaxN > kLeanExactN ? 1 : 4) void topk_
       }
       lds_barrier();
       // 4. Ordered output: each winner writes its position at its rank.
-      bitmap_prefixes(sh.sure, sh.eq, sh.pre, (n + 31) >> 5, sh.wave);
+      bitmap_prefixes<kTkThreads, kMaxN / 32>(sh.sure, sh.eq, sh.pre, (n + 31) >> 5, sh.wave);
       lds_barrier();
       for (int j = lane; j < my_nc; j += kWave) {
         const uint32_t kk = sh.ck[region + j], p = sh.cp[region + j];
