@@ -38,7 +38,8 @@
  *   validated on the host before anything is launched; on failure nothing
  *   is enqueued.  DSA_ERR_HIP reports a failed launch (hipGetLastError).
  *   Calls are re-entrant and thread-safe; the one global state is the
- *   per-device scratch of dsa_forward_noalloc.
+ *   per-device scratch of dsa_forward_noalloc (the captured step of
+ *   dsa_forward_graph_create is an object the caller owns).
  *
  * Sources of the definitions (web pages on DeepSeek-V3.2's sparse
  * attention): the indexer score and its output shape follow kernelpool's
@@ -194,6 +195,40 @@ int dsa_forward_noalloc(const void* q, const float* q_scale, const float* weight
                         int32_t max_end_pos, int32_t k, float index_scale, float softmax_scale,
                         int32_t dtype, void* out, float* lse, int32_t* topk_indices_out,
                         hipStream_t stream);
+
+/* The decode step captured once and replayed: dsa_forward recorded into a
+ * HIP graph for fixed tensors, sizes and workspace, so that a serving loop
+ * pays one graph launch per step instead of one launch per kernel, and
+ * rewrites the inputs in place between steps (new query, weights, end_pos,
+ * appended cache rows).  The path needs no memset, no allocation and nothing
+ * carried in the workspace from one step to the next, so every replay
+ * computes exactly what a dsa_forward call on the buffers' current contents
+ * would.  Callers: serving loops that replay one decode step per token.
+ *   dsa_forward_graph_create  takes dsa_forward's arguments without the
+ *       stream, validates them as dsa_forward does (nothing is created on
+ *       failure, *graph = NULL), then captures the step on a private stream
+ *       of the current device and instantiates it; DSA_ERR_HIP if capture or
+ *       instantiation fails.  The tensors and workspace must outlive the
+ *       graph; end_pos and max_end_pos keep their meaning for every replay.
+ *   dsa_forward_graph_launch  enqueues one replay on `stream` (a stream of
+ *       the same device); replays of one graph on different streams must not
+ *       overlap in time (they share the workspace).
+ *   dsa_forward_graph_destroy  releases the graph (NULL is a no-op); no
+ *       replay may still be pending.
+ * This is the one part of the library that creates runtime objects (a
+ * stream during capture, the graph); it still allocates no device memory of
+ * its own. */
+typedef struct dsa_forward_graph* dsa_forward_graph_t;
+int dsa_forward_graph_create(const void* q, const float* q_scale, const float* weights,
+                             const void* k_cache, const float* k_scale, const int32_t* end_pos,
+                             const void* q_nope, const void* q_pe, const void* kv_cache,
+                             const void* pe_cache, int32_t B, int32_t T, int32_t S_max,
+                             int32_t max_end_pos, int32_t k, float index_scale,
+                             float softmax_scale, int32_t dtype, void* out, float* lse,
+                             int32_t* topk_indices_out, void* workspace, size_t workspace_bytes,
+                             dsa_forward_graph_t* graph);
+int dsa_forward_graph_launch(dsa_forward_graph_t graph, hipStream_t stream);
+int dsa_forward_graph_destroy(dsa_forward_graph_t graph);
 
 /* Dense baseline: (c) over every causally valid position 0..bound, no index
  * list (the unmasked form of the same decode branch).  Same tensors and

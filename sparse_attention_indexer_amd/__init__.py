@@ -12,6 +12,7 @@ Stages (same names as the C ABI, without the ``dsa_`` prefix):
   sparse_mla    absorbed MLA (128 heads, 512 latent + 64 rope) over the selected rows
   forward       the three stages on one stream
   forward_noalloc  the same with the workspace in the library's per-device scratch
+  ForwardGraph  the forward step captured once into a HIP graph and replayed
   dense_mla     the same attention over every valid position (baseline)
 
 Defaults that matter for capture and latency: without ``max_end_pos`` the
@@ -83,6 +84,11 @@ def _bind(L):
                                    ctypes.c_int),
         "dsa_indexer_prep": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
                              ctypes.c_int),
+        "dsa_forward_graph_create": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                      i32, f32, f32, i32, vp, vp, vp, vp, sz,
+                                      ctypes.POINTER(vp)], ctypes.c_int),
+        "dsa_forward_graph_launch": ([vp, vp], ctypes.c_int),
+        "dsa_forward_graph_destroy": ([vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -402,6 +408,74 @@ def forward_noalloc(q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cac
             _ptr(out), _ptr(lse), _ptr(topk_out), _stream(stream))
     _check(st, "dsa_forward_noalloc")
     return out, lse, topk_out
+
+
+class ForwardGraph:
+    """The decode step captured once (dsa_forward_graph_create) and replayed
+    with launch(): the tensors are bound at construction, so a serving loop
+    rewrites their contents in place between steps.  Keeps references to
+    every bound tensor (the graph reads them at each replay)."""
+
+    def __init__(self, q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cache,
+                 index_scale, softmax_scale, out, lse, topk_out, workspace, k=MAX_TOPK,
+                 q_scale=None, k_scale=None, max_end_pos=None):
+        fp8 = q.dtype == torch.float8_e4m3fn
+        B, T = q.shape[:2]
+        S_max = k_cache.shape[1]
+        dev = q.device
+        _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), (B, T, INDEX_HEADS, INDEX_DIM))
+        _need(weights, "weights", torch.float32, (B, T, INDEX_HEADS), dev)
+        _need(k_cache, "k_cache", q.dtype, (B, S_max, INDEX_DIM), dev)
+        _need(end_pos, "end_pos", torch.int32, (B,), dev)
+        if fp8:
+            _need(q_scale, "q_scale", torch.float32, (B, T, INDEX_HEADS), dev)
+            _need(k_scale, "k_scale", torch.float32, (B, S_max), dev)
+        Bm, Tm, S_kv, _ = _mla_checks(q_nope, q_pe, kv_cache, pe_cache)
+        if (Bm, Tm, S_kv) != (B, T, S_max):
+            raise ValueError("indexer and attention tensors disagree on B, T or S_max")
+        _need(out, "out", torch.bfloat16, (B, T, MLA_HEADS, LATENT_DIM), dev)
+        if lse is not None:
+            _need(lse, "lse", torch.float32, (B, T, MLA_HEADS), dev)
+        if topk_out is not None:
+            _need(topk_out, "topk_out", torch.int32, (B, T, k), dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
+        nb = workspace.numel()
+        if nb < forward_workspace_size(B, T, S_max, k):
+            raise ValueError(f"workspace of {nb} bytes < required "
+                             f"{forward_workspace_size(B, T, S_max, k)}")
+        self._keep = (q, weights, k_cache, end_pos, q_nope, q_pe, kv_cache, pe_cache, out, lse,
+                      topk_out, workspace, q_scale, k_scale)
+        self._h = ctypes.c_void_p()
+        self._lib = lib()
+        with torch.cuda.device(dev):
+            st = self._lib.dsa_forward_graph_create(
+                _ptr(q), _ptr(q_scale) if fp8 else None, _ptr(weights), _ptr(k_cache),
+                _ptr(k_scale) if fp8 else None, _ptr(end_pos), _ptr(q_nope), _ptr(q_pe),
+                _ptr(kv_cache), _ptr(pe_cache), B, T, S_max, _max_end_pos(max_end_pos, S_max),
+                int(k), float(index_scale), float(softmax_scale), FP8_E4M3 if fp8 else BF16,
+                _ptr(out), _ptr(lse), _ptr(topk_out), _ptr(workspace), nb,
+                ctypes.byref(self._h))
+        _check(st, "dsa_forward_graph_create")
+
+    def launch(self, stream=None):
+        """Enqueue one replay of the captured step."""
+        if not self._h:
+            raise RuntimeError("the graph has been destroyed")
+        _check(self._lib.dsa_forward_graph_launch(self._h, _stream(stream)),
+               "dsa_forward_graph_launch")
+
+    def close(self):
+        """Release the graph (no replay may still be pending)."""
+        if self._h:
+            _check(self._lib.dsa_forward_graph_destroy(self._h), "dsa_forward_graph_destroy")
+            self._h = ctypes.c_void_p()
+        self._keep = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def forward_case(case, out=None, lse=None, topk_out=None, workspace=None, stream=None):

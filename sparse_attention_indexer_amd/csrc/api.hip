@@ -1,11 +1,13 @@
 // C ABI of libdsa.so (declared in include/dsa.h): argument validation on the
 // host, workspace carving, and kernel launches on the caller's stream.  No
-// allocation and no synchronisation.  The only global state is the device
-// scratch of dsa_forward_noalloc and the table of its per-device addresses.
+// device allocation and no synchronisation.  The only global state is the
+// device scratch of dsa_forward_noalloc and the table of its per-device
+// addresses; dsa_forward_graph_create returns a captured step the caller owns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <mutex>
+#include <new>
 
 #include "dsa.h"
 
@@ -305,6 +307,70 @@ DSA_EXPORT int dsa_forward_noalloc(const void* q, const float* q_scale, const fl
   return run_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
                      pe_cache, B, T, S_max, max_end_pos, k, index_scale, softmax_scale, dtype,
                      out, lse, topk_indices_out, reinterpret_cast<char*>(ws), L, stream);
+}
+
+// ---- dsa_forward_graph_*: the decode step captured into a HIP graph ----
+struct dsa_forward_graph {
+  hipGraphExec_t exec;
+};
+
+DSA_EXPORT int dsa_forward_graph_create(const void* q, const float* q_scale,
+                                        const float* weights, const void* k_cache,
+                                        const float* k_scale, const int32_t* end_pos,
+                                        const void* q_nope, const void* q_pe,
+                                        const void* kv_cache, const void* pe_cache, int32_t B,
+                                        int32_t T, int32_t S_max, int32_t max_end_pos,
+                                        int32_t k, float index_scale, float softmax_scale,
+                                        int32_t dtype, void* out, float* lse,
+                                        int32_t* topk_indices_out, void* workspace,
+                                        size_t workspace_bytes, dsa_forward_graph_t* graph) {
+  if (!graph) return kErrInvalid;
+  *graph = nullptr;
+  int st = check_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                         pe_cache, B, T, S_max, max_end_pos, k, softmax_scale, dtype, out, lse,
+                         topk_indices_out);
+  if (st) return st;
+  const ForwardLayout L = forward_layout(B, T, S_max, k);
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st) return st;
+  // Capture on a private stream (default priority), thread-local mode, so
+  // other threads' HIP calls are not drawn into the capture.
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return kErrHip;
+  hipGraph_t g = nullptr;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    st = kErrHip;
+  } else {
+    st = run_forward(q, q_scale, weights, k_cache, k_scale, end_pos, q_nope, q_pe, kv_cache,
+                     pe_cache, B, T, S_max, max_end_pos, k, index_scale, softmax_scale, dtype,
+                     out, lse, topk_indices_out, reinterpret_cast<char*>(workspace), L, cs);
+    const hipError_t e = hipStreamEndCapture(cs, &g);  // ends the capture whatever st is
+    if (!st && (e != hipSuccess || !g)) st = kErrHip;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (!st && hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) st = kErrHip;
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (st) return st;
+  dsa_forward_graph* h = new (std::nothrow) dsa_forward_graph{exec};
+  if (!h) {
+    (void)hipGraphExecDestroy(exec);
+    return kErrHip;
+  }
+  *graph = h;
+  return kOk;
+}
+
+DSA_EXPORT int dsa_forward_graph_launch(dsa_forward_graph_t graph, hipStream_t stream) {
+  if (!graph) return kErrInvalid;
+  return hipGraphLaunch(graph->exec, stream) == hipSuccess ? kOk : kErrHip;
+}
+
+DSA_EXPORT int dsa_forward_graph_destroy(dsa_forward_graph_t graph) {
+  if (!graph) return kOk;
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return e == hipSuccess ? kOk : kErrHip;
 }
 
 DSA_EXPORT size_t dsa_dense_mla_workspace_size(int32_t B, int32_t T, int32_t S_max) {

@@ -123,6 +123,26 @@ def test_forward_noalloc_validation(L):
     assert L.dsa_forward_workspace_size(1, 4096, 4096, 2048) <= scratch
 
 
+def test_forward_graph_validation(L):
+    # dsa_forward's checks come first: nothing is created (no stream, no
+    # capture) for a call dsa_forward would refuse, and *graph is NULL.
+    need = L.dsa_forward_workspace_size(2, 1, 1000, 2048)
+    base = [P, None, P, P, None, P, P, P, P, P, 2, 1, 1000, 1000, 2048, 1.0, 1.0, 0, P, None,
+            None]
+    h = ctypes.c_void_p(1234)
+    assert L.dsa_forward_graph_create(*base, P, need - 1, ctypes.byref(h)) == -4
+    assert h.value is None
+    bad = list(base)
+    bad[14] = 4096
+    assert L.dsa_forward_graph_create(*bad, P, need, ctypes.byref(h)) == -2
+    bad = list(base)
+    bad[6] = None
+    assert L.dsa_forward_graph_create(*bad, P, need, ctypes.byref(h)) == -1
+    assert L.dsa_forward_graph_create(*base, P, need, None) == -1  # nowhere to put the graph
+    assert L.dsa_forward_graph_launch(None, None) == -1
+    assert L.dsa_forward_graph_destroy(None) == 0
+
+
 def test_workspace_sizes_monotone(L):
     a = L.dsa_dense_mla_workspace_size(8, 1, 131072)
     b = L.dsa_dense_mla_workspace_size(8, 1, 262144)

@@ -724,6 +724,52 @@ def test_forward_graph_replay_matches_eager():
     assert_out_close(out, lse, o_ref, lse_ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_forward_graph_api_steps_vs_oracle(dtype):
+    """The library's captured decode step (dsa_forward_graph_create / _launch)
+    driven like a serving loop: the bound buffers are rewritten in place with a
+    new batch before each replay (new queries, caches, end positions under the
+    same max_end_pos), and every replay is checked against the oracle on that
+    batch.  Integer-valued indexer inputs, so the selection is exact end to end."""
+    m = dsa()
+    B, S, k = 2, 5000, 2048
+    steps = [([5000, 3100], 31), ([4000, 4999], 32), ([2049, 5000], 33)]
+    first = inputs.make_case("graph_api", B, 1, steps[0][0], S, dtype=dtype, index_dist="int",
+                             seed=steps[0][1], device=DEV)
+    buf = inputs.make_case("graph_api_buf", B, 1, steps[0][0], S, dtype=dtype,
+                           index_dist="int", seed=30, device=DEV)  # other contents at capture
+    ws = torch.empty(m.forward_workspace_size(B, 1, S, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, 1, 128, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, 1, 128), dtype=torch.float32, device=DEV)
+    idx = torch.full((B, 1, k), -7, dtype=torch.int32, device=DEV)
+    graph = m.ForwardGraph(buf.q, buf.w, buf.k_cache, buf.end_pos, buf.q_nope, buf.q_pe,
+                           buf.kv_cache, buf.pe_cache, buf.scale, buf.softmax_scale, out, lse,
+                           idx, ws, k=k, q_scale=buf.q_scale, k_scale=buf.k_scale,
+                           max_end_pos=S)
+    names = ("q", "w", "k_cache", "end_pos", "q_nope", "q_pe", "kv_cache", "pe_cache",
+             "q_scale", "k_scale")
+    try:
+        for eps, seed in steps:
+            banner(f"forward graph api {dtype} end_pos={eps}")
+            case = first if seed == steps[0][1] else inputs.make_case(
+                "graph_api", B, 1, eps, S, dtype=dtype, index_dist="int", seed=seed, device=DEV)
+            for nm in names:
+                src = getattr(case, nm)
+                if src is not None:
+                    getattr(buf, nm).copy_(src)
+            graph.launch()
+            torch.cuda.synchronize()
+            h = np_case(case)
+            ref_s = oracle_scores(case, h)
+            ref_idx = oracle.topk(np.nan_to_num(ref_s, nan=0.0), h["end_pos"], k)
+            assert np.array_equal(idx.cpu().numpy(), ref_idx), f"end_pos {eps}"
+            o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                        h["end_pos"], case.softmax_scale, indices=ref_idx)
+            assert_out_close(out, lse, o_ref, lse_ref)
+    finally:
+        graph.close()
+
+
 @pytest.mark.parametrize("fill", [0x00, 0xFF, 0x3C, "random"])
 def test_topk_any_workspace_content(fill):
     """The top-k workspace carries a histogram between calls; whatever it holds,
