@@ -370,9 +370,8 @@ __global__ __launch_bounds__(kWaves * 64) void mla_kernel(
 // group g, so score wave 2s+h's lane holds exactly half (h) of the B fragment
 // that the same lane of every value wave needs.  The tile's maximum per head
 // (over the four score waves, through LDS) is the softmax reference, so there
-// is no rescaling.  Latent rows sit 1056 bytes apart with chunk c of row r at
-// c ^ ((r >> 3) & 1), as in the wide form; rope parts are 128-byte rows with
-// chunk c at c ^ (r & 7).
+// is no rescaling.  Latent rows sit 1056 bytes apart, unswizzled, as in the
+// wide form; rope parts are 128-byte rows with chunk c at c ^ (r & 7).
 constexpr int kTfWaves = 4;
 constexpr int kTfThreads = kTfWaves * 64;
 constexpr int kTfHeads = 32;
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
     for (int r = 0; r < 16; ++r) {
       const int trow = 16 * wv + r;
       const int pu = max(__builtin_amdgcn_readfirstlane(s_pos[trow]), 0);
-      lds_copy16(kv_b + (size_t)pu * (kDc * 2), (ln ^ ((trow >> 3) & 1)) * 16,
+      lds_copy16(kv_b + (size_t)pu * (kDc * 2), ln * 16,
                  __builtin_amdgcn_readfirstlane(lds_addr(s_kv + trow * kTfPitch)));
     }
 #pragma unroll
@@ -492,10 +491,9 @@ __global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
   {
     const int trow = 16 * wv + r16;
     const uint8_t* kb = s_kv + trow * kTfPitch;
-    const int sw = (trow >> 3) & 1;
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
-      const uint8_t* a = kk < 16 ? kb + (((4 * kk + g) ^ sw) << 4)
+      const uint8_t* a = kk < 16 ? kb + ((4 * kk + g) << 4)
                                  : s_pe + trow * 128 + ((((kk - 16) * 4 + g) ^ (trow & 7)) << 4);
       const uint4 kf = *reinterpret_cast<const uint4*>(a);
 #pragma unroll
@@ -546,14 +544,14 @@ __global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
   for (int j = 0; j < 8; ++j) o[j][0] = o[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
     const uint8_t* vrow = s_kv + (4 * g + (r16 >> 2)) * kTfPitch + 8 * (r16 & 1);
-    const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+    const int vch = (r16 & 3) >> 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint4 pb0 = s_p[ks][0][lane], pb1 = s_p[ks][1][lane];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ct = 8 * wv + j;
-        const int off = ((2 * ct + vch) ^ vsw) << 4;
+        const int off = (2 * ct + vch) << 4;
         const uint8_t* base = vrow + 32 * ks * kTfPitch + off;
         const i16x4 lo = lds_read_tr16(base);
         const i16x4 hi = lds_read_tr16(base + 16 * kTfPitch);
@@ -630,13 +628,13 @@ constexpr int kWdThreads = kWdWaves * 64;
 constexpr int kWdRt = 32;                               // rows per tile
 constexpr int kWdRw = kWdRt / kWdWaves;                 // rows each wave copies (4)
 constexpr int kWdNbuf = 3;
-// Latent rows sit 1056 bytes apart (8 banks), and the 16-byte chunks of rows
-// 8..15 and 24..31 of a tile are XOR-swizzled by 1: chunk c of row r is at
-// position c ^ ((r >> 3) & 1).  The score reads (16 rows, one chunk each per
-// quarter wave) and the transposing value reads (8 rows, two chunks each per
-// half wave) are then both free of bank conflicts.
+// Latent rows sit 1056 bytes apart (8 banks), chunks in order.  Measured with
+// the LDS bank-conflict counter on gfx950, both the score reads (16 rows, one
+// chunk each per quarter wave) and the transposing value reads (8 rows, two
+// chunks each per half wave) are then free of conflicts; an XOR swizzle of
+// the chunks of rows 8..15 by one, which a 16-lane model of the banks called
+// neutral, made 40 % of the score reads' LDS cycles conflict cycles.
 constexpr int kWdPitch = 1056;
-__device__ __forceinline__ int wd_swz(int row) { return (row >> 3) & 1; }
 constexpr int kWdTileKv = kWdRt * kWdPitch;
 constexpr int kWdTileBytes = kWdTileKv + kWdRt * 128;
 constexpr int kWdDims = kDc / kWdWaves;                 // latent dims per value wave (64)
@@ -744,8 +742,8 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
       const int pu = __builtin_amdgcn_readfirstlane(rpos[r]);
       const uint8_t* rowp = kv_b + (size_t)pu * (kDc * 2);
       const int trow = kWdRw * wv + r;
-      // Lane L writes position L, so it fetches chunk L ^ swizzle.
-      lds_copy16(rowp, (opaque_lane() ^ wd_swz(trow)) * 16,
+      // Lane L writes chunk L.
+      lds_copy16(rowp, opaque_lane() * 16,
                  __builtin_amdgcn_readfirstlane(lds_addr(base + trow * kWdPitch)));
     }
     // Rope parts of the 4 rows, one copy per row by lanes 8r..8r+7 (so the
@@ -794,10 +792,9 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
     const int slot = it % kWdNbuf;
     if (have_s) {
       const uint8_t* buf = s_ring + slot * kWdTileBytes;
-      // Rows r16 and 16 + r16 share their swizzle (r16 >> 3): latent step s
-      // of row tile mt is at the offset mt*16*pitch + 64*s from one base.
-      // The rope chunks (4j' + g) ^ (r16 & 7) differ per lane.
-      const uint8_t* kb = buf + r16 * kWdPitch + ((g ^ (r16 >> 3)) << 4) + 9 * 64 * dh;
+      // Latent step s of row tile mt is at the offset mt*16*pitch + 64*s from
+      // one base.  The rope chunks (4j' + g) ^ (r16 & 7) differ per lane.
+      const uint8_t* kb = buf + r16 * kWdPitch + (g << 4) + 9 * 64 * dh;
       const uint8_t* rb = buf + kWdTileKv + r16 * 128;
       f32x4 sp[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                         {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
@@ -877,17 +874,17 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
           for (int j = 0; j < kWdCt; ++j) o[j][h] *= al;
         }
       }
-      // Rows 4g + r16/4 (+16): their swizzle is g >> 1 for both halves.
+      // Rows 4g + r16/4 (+16).
       const uint8_t* vrow = s_ring + (pt % kWdNbuf) * kWdTileBytes +
                             (4 * g + (r16 >> 2)) * kWdPitch + 8 * (r16 & 1);
-      const int vsw = g >> 1, vch = (r16 & 3) >> 1;
+      const int vch = (r16 & 3) >> 1;
 #pragma unroll
       for (int jh = 0; jh < kWdCt; jh += 2) {
         uint4 va[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int ct = kWdCt * wave + jh + jj;
-          const int off = ((2 * ct + vch) ^ vsw) << 4;  // this lane's 16-byte chunk
+          const int off = (2 * ct + vch) << 4;  // this lane's 16-byte chunk
           const i16x4 lo = lds_read_tr16(vrow + off);
           const i16x4 hi = lds_read_tr16(vrow + 16 * kWdPitch + off);
           va[jj] = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
