@@ -6,39 +6,34 @@
 //   out[h,:] = sum_j softmax_j(z[h,:]) * kv[pos_j,:]
 //
 // Work item: one query row and one split of its row list.  Two forms:
-//   narrow (mla_kernel, few query rows, i.e. small-batch decode): a 2-wave
-//     workgroup takes 32 of the 128 heads, so one query spreads over many CUs;
-//   wide (mla_wide_kernel, many query rows): an 8-wave workgroup takes all
-//     128 heads, so every gathered row is read from HBM once for all heads;
-//     its layout and pipeline are described above the kernel.
-// The rest of this header describes the narrow form; the wide one shares its
-// gathers, score layout and online softmax.
+//   tile (mla_tile_kernel, at most 16 query rows, i.e. small-batch decode): a
+//     4-wave workgroup takes 32 of the 128 heads and one 64-row tile of the
+//     list, so one query spreads over 128 workgroups;
+//   wide (mla_wide_kernel, more rows): an 8-wave workgroup takes all 128
+//     heads, so every gathered row is read from HBM once for all heads, and
+//     walks its split in 32-row tiles through a 3-slot ring.
+// Their layouts and pipelines are described above each kernel; they share:
 //
 // Gathers.  Rows are copied from HBM straight into LDS (global_load_lds, 16
-// bytes a lane, no register staging) into a 2-slot ring, so the next tile is
-// in flight while one is computed.  A 512-wide latent row (1 KiB) is one
-// instruction; the 64-wide rope part of 8 rows is another, with its 16-byte
-// chunks XOR-swizzled by row so the score reads do not collide on banks.  The
-// split's row positions are first staged in LDS.  Barriers are plain
-// s_barrier with explicit waits (vmcnt for this wave's copies, lgkmcnt for LDS
-// writes), so the copies for the next tile stay in flight across them.
+// bytes a lane, no register staging).  A 512-wide latent row (1 KiB) is one
+// instruction; the 64-wide rope parts of 8 rows are another, with their
+// 16-byte chunks XOR-swizzled by row so the score reads do not collide on
+// banks.  The positions are first staged in LDS.  Barriers are plain
+// s_barrier with explicit waits (vmcnt for this wave's copies, lgkmcnt for
+// LDS writes), so copies still in flight stay in flight across them.
 //
 // Math, transposed so that each lane owns one head.  Scores are computed as
-// S^T[row][head] = KV[row] . Q[head] (16x16x32 bf16 MFMA, rows as M, the
-// wave's 16 heads as N, K = 576): the lane holding head h gets 16 of the
-// tile's 64 rows.  The online softmax state (running max, partial sum) is
-// therefore per lane; the max over rows needs only two cross-lane swaps
-// (v_permlane32_swap / v_permlane16_swap).  The probabilities stay in
-// registers: the rows a lane holds become the B operand of the value
+// S^T[row][head] = KV[row] . Q[head] (16x16x32 bf16 MFMA, rows as M, 16 heads
+// as N, K = 576): the lane holding head h gets 4 rows of each 16-row M-tile.
+// The softmax state (running max, partial sum) is therefore per lane; the max
+// over rows needs only two cross-lane swaps (v_permlane32_swap /
+// v_permlane16_swap).  The probabilities are the B operand of the value
 // contraction O^T[c][head] += V^T[c][rows] . P[rows][head], whose A operand is
-// read from the row-major LDS tile with ds_read_tr16_b64 (the same K order,
-// rows 16s+4g..16s+4g+3 for lane group g, is used on both sides).  O^T has
-// the head in the lane too, so rescaling by exp2(m_old - m_new) is one
-// multiply per accumulator; it is done lazily, only when a tile's max exceeds
-// the running reference by more than 2^8 (probabilities stay below 256).  The
-// 16x512 fp32 accumulator lives in registers.  With several splits per row,
-// unnormalised partial outputs plus (max, sum) go to the workspace and a
-// combine kernel merges them.
+// read from the row-major LDS tile with ds_read_tr16_b64 (the same K order of
+// rows on both sides).  O^T has the head in the lane too, so rescaling by
+// exp2(m_old - m_new) is one multiply per accumulator.  With several splits
+// per row, unnormalised partial outputs plus (max, sum) go to the workspace
+// and a combine kernel merges them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -47,310 +42,14 @@ namespace dsa {
 constexpr int kHeads = 128;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kNbuf = 2;                     // tiles in the LDS ring
-constexpr int kKvPitch = 1040;               // bytes per latent row in LDS (+16: bank spread)
 constexpr int kMaxSplitRows = 2048;
 
-// Shape of one workgroup: kWaves waves of 16 heads; every wave copies kRw
-// rows of each tile (one instruction per latent row, one per 8 rope rows),
-// so a tile has kRw*kWaves rows.
-template <int kWaves, int kRw>
-struct MlaShape {
-  static constexpr int kThreads = kWaves * 64;
-  static constexpr int kHeadsPerBlock = 16 * kWaves;
-  static constexpr int kHeadGroups = kHeads / kHeadsPerBlock;
-  static constexpr int kRt = kRw * kWaves;                // gathered rows per tile
-  static constexpr int kLoadsPerTile = kRw + kRw / 8;     // per wave
-  static constexpr int kMt = kRt / 16;                    // 16-row M-tiles per tile
-  static constexpr int kKs = kRt / 32;                    // 32-row K-steps of the value product
-  static constexpr int kTileKv = kRt * kKvPitch;
-  static constexpr int kTileBytes = kTileKv + kRt * 128;  // + rope rows (128 B each)
-};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;
 
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return pack2_bf16(a, b); }
-
-// Most positions a split of the narrow form holds (its plans stay below).
-constexpr int kNarrowMaxRows = 512;
-
-template <bool kDense, int kWaves, int kRw>
-__global__ __launch_bounds__(kWaves * 64) void mla_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
-    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ pe,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ end_pos, int T, int S_max,
-    int k, int rows_per_split, int n_splits, int n_items, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float4* __restrict__ part_ml) {
-  using S = MlaShape<kWaves, kRw>;
-  constexpr int kLoadsPerTile = S::kLoadsPerTile;
-  constexpr int kThreads = S::kThreads, kRt = S::kRt, kMt = S::kMt, kKs = S::kKs;
-  constexpr int kTileKv = S::kTileKv, kTileBytes = S::kTileBytes;
-  __shared__ __align__(16) uint8_t s_ring[kNbuf * kTileBytes];
-  __shared__ int s_pos[kNbuf][kRt];  // positions of the tiles in the ring (-1 = empty)
-  __shared__ int s_idx[kDense ? 1 : kNarrowMaxRows];  // the split's positions
-
-  // Block -> (item = row * n_splits + split, head group).  The head groups of
-  // one item get ids that are 8 apart, i.e. fall on the same XCD (ids are dealt
-  // round-robin over the 8 XCDs), so later groups find the rows in its L2.
-  int X, hg;
-  if constexpr (S::kHeadGroups == 1) {
-    X = blockIdx.x;
-    hg = 0;
-  } else {
-    constexpr int G = S::kHeadGroups;
-    const int bid = blockIdx.x;
-    X = (bid / (8 * G)) * 8 + (bid & 7);
-    hg = (bid >> 3) % G;
-  }
-  if (X >= n_items) return;
-  const int row = X / n_splits, split = X - row * n_splits;
-  const int b = row / T, t = row - b * T;
-
-  // Entries in this row's list.  Dense: the causal bound.  Sparse: k, or,
-  // when end_pos is given (a list from the top-k selection, whose kept
-  // positions fill its first min(k, bound) slots), only those slots.
-  int n_list;
-  if (kDense || end_pos != nullptr) {
-    const int ep = min(max(end_pos[b], T), S_max);
-    n_list = ep - T + t + 1;
-    if (!kDense) n_list = min(n_list, k);
-  } else {
-    n_list = k;
-  }
-  const int j_begin = split * rows_per_split;
-  const int j_end = min(j_begin + rows_per_split, n_list);
-  const int n_rows = max(j_end - j_begin, 0);
-  const int n_tiles = (n_rows + kRt - 1) / kRt;
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, r16 = lane & 15;
-
-  // Position of split entry j (-1 = empty slot, also past the end).
-  auto entry_pos = [&](int j) {
-    int pos = -1;
-    if (j < n_rows) {
-      if constexpr (kDense) pos = j_begin + j;
-      else pos = s_idx[j];
-    }
-    return pos;
-  };
-
-  // The split's positions are loaded first and the query's fragments right
-  // after them; the positions go to LDS as soon as they arrive, so the first
-  // tiles' copies start while the query loads are still in flight (the
-  // positions are a few hundred bytes, the query 36 KiB a workgroup).
-  constexpr int kIdxPer = (kNarrowMaxRows + kThreads - 1) / kThreads;
-  int pv[kIdxPer];
-  if constexpr (!kDense) {
-    const int32_t* src = idx + (size_t)row * k + j_begin;
-#pragma unroll
-    for (int u = 0; u < kIdxPer; ++u) {
-      const int j = threadIdx.x + u * kThreads;
-      pv[u] = j < n_rows ? src[j] : -1;
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);  // the position loads go out before the query's
-
-  // Query fragment (B operand of S^T = KV . Q^T): head hg*16*kWaves + wave*16 + r16;
-  // K-step kk holds dims kk*32 + 8g .. +7 of [q_nope | q_pe].
-  const int head = hg * S::kHeadsPerBlock + wave * 16 + r16;
-  uint4 qb[18];
-  {
-    const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc;
-    const uint16_t* qp = q_pe + ((size_t)row * kHeads + head) * kDr;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qb[kk] = ldg16(qn + kk * 32 + g * 8);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = ldg16(qp + kk * 32 + g * 8);
-  }
-  if constexpr (!kDense) {
-#pragma unroll
-    for (int u = 0; u < kIdxPer; ++u) {
-      const int j = threadIdx.x + u * kThreads;
-      if (j < n_rows) s_idx[j] = (pv[u] < 0 || pv[u] >= S_max) ? -1 : pv[u];
-    }
-    lds_barrier();  // LDS only: the query loads stay in flight
-  }
-
-  const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
-  const uint8_t* pe_b = reinterpret_cast<const uint8_t*>(pe) + (size_t)b * S_max * kDr * 2;
-
-  // This wave copies rows kRw*wave .. kRw*wave+kRw-1 of tile `tile` into ring
-  // slot tile % kNbuf.  Empty slots copy row 0 (masked in the softmax).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int tile) {
-    uint8_t* base = s_ring + (tile % kNbuf) * kTileBytes;
-    int rpos[kRw];
-#pragma unroll
-    for (int r = 0; r < kRw; ++r) rpos[r] = entry_pos(tile * kRt + kRw * wv + r);
-    // The tile's positions for the softmax's validity test (published by the
-    // barrier that follows the wait for this tile).
-    {
-      int mine = rpos[0];
-#pragma unroll
-      for (int r = 1; r < kRw; ++r) mine = lane == r ? rpos[r] : mine;
-      if (lane < kRw) s_pos[tile % kNbuf][kRw * wv + lane] = mine;
-    }
-#pragma unroll
-    for (int r = 0; r < kRw; ++r) rpos[r] = max(rpos[r], 0);
-#pragma unroll
-    for (int r = 0; r < kRw; ++r) {
-      const int trow = kRw * wv + r;
-      const int pu = __builtin_amdgcn_readfirstlane(rpos[r]);
-      lds_copy16(kv_b + (size_t)pu * (kDc * 2), lane * 16,
-                 __builtin_amdgcn_readfirstlane(lds_addr(base + trow * kKvPitch)));
-    }
-    // Rope parts, 8 rows per instruction: lane L writes chunk L%8 of row L/8,
-    // holding the row's global chunk (L%8) ^ (row & 7).
-#pragma unroll
-    for (int q8 = 0; q8 < kRw / 8; ++q8) {
-      const int r = 8 * q8 + (lane >> 3);
-      int pos = rpos[0];
-#pragma unroll
-      for (int rr = 1; rr < kRw; ++rr) pos = r == rr ? rpos[rr] : pos;
-      const int trow = kRw * wv + r;
-      const int chunk = (lane & 7) ^ (trow & 7);
-      lds_copy16_v(pe_b + (size_t)pos * (kDr * 2) + chunk * 16,
-                   __builtin_amdgcn_readfirstlane(lds_addr(base + kTileKv + (kRw * wv + 8 * q8) * 128)));
-    }
-  };
-
-  // Running softmax state for head `head` (base 2): reference max, and this
-  // lane's share of the sum relative to it.
-  float m_run = -INFINITY, l_part = 0.f;
-  f32x4 o[32];  // O^T: tile ct holds latent dims ct*16 + 4g + i for this lane's head
-#pragma unroll
-  for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int p = 0; p < kNbuf - 1 && p < n_tiles; ++p) issue(p);
-
-#pragma unroll 1
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    if (tile + kNbuf - 1 < n_tiles) issue(tile + kNbuf - 1);
-    static_assert(kNbuf == 2, "the wait below assumes one tile in flight");
-    if (tile + 1 < n_tiles)  // the next tile's copies may still be in flight
-      __builtin_amdgcn_s_waitcnt(wait_vm(kLoadsPerTile));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    lds_barrier();  // every wave's copies for this tile have landed
-
-    const uint8_t* buf = s_ring + (tile % kNbuf) * kTileBytes;
-
-    // ---- scores S^T[row][head], rows mt*16 + 4g + i ----
-    f32x4 sc[kMt];
-#pragma unroll
-    for (int mt = 0; mt < kMt; ++mt) sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < kMt; ++mt) {
-        const int trow = mt * 16 + r16;
-        const uint8_t* a;
-        if (kk < 16) {
-          a = buf + trow * kKvPitch + (kk * 32 + 8 * g) * 2;
-        } else {
-          const int chunk = ((kk - 16) * 4 + g) ^ (trow & 7);
-          a = buf + kTileKv + trow * 128 + chunk * 16;
-        }
-        sc[mt] = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(a)),
-                                    as_bf16x8(qb[kk]), sc[mt]);
-      }
-    }
-
-    // ---- online softmax for this lane's head ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < kMt; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = s_pos[tile % kNbuf][mt * 16 + 4 * g + i] >= 0;
-        sc[mt][i] = valid ? sc[mt][i] * scale_log2 : -INFINITY;  // now log2-domain score
-        mx = fmaxf(mx, sc[mt][i]);
-      }
-    mx = group_max(mx);
-    // Lazy rescaling: the reference m_run moves only when this tile's max
-    // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
-    // below 2^kRescaleSlack and the accumulators are rarely touched.
-    // Until a head has seen a valid row its accumulators and sum are zero, so
-    // its first reference needs no rescaling.
-    const bool grow = mx > m_run + kRescaleSlack;
-    const bool fresh = m_run == -INFINITY;
-    if (__ballot(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = fresh ? 0.f : exp2f(m_run - m_new);
-      m_run = m_new;
-      l_part *= alpha;
-      if (__ballot(grow && !fresh) != 0) {
-#pragma unroll
-        for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
-      }
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    uint4 pb[kKs];  // B operands of the value contraction, one per 32-row K-step
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      float p[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[h][i] = exp2f(sc[2 * ks + h][i] - m_use);
-          psum += p[h][i];
-        }
-      // K-step ks covers M-tiles 2ks and 2ks+1: rows 32ks + 4g + i, then 32ks + 16 + 4g + i.
-      pb[ks] = uint4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                     pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-    }
-    l_part += psum;
-
-    // ---- values: O^T[c][head] += V^T . P ----
-    // Transposed reads: lane r16 of group g gets V[32ks + 16h + 4g + j][c0 + r16]
-    // (j = 0..3) from the 8-byte rows addressed by lanes 4j + r16/4.
-    const uint8_t* vrow = buf + (4 * g + (r16 >> 2)) * kKvPitch + 8 * (r16 & 3);
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct) {
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const i16x4 lo = lds_read_tr16(vrow + (32 * ks) * kKvPitch + ct * 32);
-        const i16x4 hi = lds_read_tr16(vrow + (32 * ks + 16) * kKvPitch + ct * 32);
-        const uint4 va = uint4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-        o[ct] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb[ks]), o[ct]);
-      }
-    }
-    lds_barrier();  // every wave is done with this slot before it is refilled
-  }
-
-  // ---- finish ----
-  const float l_tot = group_sum(l_part);
-  if (n_splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = out + ((size_t)row * kHeads + head) * kDc + 4 * g;
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct)
-      *reinterpret_cast<uint2*>(orow + ct * 16) =
-          uint2{pack_bf16(o[ct][0] * inv, o[ct][1] * inv), pack_bf16(o[ct][2] * inv, o[ct][3] * inv)};
-    if (lse != nullptr && g == 0)
-      lse[(size_t)row * kHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    // Partial output: the unnormalised accumulator rounded to bf16 (the
-    // range of fp32, so no scaling is needed), plus (max, sum) in fp32.  The
-    // layout is [item][16-dim tile][head][16]: each store instruction writes
-    // 512 contiguous bytes (the wave's 16 heads), i.e. whole cache lines.
-    uint16_t* prow = part_o + (size_t)X * kHeads * kDc + head * 16 + 4 * g;
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct)
-      *reinterpret_cast<uint2*>(prow + ct * kHeads * 16) =
-          uint2{pack_bf16(o[ct][0], o[ct][1]), pack_bf16(o[ct][2], o[ct][3])};
-    if (g == 0) part_ml[(size_t)X * kHeads + head] = float4{m_run, l_tot, 0.f, 0.f};
-  }
-}
 
 // ---- Tile form: few query rows, one 64-row tile per workgroup -------------
 //
@@ -608,14 +307,14 @@ __global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
 //           latent 288..511 and the rope part), its query fragments of both
 //           16-head tiles in registers.  Each K fragment read from LDS then
 //           feeds two MFMAs, so a tile's K is read from LDS four times, not
-//           eight (those reads bound the kernel).  The pair swaps the partial
+//           eight (the largest LDS traffic of the tile).  The pair swaps the partial
 //           scores of the head tile it does not keep through LDS (2 KiB a
-//           wave), and wave w finishes head tile w, as in the narrow form;
+//           wave), and wave w finishes head tile w;
 //   values  O^T[c][head]: wave w takes latent dims 64w..64w+63 for all 128
 //           heads (4 x 8 accumulator tiles, 128 registers), so each transposed
 //           V fragment feeds 8 head tiles and V is read from LDS once per tile
-//           instead of once per wave (in the narrow form the 8-fold re-reading
-//           of V through the transposing LDS read dominates).
+//           instead of once per wave (a split by heads alone would read V
+//           eight times through the transposing LDS read).
 // The probabilities cross between the two through LDS: the lane of a score
 // wave that holds head n and rows {4g+i, 16+4g+i} holds exactly the B
 // fragment (same K order) that lane (n, g) of every value wave needs for that
@@ -1089,25 +788,14 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #ifndef DSA_CB_SPLIT_ROWS
 #define DSA_CB_SPLIT_ROWS 2
 #endif
-#ifndef DSA_MLA_SMALL_ROWS
-#define DSA_MLA_SMALL_ROWS 16
-#endif
-#ifndef DSA_MLA_SMALL_SPLIT_MIN
-#define DSA_MLA_SMALL_SPLIT_MIN 64
-#endif
 #ifndef DSA_MLA_DENSE_SMALL_WORK
 #define DSA_MLA_DENSE_SMALL_WORK 65536
 #endif
 
-// Few query rows (decode at small batch): blocks of 2 waves (32 heads, 16 rows
-// per wave per tile) for one or two rows, else of 4 waves (64 heads, 8 rows
-// per wave per tile: half the L2 re-reads of each gathered row, which pays
-// once several rows fill the chip), and short splits, so one query is spread
-// over many CUs.
-// Otherwise 8-wave blocks of all 128 heads (every gathered row read once) and
-// about one block per CU.
-static int narrow_waves(long rows) { return rows <= 2 ? 2 : 4; }
-
+// Few query rows (decode at small batch): the tile form, 32 heads and 64 rows
+// per workgroup, so one query is spread over many CUs.  Otherwise 8-wave
+// blocks of all 128 heads (every gathered row read once) and about one block
+// per CU.
 #ifndef DSA_MLA_TILE_ROWS
 #define DSA_MLA_TILE_ROWS 16
 #endif
@@ -1116,13 +804,6 @@ MlaPlan sparse_mla_plan(int B, int T, int k) {
   const long rows = (long)B * T;
   if (rows <= DSA_MLA_TILE_ROWS)  // one 64-row tile per workgroup of 32 heads
     return MlaPlan{kTfRows, (k + kTfRows - 1) / kTfRows, kTfWaves, true};
-  if (rows <= DSA_MLA_SMALL_ROWS) {
-    // Splits of k*rows/128 rows (a power of two, at least DSA_MLA_SMALL_SPLIT_MIN):
-    // about 128 items of 2 head groups each.
-    int rps = DSA_MLA_SMALL_SPLIT_MIN;
-    while (rps < kMaxSplitRows && (long)rps * 128 < (long)k * rows) rps *= 2;
-    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (k + rps - 1) / rps, narrow_waves(rows)};
-  }
   long ns = DSA_MLA_TARGET_BLOCKS / rows;
   const long max_ns = (k + 63) / 64;
   ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
@@ -1136,15 +817,10 @@ MlaPlan dense_mla_plan(int B, int T, int S_max, int max_end_pos) {
   const int ext = max_end_pos > 0 ? max_end_pos : S_max;
   // Rows per split depend only on the allocation sizes, so the workspace
   // computed from S_max always covers the launch.
-  // Few rows over a short context: the small-batch shape, as on the sparse
-  // path; otherwise 8-wave blocks, which gather every row once for all heads.
+  // Few rows over a short context: the tile form, as on the sparse path;
+  // otherwise 8-wave blocks, which gather every row once for all heads.
   if (rows <= DSA_MLA_TILE_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK)
     return MlaPlan{kTfRows, (ext + kTfRows - 1) / kTfRows, kTfWaves, true};
-  if (rows <= DSA_MLA_SMALL_ROWS && (long)S_max * rows <= DSA_MLA_DENSE_SMALL_WORK) {
-    int rps = DSA_MLA_SMALL_SPLIT_MIN;
-    while (rps < kMaxSplitRows && (long)rps * 128 < (long)S_max * rows) rps *= 2;
-    if (rps <= kNarrowMaxRows) return MlaPlan{rps, (ext + rps - 1) / rps, narrow_waves(rows)};
-  }
   long rps = (long)S_max * rows / DSA_MLA_TARGET_BLOCKS;
   rps = rps < 512 ? 512 : (rps > kMaxSplitRows ? kMaxSplitRows : rps);
   const int r = round_up((int)rps, 64);
@@ -1155,26 +831,6 @@ size_t mla_workspace_bytes(int B, int T, const MlaPlan& plan) {
   if (plan.n_splits <= 1) return 0;
   const size_t items = (size_t)B * T * plan.n_splits;
   return items * kHeads * kDc * sizeof(uint16_t) + items * kHeads * sizeof(float4);
-}
-
-template <bool kDense, int kWaves, int kRw>
-static int launch_mla_shape(const void* q_nope, const void* q_pe, const void* kv,
-                            const void* pe, const int32_t* idx, const int32_t* end_pos, int T,
-                            int S_max, int k, const MlaPlan& plan, int rows, float softmax_scale,
-                            void* out, float* lse, uint16_t* part_o, float4* part_ml,
-                            hipStream_t stream) {
-  using S = MlaShape<kWaves, kRw>;
-  const int n_items = rows * plan.n_splits;
-  const unsigned grid = S::kHeadGroups == 1
-                            ? (unsigned)n_items
-                            : (unsigned)(((n_items + 7) / 8) * 8 * S::kHeadGroups);
-  hipLaunchKernelGGL((mla_kernel<kDense, kWaves, kRw>), dim3(grid), dim3(S::kThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(q_nope),
-                     reinterpret_cast<const uint16_t*>(q_pe), reinterpret_cast<const uint16_t*>(kv),
-                     reinterpret_cast<const uint16_t*>(pe), idx, end_pos, T, S_max, k,
-                     plan.rows_per_split, plan.n_splits, n_items, softmax_scale * kLog2e,
-                     reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
-  return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 template <bool kDense>
@@ -1200,7 +856,7 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
                        idx, end_pos, T, S_max, k, plan.n_splits, n_items, softmax_scale * kLog2e,
                        reinterpret_cast<uint16_t*>(out), lse, part_o, part_ml);
     st = hipGetLastError() == hipSuccess ? 0 : -5;
-  } else if (plan.waves == 8) {
+  } else {
     hipLaunchKernelGGL((mla_wide_kernel<kDense>), dim3((unsigned)n_items), dim3(kWdThreads), 0,
                        stream, reinterpret_cast<const uint16_t*>(q_nope),
                        reinterpret_cast<const uint16_t*>(q_pe),
@@ -1209,12 +865,6 @@ static int launch_mla(const void* q_nope, const void* q_pe, const void* kv, cons
                        softmax_scale * kLog2e, reinterpret_cast<uint16_t*>(out), lse, part_o,
                        part_ml);
     st = hipGetLastError() == hipSuccess ? 0 : -5;
-  } else if (plan.waves == 4) {
-    st = launch_mla_shape<kDense, 4, 8>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
-                                        rows, softmax_scale, out, lse, part_o, part_ml, stream);
-  } else {
-    st = launch_mla_shape<kDense, 2, 16>(q_nope, q_pe, kv, pe, idx, end_pos, T, S_max, k, plan,
-                                         rows, softmax_scale, out, lse, part_o, part_ml, stream);
   }
   if (st) return st;
   if (plan.n_splits > 1) {
