@@ -404,16 +404,18 @@ def test_sparse_mla_single_row_and_empty():
 
 
 @pytest.mark.parametrize("B,T,S,ep,k,fill", [
-    (2, 8, 5000, [5000, 2500], 2048, "random"),    # 16 rows: the 4-wave small-batch form
+    (2, 2, 5000, [5000, 2500], 2048, "random"),    # 4 rows: the tile form, 32 splits
+    (2, 8, 5000, [5000, 2500], 2048, "random"),    # 16 rows: the 8-wave form, 16 splits
+    (5, 1, 9000, [9000, 4100, 2048, 700, 9000], 2048, "first"),  # 5 rows: 8-wave, 32 splits
     (2, 60, 5000, [5000, 1500], 2048, "random"),   # 120 rows: the many-row form, 2 splits
     (1, 300, 3000, [3000], 2048, "random"),        # 300 rows: one split, direct output
     (4, 9, 400, [400, 30, 200, 9], 100, "last"),   # splits of 64 + 36, short rows, ragged
 ])
 def test_sparse_mla_many_rows(B, T, S, ep, k, fill):
-    """Batches with more than 16 query rows take the 8-wave form (scores per
+    """Batches with more than 4 query rows take the 8-wave form (scores per
     16 heads, values per 64 latent dims, probabilities exchanged through LDS),
-    3 to 16 rows the 4-wave small-batch form; checked on sampled rows,
-    including the first and last."""
+    up to 4 rows the tile form (32 heads, one 64-row tile per workgroup);
+    checked on sampled rows, including the first and last."""
     m = dsa()
     banner(f"sparse_mla many rows B={B} T={T} k={k}")
     case = _mla_inputs(B, T, S, ep, 15)
@@ -448,7 +450,7 @@ def test_dense_mla_many_rows():
 @pytest.mark.parametrize("S,ep,T", [(3000, [3000, 1200], 1), (20000, [20000, 9000], 1),
                                     (4000, [4000, 2100], 3)])
 def test_dense_mla_vs_oracle(S, ep, T):
-    """Two rows (2-wave blocks) and six rows (4-wave blocks), splits ragged at the end."""
+    """Two rows and six rows in the tile form (64-position splits), ragged at the end."""
     m = dsa()
     banner(f"dense_mla S={S} T={T}")
     B = 2
