@@ -12,10 +12,12 @@
 //
 // Four ways to run it, chosen on the host from the row count and the
 // longest row:
-//  * up to 1024 rows of 4097..32768 positions (decode): topk_cut_kernel
-//    spreads each row over workgroups of 2048 positions that cut it down to
-//    position-ordered candidate regions, and topk_pick_kernel, one workgroup
-//    per row, selects among them (two launches);
+//  * up to 1024 rows of 4097..32768 positions, or up to 16 rows of up to
+//    131072 (decode): topk_cut_kernel spreads each row over workgroups of
+//    2048 positions (8192 above 32768)
+//    that cut it down to position-ordered candidate regions, and
+//    topk_pick_kernel, one workgroup per row, selects among them (two
+//    launches);
 //  * other rows when there are at most 1024: topk_split_kernel spreads each
 //    row over workgroups that append their candidates to one list per row,
 //    and topk_finish_kernel selects among them (one launch when a row fits
@@ -530,30 +532,39 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode rows (up to 1024 rows of 4097..32768 positions), two launches.
-//   topk_cut_kernel: a row is spread over workgroups of 512 * kPer = 2048
-//     positions (wave w of a workgroup owns its 64 * kPer consecutive
-//     positions, so every load instruction reads 256 contiguous bytes).  Every workgroup derives the same cut L
-//     from the row's 2048-position sample (as the split top-k) and writes its
-//     keys >= L with their positions to its own region of the row's list, in
-//     position order (waves in order, a wave's entries by ballot rank), and a
-//     header (count, L).  No atomics, nothing to clear.
-//   topk_pick_kernel: one workgroup per row copies the regions into LDS,
-//     takes them into registers (entry tid + 512 u of their concatenation is
-//     thread tid's entry u, 8 per thread) and selects among them as the
-//     finishing launch of the split path does (split_select: radix rounds
-//     over key - L, winner and tie bitmaps, each winner's slot from the
-//     bitmaps' prefix counts).
+// Decode rows (up to 1024 rows of 4097..32768 positions, or up to 16 rows of
+// up to 131072), two launches.
+//   topk_cut_kernel: a row is spread over workgroups of 512 * kPer positions
+//     (2048, or 8192 for rows above 32768; wave w of a workgroup owns its
+//     64 * kPer consecutive positions, so every load instruction reads 256
+//     contiguous bytes).  Every workgroup derives the same cut L from the
+//     row's 2048-position sample (as the split top-k) and writes its keys >= L
+//     with their positions to its own region of the row's list, in position
+//     order (waves in order, a wave's entries by ballot rank), and a header
+//     (count, L).  No atomics, nothing to clear.
+//   topk_pick_kernel: one workgroup per row copies the regions into LDS in
+//     position order, takes entries 8t..8t+7 (16 for the long rows) of their
+//     concatenation into thread t's registers and selects among them with
+//     ordered_select (radix rounds over key - L, each winner's slot from one
+//     block scan).
 // When the list misses (fewer than k keys, a region over its capacity, more
 // entries than the pick holds, or a row longer than promised) the pick
 // workgroup selects the row from scratch (full_row_topk), which is exact
 // whatever the sample said.
 constexpr int kCutCap = 2048;                    // list entries per region
 constexpr int kCutMaxRegions = 16;
-constexpr int kPickCap = 4096;                   // entries the pick workgroup selects over
-constexpr int kPickEnt = kPickCap / kTkThreads;  // per thread (8)
 constexpr int kCutPer = 4;                       // positions per thread of a cut workgroup
-constexpr int kCutMaxN = kCutMaxRegions * kTkThreads * kCutPer;  // 32768
+constexpr int kCutPerLong = 16;                  // the same for rows of 32769..131072
+constexpr int kCutMaxN = kCutMaxRegions * kTkThreads * kCutPer;          // 32768
+constexpr int kCutMaxNLong = kCutMaxRegions * kTkThreads * kCutPerLong;  // 131072
+// Entries the pick workgroup selects over (8 or 16 a thread), and how many
+// of each region's entries a thread loads together with the headers: a
+// 131072-position row keeps ~4500 candidates, ~280 a region.
+template <int kPer> struct PickShape {
+  static constexpr int kCap = kPer == kCutPer ? 4096 : 8192;
+  static constexpr int kEnt = kCap / kTkThreads;
+  static constexpr int kSpec = kPer == kCutPer ? 8 : 12;
+};
 
 struct CutHdr {
   uint32_t count, L, pad0, pad1;
@@ -564,8 +575,17 @@ struct CutWs {
   int n_reg;    // regions (workgroups) per row
 };
 
+// Rows above 32768 positions take the cut path only in small batches: at
+// batch 8 x 131072 its top-k took 15.5 us against 18.4 us for the split path,
+// at batch 64 (8192..131072 positions) 32.4 us against 24.7 us.
+constexpr int kCutLongRows = 16;
 __host__ inline bool cut_path(int rows, int max_end_pos) {
-  return rows <= kMultiRows && max_end_pos > kSplitThreads * kSpPerShort && max_end_pos <= kCutMaxN;
+  if (rows > kMultiRows || max_end_pos <= kSplitThreads * kSpPerShort) return false;
+  return max_end_pos <= kCutMaxN || (rows <= kCutLongRows && max_end_pos <= kCutMaxNLong);
+}
+// Positions per thread of the cut workgroups for rows of at most max_end_pos.
+__host__ inline int cut_per(int max_end_pos) {
+  return max_end_pos <= kCutMaxN ? kCutPer : kCutPerLong;
 }
 __host__ inline size_t cut_ws_bytes(int rows) {
   return align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)) +
@@ -576,7 +596,7 @@ __host__ inline CutWs carve_cut_ws(void* ws, int rows, int max_end_pos) {
   char* p = reinterpret_cast<char*>(ws);
   w.hdr = reinterpret_cast<CutHdr*>(p);
   w.list = reinterpret_cast<uint2*>(p + align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)));
-  const int blk = kTkThreads * kCutPer;
+  const int blk = kTkThreads * cut_per(max_end_pos);
   w.n_reg = (max_end_pos + blk - 1) / blk;
   return w;
 }
@@ -677,7 +697,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __res
 
 union PickLds {
   TopkShared full;                 // full_row_topk (the fallback)
-  uint2 list[kPickCap];            // the regions' entries, concatenated (position order)
+  uint2 list[PickShape<kCutPerLong>::kCap];  // the regions' entries, concatenated (position order)
   SelectSharedT<kCutMaxN> sel;     // the selection, once the list is in registers
 };
 
@@ -687,7 +707,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
                                                                int T, int S_max, int k,
                                                                int32_t* __restrict__ out, CutWs ws) {
   constexpr int kBlk = kTkThreads * kPer;
-  constexpr int kSpec = 8;  // entries per thread loaded before the counts are known
+  constexpr int kSpec = PickShape<kPer>::kSpec;  // entries per thread loaded with the headers
+  constexpr int kPickCap = PickShape<kPer>::kCap, kPickEnt = PickShape<kPer>::kEnt;
   static_assert(kTkThreads == kCutMaxRegions * 32 && 32 * kSpec <= kCutCap, "32 threads per region");
   __shared__ __align__(16) PickLds lds;
   const int row = blockIdx.x;
@@ -1051,11 +1072,19 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
   if (cut_path(rows, max_end_pos)) {
     const CutWs ws = carve_cut_ws(workspace, rows, max_end_pos);
     const dim3 grid((unsigned)((long)rows * ws.n_reg)), block(kTkThreads);
-    hipLaunchKernelGGL(topk_cut_kernel<kCutPer>, grid, block, 0, stream, scores, end_pos, T, S_max,
-                       k, out, ws);
-    if (hipGetLastError() != hipSuccess) return -5;
-    hipLaunchKernelGGL(topk_pick_kernel<kCutPer>, dim3((unsigned)rows), block, 0, stream, scores,
-                       end_pos, T, S_max, k, out, ws);
+    if (cut_per(max_end_pos) == kCutPer) {
+      hipLaunchKernelGGL(topk_cut_kernel<kCutPer>, grid, block, 0, stream, scores, end_pos, T,
+                         S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL(topk_pick_kernel<kCutPer>, dim3((unsigned)rows), block, 0, stream,
+                         scores, end_pos, T, S_max, k, out, ws);
+    } else {
+      hipLaunchKernelGGL(topk_cut_kernel<kCutPerLong>, grid, block, 0, stream, scores, end_pos, T,
+                         S_max, k, out, ws);
+      if (hipGetLastError() != hipSuccess) return -5;
+      hipLaunchKernelGGL(topk_pick_kernel<kCutPerLong>, dim3((unsigned)rows), block, 0, stream,
+                         scores, end_pos, T, S_max, k, out, ws);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   if (rows <= kMultiRows) {

@@ -259,6 +259,21 @@ def test_topk_small_k_and_causal_rows(k):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "relu", "equal"])
+def test_topk_split_path_rows(kind):
+    """More than 16 rows of more than 32768 positions take the split path (lists
+    appended under one device-scope atomic per workgroup, then one finishing
+    workgroup per row); fewer such rows take the cut path of the tests above."""
+    m = dsa()
+    banner(f"topk split path {kind}")
+    B, T, S, k = 20, 1, 70001, 2048
+    ep = np.array([S - 997 * i for i in range(B)], np.int32)
+    scores = inputs.make_scores(B, T, S, kind=kind, seed=31, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_topk_longest_rows():
     m = dsa()
     banner("topk 131072-long rows")
@@ -772,14 +787,17 @@ def test_forward_graph_api_steps_vs_oracle(dtype):
         graph.close()
 
 
+@pytest.mark.parametrize("S", [40000, 140000])
 @pytest.mark.parametrize("fill", [0x00, 0xFF, 0x3C, "random"])
-def test_topk_any_workspace_content(fill):
-    """The top-k workspace carries a histogram between calls; whatever it holds,
-    the selection is exact (a stale or garbage histogram only costs speed)."""
+def test_topk_any_workspace_content(fill, S):
+    """Whatever the top-k workspace holds on entry (region headers, lists and the
+    list counters of the split path, which the call clears itself), the
+    selection is exact: rows up to 131072 positions take the cut path, longer
+    promised bounds the split path."""
     m = dsa()
-    banner(f"topk workspace fill={fill}")
-    B, T, S, k = 3, 1, 40000, 2048
-    ep = np.array([40000, 33000, 9000], np.int32)
+    banner(f"topk workspace fill={fill} S={S}")
+    B, T, k = 3, 1, 2048
+    ep = np.array([S if S <= 131072 else 120000, 33000, 9000], np.int32)
     scores = inputs.make_scores(B, T, S, kind="normal", seed=21, device=DEV)
     nbytes = m.lib().dsa_topk_workspace_size(B, T, S, k)
     if fill == "random":
@@ -790,7 +808,7 @@ def test_topk_any_workspace_content(fill):
         ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
     ref = oracle.topk(scores.cpu().numpy(), ep, k)
     end_pos = torch.from_numpy(ep).to(DEV)
-    for rep in range(3):  # the first call may take the slow path, later ones the fast path
+    for rep in range(3):  # repeated calls over the same workspace
         out = m.topk(scores, end_pos, k, max_end_pos=S, workspace=ws)
         assert np.array_equal(out.cpu().numpy(), ref), rep
 
