@@ -12,9 +12,8 @@
 //
 // Four ways to run it, chosen on the host from the row count and the
 // longest row:
-//  * up to 1024 rows of 4097..32768 positions, or up to 16 rows of up to
-//    131072 (decode): topk_cut_kernel spreads each row over workgroups of
-//    2048 positions (8192 above 32768)
+//  * up to 1024 rows of 4097..131072 positions (decode): topk_cut_kernel
+//    spreads each row over workgroups of 2048 positions (8192 above 32768)
 //    that cut it down to position-ordered candidate regions, and
 //    topk_pick_kernel, one workgroup per row, selects among them (two
 //    launches);
@@ -532,8 +531,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode rows (up to 1024 rows of 4097..32768 positions, or up to 16 rows of
-// up to 131072), two launches.
+// Decode rows (up to 1024 rows of 4097..131072 positions), two launches.
 //   topk_cut_kernel: a row is spread over workgroups of 512 * kPer positions
 //     (2048, or 8192 for rows above 32768; wave w of a workgroup owns its
 //     64 * kPer consecutive positions, so every load instruction reads 256
@@ -543,7 +541,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
 //     order (waves in order, a wave's entries by ballot rank), and a header
 //     (count, L).  No atomics, nothing to clear.
 //   topk_pick_kernel: one workgroup per row copies the regions into LDS in
-//     position order, takes entries 8t..8t+7 (16 for the long rows) of their
+//     position order (32 threads per region load its first entries together
+//     with the headers; the whole workgroup copies what a region holds beyond
+//     them), takes entries 8t..8t+7 (16 for the long rows) of their
 //     concatenation into thread t's registers and selects among them with
 //     ordered_select (radix rounds over key - L, each winner's slot from one
 //     block scan).
@@ -551,7 +551,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
 // entries than the pick holds, or a row longer than promised) the pick
 // workgroup selects the row from scratch (full_row_topk), which is exact
 // whatever the sample said.
-constexpr int kCutCap = 2048;                    // list entries per region
+// List entries per region: a 2048-position region can never overflow; an
+// 8192-position region of a row of ~8-12K positions keeps ~2500 candidates
+// (the sample's margin over k grows as 4 sqrt(n)), the rest far fewer.
+constexpr int kCutCap = 2048;
+constexpr int kCutCapLong = 3072;
 constexpr int kCutMaxRegions = 16;
 constexpr int kCutPer = 4;                       // positions per thread of a cut workgroup
 constexpr int kCutPerLong = 16;                  // the same for rows of 32769..131072
@@ -561,6 +565,7 @@ constexpr int kCutMaxNLong = kCutMaxRegions * kTkThreads * kCutPerLong;  // 1310
 // of each region's entries a thread loads together with the headers: a
 // 131072-position row keeps ~4500 candidates, ~280 a region.
 template <int kPer> struct PickShape {
+  static constexpr int kRegCap = kPer == kCutPer ? kCutCap : kCutCapLong;  // entries per region
   static constexpr int kCap = kPer == kCutPer ? 4096 : 8192;
   static constexpr int kEnt = kCap / kTkThreads;
   static constexpr int kSpec = kPer == kCutPer ? 8 : 12;
@@ -571,17 +576,16 @@ struct CutHdr {
 };
 struct CutWs {
   CutHdr* hdr;  // [rows][kCutMaxRegions]
-  uint2* list;  // [rows][kCutMaxRegions][kCutCap]: (key, position)
+  uint2* list;  // [rows][kCutMaxRegions][PickShape<per>::kRegCap]: (key, position)
   int n_reg;    // regions (workgroups) per row
 };
 
-// Rows above 32768 positions take the cut path only in small batches: at
-// batch 8 x 131072 its top-k took 15.5 us against 18.4 us for the split path,
-// at batch 64 (8192..131072 positions) 32.4 us against 24.7 us.
-constexpr int kCutLongRows = 16;
+// Rows of 4097..131072 positions take the cut path: at batch 8 x 131072 its
+// top-k took 15.8 us against 18.4 us for the split path, at batch 64 (rows of
+// 8192..131072 positions) 22.4 us against 24.7 us.
 __host__ inline bool cut_path(int rows, int max_end_pos) {
-  if (rows > kMultiRows || max_end_pos <= kSplitThreads * kSpPerShort) return false;
-  return max_end_pos <= kCutMaxN || (rows <= kCutLongRows && max_end_pos <= kCutMaxNLong);
+  return rows <= kMultiRows && max_end_pos > kSplitThreads * kSpPerShort &&
+         max_end_pos <= kCutMaxNLong;
 }
 // Positions per thread of the cut workgroups for rows of at most max_end_pos.
 __host__ inline int cut_per(int max_end_pos) {
@@ -589,7 +593,7 @@ __host__ inline int cut_per(int max_end_pos) {
 }
 __host__ inline size_t cut_ws_bytes(int rows) {
   return align256((size_t)rows * kCutMaxRegions * sizeof(CutHdr)) +
-         (size_t)rows * kCutMaxRegions * kCutCap * sizeof(uint2);
+         (size_t)rows * kCutMaxRegions * kCutCapLong * sizeof(uint2);
 }
 __host__ inline CutWs carve_cut_ws(void* ws, int rows, int max_end_pos) {
   CutWs w;
@@ -679,8 +683,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_cut_kernel(const float* __res
     at += w < wave ? c : 0u;
     total += c;
   }
-  if (total <= (uint32_t)kCutCap) {
-    uint2* reg = ws.list + ((size_t)row * kCutMaxRegions + blk) * kCutCap;
+  constexpr int kRegCap = PickShape<kPer>::kRegCap;
+  if (total <= (uint32_t)kRegCap) {
+    uint2* reg = ws.list + ((size_t)row * kCutMaxRegions + blk) * kRegCap;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint64_t m = mk[u];
@@ -709,8 +714,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
   constexpr int kBlk = kTkThreads * kPer;
   constexpr int kSpec = PickShape<kPer>::kSpec;  // entries per thread loaded with the headers
   constexpr int kPickCap = PickShape<kPer>::kCap, kPickEnt = PickShape<kPer>::kEnt;
-  static_assert(kTkThreads == kCutMaxRegions * 32 && 32 * kSpec <= kCutCap, "32 threads per region");
+  constexpr int kRegCap = PickShape<kPer>::kRegCap;
+  constexpr uint32_t kHead = 32 * kSpec;  // entries of a region staged by its own 32 threads
+  constexpr int kRem = (kRegCap - (int)kHead + kTkThreads - 1) / kTkThreads;
+  static_assert(kTkThreads == kCutMaxRegions * 32 && (int)kHead <= kRegCap, "32 threads per region");
   __shared__ __align__(16) PickLds lds;
+  __shared__ uint2 s_reg[kCutMaxRegions];  // (first slot, count) of each region
   const int row = blockIdx.x;
   const int n = row_len(end_pos, row, T, S_max);
   if (n <= k) return;  // done by the cut launch
@@ -723,34 +732,59 @@ __global__ __launch_bounds__(kTkThreads) void topk_pick_kernel(const float* __re
   const int tid = threadIdx.x;
   const int nr = (n + kBlk - 1) / kBlk;  // regions holding positions of this row
   const CutHdr* hdr = ws.hdr + (size_t)row * kCutMaxRegions;
-  const uint2* list = ws.list + (size_t)row * kCutMaxRegions * kCutCap;
+  const uint2* list = ws.list + (size_t)row * kCutMaxRegions * kRegCap;
   // Thread (w, r) = (tid / 32, tid % 32) copies entries r + 32 j of region w.
   // The first kSpec of them are loaded together with the headers.
   const int w = tid >> 5, r = tid & 31;
   uint2 e[kSpec];
 #pragma unroll
-  for (int j = 0; j < kSpec; ++j) e[j] = list[(size_t)w * kCutCap + r + 32 * j];
-  uint32_t M = 0, ok = 1, P = 0, cw = 0;
+  for (int j = 0; j < kSpec; ++j) e[j] = list[(size_t)w * kRegCap + r + 32 * j];
+  uint32_t M = 0, ok = 1, P = 0, cw = 0, over = 0;
   const uint32_t L = hdr[0].L;
 #pragma unroll
   for (int i = 0; i < kCutMaxRegions; ++i) {
     const CutHdr h = i < nr ? hdr[i] : CutHdr{0u, 0u, 0u, 0u};
-    ok &= h.count <= (uint32_t)kCutCap ? 1u : 0u;
+    ok &= h.count <= (uint32_t)kRegCap ? 1u : 0u;
     P += i < w ? h.count : 0u;
     cw = i == w ? h.count : cw;
     M += h.count;
+    over |= (h.count > kHead ? 1u : 0u) << i;
   }
   if (!ok || M < (uint32_t)k || M > (uint32_t)kPickCap) {
     full_row_topk(x, n, k, o, lds.full);
     return;
   }
-  // Stage the list in LDS, in position order.
+  // Stage the list in LDS, in position order: first the entries already
+  // loaded, then, region by region, what a region holds beyond its first
+  // kHead entries, spread over the whole workgroup (all of a region's loads
+  // issued before its stores).
   if (w < nr) {
 #pragma unroll
     for (int j = 0; j < kSpec; ++j)
       if ((uint32_t)(r + 32 * j) < cw) lds.list[P + r + 32 * j] = e[j];
-    for (int j = kSpec; (uint32_t)(r + 32 * j) < cw; ++j)
-      lds.list[P + r + 32 * j] = list[(size_t)w * kCutCap + r + 32 * j];
+  }
+  if (over != 0u) {  // uniform
+    if (r == 0) s_reg[w] = uint2{P, cw};
+    lds_barrier();
+    do {
+      const int i = __builtin_ctz(over);
+      over &= over - 1u;
+      const uint2 pc = s_reg[i];
+      const uint32_t rem = pc.y - kHead;
+      const uint2* src = list + (size_t)i * kRegCap + kHead;
+      uint2* dst = lds.list + pc.x + kHead;
+      uint2 rv[kRem];
+#pragma unroll
+      for (int u = 0; u < kRem; ++u) {
+        const uint32_t ei = (uint32_t)tid + kTkThreads * u;
+        rv[u] = ei < rem ? src[ei] : uint2{0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kRem; ++u) {
+        const uint32_t ei = (uint32_t)tid + kTkThreads * u;
+        if (ei < rem) dst[ei] = rv[u];
+      }
+    } while (over != 0u);
   }
   lds_barrier();
   // Thread tid takes entries 8 tid .. 8 tid + 7 of the position-ordered list,

@@ -260,14 +260,19 @@ def test_topk_small_k_and_causal_rows(k):
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "relu", "equal"])
-def test_topk_split_path_rows(kind):
-    """More than 16 rows of more than 32768 positions take the split path (lists
-    appended under one device-scope atomic per workgroup, then one finishing
-    workgroup per row); fewer such rows take the cut path of the tests above."""
+@pytest.mark.parametrize("S", [70001, 140001])
+def test_topk_many_long_rows(kind, S):
+    """Twenty rows: sixteen long ones and four of 8200..16384 positions.  Up to 131072
+    positions the cut path (8192-position regions) takes them; the short rows fill a
+    region past the share its own threads stage, and "equal" overflows every region
+    (the pick then selects the row from the scores).  Longer rows take the split path
+    (lists appended under one device-scope atomic per workgroup, then one finishing
+    workgroup per row)."""
     m = dsa()
-    banner(f"topk split path {kind}")
-    B, T, S, k = 20, 1, 70001, 2048
-    ep = np.array([S - 997 * i for i in range(B)], np.int32)
+    banner(f"topk many long rows {kind} S={S}")
+    T, k = 1, 2048
+    ep = np.array([S - 997 * i for i in range(16)] + [8200, 12000, 16384, 9000], np.int32)
+    B = len(ep)
     scores = inputs.make_scores(B, T, S, kind=kind, seed=31, device=DEV)
     out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
     ref = oracle.topk(scores.cpu().numpy(), ep, k)
