@@ -302,14 +302,16 @@ __global__ __launch_bounds__(kTfThreads) void mla_tile_kernel(
 // ---- Wide form: many query rows -------------------------------------------
 //
 // Eight waves (two per SIMD).  The two contractions are split differently:
-//   scores  S^T[row][head]: the wave pair 2p, 2p+1 takes heads 32p..32p+31,
-//           wave 2p+d the half d of the 576 score dims (latent 0..287, or
-//           latent 288..511 and the rope part), its query fragments of both
-//           16-head tiles in registers.  Each K fragment read from LDS then
-//           feeds two MFMAs, so a tile's K is read from LDS four times, not
-//           eight (the largest LDS traffic of the tile).  The pair swaps the partial
-//           scores of the head tile it does not keep through LDS (2 KiB a
-//           wave), and wave w finishes head tile w;
+//   scores  S^T[row][head]: wave w takes head tile w (heads 16w..16w+15) over
+//           all 576 score dims, its 18 query fragments in registers, with two
+//           accumulators per 16-row tile (even and odd dim steps) so that four
+//           MFMA chains are in flight.  Each wave reads the whole tile's K from
+//           LDS; no partial scores cross between waves, so a tile needs one
+//           barrier.  (Splitting the dims between the waves of a pair, so that
+//           each K fragment fed two MFMAs and a tile's K was read four times
+//           instead of eight, cost the exchange of partial scores and a second
+//           barrier per tile, and was slower: batch-64 decode 67.7 against 64.5
+//           us, prefill 5.44 against 5.04 ms);
 //   values  O^T[c][head]: wave w takes latent dims 64w..64w+63 for all 128
 //           heads (4 x 8 accumulator tiles, 128 registers), so each transposed
 //           V fragment feeds 8 head tiles and V is read from LDS once per tile
@@ -338,8 +340,8 @@ constexpr int kWdTileKv = kWdRt * kWdPitch;
 constexpr int kWdTileBytes = kWdTileKv + kWdRt * 128;
 constexpr int kWdDims = kDc / kWdWaves;                 // latent dims per value wave (64)
 constexpr int kWdCt = kWdDims / 16;                     // their 16-dim tiles (4)
-constexpr int kWdSteps = (kDc + kDr) / 32 / 2;          // 32-dim score steps per dim half (9)
-static_assert(kWdSteps == 9 && kDc / 32 == 16, "dim halves: latent steps 0-8 | 9-15 and rope 0-1");
+constexpr int kWdSteps = (kDc + kDr) / 32;              // 32-dim score steps (16 latent, 2 rope)
+static_assert(kWdSteps == 18 && kDc / 32 == 16, "latent steps 0-15, rope steps 16-17");
 static_assert(kWdRw == 4, "rope copies use lanes 8r..8r+7 for row r");
 
 template <bool kDense>
@@ -355,7 +357,6 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   __shared__ float s_alpha[2][kHeads];                    // a tile's rescale per head
   __shared__ float s_fin[2][kHeads];                    // m, l per head
   __shared__ __align__(8) uint8_t s_vmask[kWdNbuf][kWdWaves];  // bit r: row 4w+r is valid
-  __shared__ __align__(16) float4 s_x[kWdWaves][2][64];     // partial scores for the pair wave
   __shared__ int s_grow[2];                             // last tile (per parity) whose max moved
   __shared__ int s_idx[kDense ? 1 : kMaxSplitRows];     // the split's positions
 
@@ -404,17 +405,13 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   // Query fragments of the pair's two head tiles (heads 32*(wave/2) + 16*ht
   // + r16) over this wave's dim half: step j is score step 9*dh + j, latent
   // dims 32*step.. for steps below 16, the rope part after.
-  const int head = 16 * wave + r16;  // the head this lane finishes
-  const int dh = wv & 1;
-  uint4 qb[2][kWdSteps];
+  const int head = 16 * wave + r16;  // the head this lane scores and finishes
+  uint4 qb[kWdSteps];
+  {
+    const uint16_t* qn = q_nope + ((size_t)row * kHeads + head) * kDc + g * 8;
+    const uint16_t* qp = q_pe + ((size_t)row * kHeads + head) * kDr + g * 8;
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int hq = 16 * ((wave & ~1) + ht) + r16;
-    const uint16_t* qn = q_nope + ((size_t)row * kHeads + hq) * kDc + 9 * 32 * dh + g * 8;
-    const uint16_t* qp = q_pe + ((size_t)row * kHeads + hq) * kDr + g * 8;
-#pragma unroll
-    for (int j = 0; j < kWdSteps; ++j)
-      qb[ht][j] = ldg16(j < 7 || dh == 0 ? qn + j * 32 : qp + (j - 7) * 32);
+    for (int j = 0; j < kWdSteps; ++j) qb[j] = ldg16(j < 16 ? qn + j * 32 : qp + (j - 16) * 32);
   }
 
   const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * S_max * kDc * 2;
@@ -473,8 +470,7 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
   if (n_tiles > 0) issue(0);
 
   // Iteration it: scores and softmax of tile it, then the values of tile it-1
-  // (whose P was written in the previous iteration): one barrier per tile, and
-  // one between the two halves of the scores.
+  // (whose P was written in the previous iteration): one barrier per tile.
 #pragma unroll 1
   for (int it = 0; it <= n_tiles; ++it) {
     static_assert(kWdNbuf == 3, "slots: tile it-1 (values), tile it (scores), tile it+1 (copies)");
@@ -484,44 +480,32 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
     const int lane = opaque_lane(), g = lane >> 4, r16 = lane & 15;  // recomputed addresses
     const int head = 16 * wave + r16;
 
-    // ---- scores of tile it, this wave's dim half for the pair's 32 heads;
-    //      rows mt*16 + 4g + i ----
+    // ---- scores of tile it for this wave's 16 heads; rows mt*16 + 4g + i ----
     f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     const bool have_s = it < n_tiles;
     const int slot = it % kWdNbuf;
     if (have_s) {
       const uint8_t* buf = s_ring + slot * kWdTileBytes;
-      // Latent step s of row tile mt is at the offset mt*16*pitch + 64*s from
+      // Latent step j of row tile mt is at the offset mt*16*pitch + 64*j from
       // one base.  The rope chunks (4j' + g) ^ (r16 & 7) differ per lane.
-      const uint8_t* kb = buf + r16 * kWdPitch + (g << 4) + 9 * 64 * dh;
+      const uint8_t* kb = buf + r16 * kWdPitch + (g << 4);
       const uint8_t* rb = buf + kWdTileKv + r16 * 128;
-      f32x4 sp[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+      // Two accumulators per row tile (even and odd steps): four independent
+      // MFMA chains.
+      f32x4 sh[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                         {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
       for (int j = 0; j < kWdSteps; ++j) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const uint8_t* a = kb + mt * 16 * kWdPitch + 64 * j;
-          if (j >= 7 && dh == 1) a = rb + mt * 16 * 128 + ((((j - 7) * 4 + g) ^ (r16 & 7)) << 4);
+          const uint8_t* a = j < 16 ? kb + mt * 16 * kWdPitch + 64 * j
+                                    : rb + mt * 16 * 128 + ((((j - 16) * 4 + g) ^ (r16 & 7)) << 4);
           const uint4 kf = *reinterpret_cast<const uint4*>(a);
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-            sp[ht][mt] = mfma_bf16_16x16x32(as_bf16x8(kf), as_bf16x8(qb[ht][j]), sp[ht][mt]);
+          sh[j & 1][mt] = mfma_bf16_16x16x32(as_bf16x8(kf), as_bf16x8(qb[j]), sh[j & 1][mt]);
         }
       }
-      // Keep head tile dh, hand the other one's partial to the pair wave.
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sc[mt] = dh ? sp[1][mt] : sp[0][mt];
-        const f32x4 give = dh ? sp[0][mt] : sp[1][mt];
-        s_x[wv][mt][lane] = float4{give[0], give[1], give[2], give[3]};
-      }
-      lds_barrier();  // the pair's partials are visible
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const float4 got = s_x[wv ^ 1][mt][lane];
-        sc[mt][0] += got.x, sc[mt][1] += got.y, sc[mt][2] += got.z, sc[mt][3] += got.w;
-      }
+      for (int mt = 0; mt < 2; ++mt) sc[mt] = sh[0][mt] + sh[1][mt];
     }
 
     // ---- online softmax of tile it for this lane's head (branch-free) ----
