@@ -402,9 +402,8 @@ __global__ __launch_bounds__(kWdThreads) void mla_wide_kernel(
     return pos;
   };
 
-  // Query fragments of the pair's two head tiles (heads 32*(wave/2) + 16*ht
-  // + r16) over this wave's dim half: step j is score step 9*dh + j, latent
-  // dims 32*step.. for steps below 16, the rope part after.
+  // Query fragments of this wave's head tile: step j covers latent dims
+  // 32j.. for j < 16, the rope part after.
   const int head = 16 * wave + r16;  // the head this lane scores and finishes
   uint4 qb[kWdSteps];
   {
