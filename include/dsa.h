@@ -123,8 +123,9 @@ int dsa_index_scores(const void* q, const float* q_scale, const float* weights,
  * Integer-only selection (order-preserving 32-bit keys): the result is
  * exact.  1 <= k <= 2048.
  * Workspace: dsa_topk_workspace_size bytes, 256-byte aligned (0 bytes, and
- * NULL allowed, when B*T > 1024; otherwise 64 KiB per row when S_max <= 4096
- * and 256 KiB per row above that).  It holds the per-row candidate lists of
+ * NULL allowed, when B*T > 1024; otherwise just over 64 KiB per row when
+ * S_max <= 4096 and just over 384 KiB per row above that: 16 candidate
+ * regions of 3072 (key, position) pairs each).  It holds the per-row candidate lists of
  * one call; its contents on entry do not matter (the call clears whatever it
  * needs cleared) and are unspecified afterwards.  Calls that overlap in time
  * must not share a workspace. */

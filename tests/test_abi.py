@@ -150,6 +150,12 @@ def test_workspace_sizes_monotone(L):
     # up to 1024 rows: two counters and a list of 8192 (key, position) pairs per row
     assert L.dsa_topk_workspace_size(1, 1, 32768, 2048) >= 8192 * 8
     assert L.dsa_topk_workspace_size(64, 1, 131072, 2048) >= 64 * 8192 * 8
+    # the per-row figures dsa.h states: just over 64 KiB up to 4096 positions, just
+    # over 384 KiB (16 regions of 3072 pairs) above
+    for rows, S in ((1, 4096), (7, 1000), (1, 4097), (3, 32768), (64, 131072)):
+        per_row = L.dsa_topk_workspace_size(rows, 1, S, 2048) / rows
+        lo = (64 if S <= 4096 else 384) * 1024
+        assert lo <= per_row < lo + 1024, (rows, S, per_row)
     # more rows: one workgroup per row, no workspace
     assert L.dsa_topk_workspace_size(2048, 1, 65536, 2048) == 0
     assert L.dsa_topk_workspace_size(8, 1024, 8192, 2048) == 0
