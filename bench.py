@@ -15,8 +15,9 @@ against a measured device copy, MFMA FLOPs against the bf16 peak for the
 prefill), a roofline entry for the dominant stage (algorithmic bytes per call
 / average call time, from HIP events on the launch stream), the same figures
 for the batch-64 fp8 decode and the 8192-query prefill workloads, the CPU
-oracle timed on a bounded sample of each workload, and the measured
-sparse-vs-dense break-even context of the batch-8 fp8 sweep.
+oracle timed on a bounded sample of each workload, the measured
+sparse-vs-dense break-even context of the batch-8 fp8 sweep, and the headline
+step through the library's captured-step API (one graph launch per step).
 """
 from __future__ import annotations
 
@@ -271,6 +272,61 @@ def bench_workload(dsa, torch, case, steps, warmup, per_kernel=True, replays=50)
     res["stage_reps"] = reps
     del scores, topk_ws, mla_ws
     return res
+
+
+def bench_library_graph(dsa, torch, case, steps, warmup):
+    """The step through the library's own captured decode step: one
+    dsa_forward_graph_create per rotated input copy, then exactly `steps`
+    dsa_forward_graph_launch calls (one per step, round robin over the copies)
+    between two events on the launch stream."""
+    copies = rotation(case)
+    B, T, S, k = case.B, case.T, case.S_max, case.topk
+    dev = case.q.device
+    ws = torch.zeros(dsa.forward_workspace_size(B, T, S, k), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    graphs = [dsa.ForwardGraph(c.q, c.w, c.k_cache, c.end_pos, c.q_nope, c.q_pe, c.kv_cache,
+                               c.pe_cache, c.scale, c.softmax_scale, out, lse, idx, ws, k=k,
+                               q_scale=c.q_scale, k_scale=c.k_scale, max_end_pos=c.max_end_pos)
+              for c in copies]
+    stream = torch.cuda.current_stream()
+    for i in range(max(warmup, len(graphs))):
+        graphs[i % len(graphs)].launch(stream)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].launch(stream)
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    for g in graphs:
+        g.close()
+    # For comparison: the same steps as plain dsa_forward calls (five kernel launches
+    # each, no graph).
+    def eager(i):
+        c = copies[i % len(copies)]
+        dsa.forward(c.q, c.w, c.k_cache, c.end_pos, c.q_nope, c.q_pe, c.kv_cache, c.pe_cache,
+                    c.scale, c.softmax_scale, k=k, q_scale=c.q_scale, k_scale=c.k_scale,
+                    max_end_pos=c.max_end_pos, out=out, lse=lse, topk_out=idx, workspace=ws,
+                    stream=stream)
+    for i in range(warmup):
+        eager(i)
+    torch.cuda.synchronize()
+    s.record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        eager(i)
+    eager_host_us = (time.perf_counter() - t0) / steps * 1e6
+    e.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = s.elapsed_time(e) / steps
+    return {"ms_per_step": round(ms, 5), "query_tok_s": round(B * T / (ms * 1e-3), 1),
+            "graphs": len(graphs), "steps": steps, "host_us_per_launch": round(host_us, 2),
+            "eager_ms_per_step": round(eager_ms, 5), "eager_host_us_per_step": round(eager_host_us, 2)}
 
 
 def stage_fractions(stage_ms, work, copy_gbs, mfma_stages=()):
@@ -657,6 +713,8 @@ def main(argv=None):
         "copy_bandwidth": copy,
         "peaks": rocminfo_peaks(),
     }
+    # The same step through the library's captured-step API (one launch call a step).
+    line["library_graph_step"] = bench_library_graph(dsa, torch, case, args.steps, args.warmup)
     detail = {"headline": r}
     host_case = case.to("cpu")
     del case
