@@ -587,6 +587,9 @@ __host__ inline bool cut_path(int rows, int max_end_pos) {
   return rows <= kMultiRows && max_end_pos > kSplitThreads * kSpPerShort &&
          max_end_pos <= kCutMaxNLong;
 }
+static_assert(kSplitThreads * kSpPerShort == 4096 && kCutMaxNLong > kSpShortMax,
+              "the split path sees rows of at most 4096 positions (one workgroup, 8 a "
+              "thread) or longer than the cut path's 131072 (16 a thread)");
 // Positions per thread of the cut workgroups for rows of at most max_end_pos.
 __host__ inline int cut_per(int max_end_pos) {
   return max_end_pos <= kCutMaxN ? kCutPer : kCutPerLong;
@@ -1129,30 +1132,21 @@ int launch_topk(const float* scores, const int32_t* end_pos, int B, int T, int S
       if (hipGetLastError() != hipSuccess) return -5;
     }
     const dim3 grid((unsigned)((long)rows * ws.n_blk));
+    // The cut path takes every row count here with max_end_pos in 4097..131072,
+    // so this path sees max_end_pos <= 4096 (8 positions a thread, one
+    // workgroup per row) or above 131072 (16 a thread, several workgroups).
     // With one workgroup per row the first launch selects every row itself
     // (or sends it to full_row_topk): no list, no second launch.
     if (ws.n_blk == 1) {
-      if (split_per_thread(max_end_pos) == kSpPerShort)
-        hipLaunchKernelGGL((topk_split_kernel<kSpPerShort, true>), grid, dim3(kTkThreads), 0,
-                           stream, scores, end_pos, T, S_max, k, out, ws);
-      else
-        hipLaunchKernelGGL((topk_split_kernel<kSpPerLong, true>), grid, dim3(kTkThreads), 0,
-                           stream, scores, end_pos, T, S_max, k, out, ws);
+      hipLaunchKernelGGL((topk_split_kernel<kSpPerShort, true>), grid, dim3(kTkThreads), 0,
+                         stream, scores, end_pos, T, S_max, k, out, ws);
       return hipGetLastError() == hipSuccess ? 0 : -5;
     }
-    if (split_per_thread(max_end_pos) == kSpPerShort) {
-      hipLaunchKernelGGL((topk_split_kernel<kSpPerShort, false>), grid, dim3(kTkThreads), 0,
-                         stream, scores, end_pos, T, S_max, k, out, ws);
-      if (hipGetLastError() != hipSuccess) return -5;
-      hipLaunchKernelGGL(topk_finish_kernel<kSpPerShort>, dim3((unsigned)rows), dim3(kTkThreads),
-                         0, stream, scores, end_pos, T, S_max, k, out, ws);
-    } else {
-      hipLaunchKernelGGL((topk_split_kernel<kSpPerLong, false>), grid, dim3(kTkThreads), 0,
-                         stream, scores, end_pos, T, S_max, k, out, ws);
-      if (hipGetLastError() != hipSuccess) return -5;
-      hipLaunchKernelGGL(topk_finish_kernel<kSpPerLong>, dim3((unsigned)rows), dim3(kTkThreads),
-                         0, stream, scores, end_pos, T, S_max, k, out, ws);
-    }
+    hipLaunchKernelGGL((topk_split_kernel<kSpPerLong, false>), grid, dim3(kTkThreads), 0,
+                       stream, scores, end_pos, T, S_max, k, out, ws);
+    if (hipGetLastError() != hipSuccess) return -5;
+    hipLaunchKernelGGL(topk_finish_kernel<kSpPerLong>, dim3((unsigned)rows), dim3(kTkThreads),
+                       0, stream, scores, end_pos, T, S_max, k, out, ws);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   if (S_max <= kLeanExactN) {  // every row is at most 8192 long
