@@ -765,6 +765,13 @@ def main(argv=None):
                                     "workload": "sweep_b8_fp8", "contexts": ctxs,
                                     "sparse_ms": [round(x, 5) for x in sp],
                                     "dense_ms": [round(x, 5) for x in de]}
+        # Contexts of at most k positions keep every key, so skipping the indexer and the
+        # selection (dense attention over each causal prefix) gives the same output; the
+        # default path runs every stage, and this is the time such a bypass takes.
+        short = [i for i, c in enumerate(ctxs) if c <= inputs.TOPK]
+        line["dense_break_even"]["bypass"] = {
+            "contexts": [ctxs[i] for i in short], "ms": [round(de[i], 5) for i in short],
+            "full_path_ms": [round(sp[i], 5) for i in short]}
         detail["sweep"] = line["dense_break_even"]
 
     if not args.no_cpu:

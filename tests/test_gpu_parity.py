@@ -683,6 +683,35 @@ def test_forward_sweep_b8_fp8_sampled(n):
     _check_forward_rows(inputs.sweep(n, device=DEV), [0, 7])
 
 
+@pytest.mark.parametrize("n,T", [(1024, 1), (2048, 1), (2000, 16)])
+def test_forward_short_context_equals_dense(n, T):
+    """Every query with at most k valid positions keeps all of them (topk(min(k, end_pos))
+    of Indexer.forward), so the full indexer -> top-k -> attention path must give the
+    dense attention over each causal prefix (the bypass MLX takes for short contexts):
+    the selection is 0..bound then -1 bit for bit, and the two outputs agree within the
+    attention tolerance."""
+    m = dsa()
+    banner(f"forward short context n={n} T={T}")
+    B, k = 8 if T == 1 else 2, 2048
+    case = inputs.make_case(f"short_{n}_{T}", B, T, [n] * B, n, dtype="fp8", seed=29,
+                            device=DEV)
+    out, lse, idx = m.forward_case(case, topk_out=torch.empty((B, T, k), dtype=torch.int32,
+                                                               device=DEV))
+    dout, dlse = m.dense_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, case.end_pos,
+                             case.softmax_scale, max_end_pos=n)
+    torch.cuda.synchronize()
+    bound = n - T + np.arange(T)  # last valid position of each query row
+    want = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        want[t, :bound[t] + 1] = np.arange(bound[t] + 1)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], want), b
+    diff = (out.float() - dout.float()).abs().max().item()
+    assert diff <= OUT_TOL, diff
+    assert (lse - dlse).abs().max().item() <= LSE_TOL
+
+
 def test_forward_deterministic():
     m = dsa()
     banner("forward determinism")
