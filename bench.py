@@ -536,6 +536,18 @@ def _oracle_step(h, case, rows=None):
                case.softmax_scale, indices=idx, rows=rows)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, budget_s=15.0):
     """The CPU oracle (as it stands) on a bounded sample: whole decode steps of the workload."""
     import oracle
@@ -548,7 +560,7 @@ def cpu_baseline(case, budget_s=15.0):
         if el >= budget_s or reps >= 2000:
             break
     q_tok = reps * case.B * case.T
-    return {"value": q_tok / el, "unit": "query-tok/s", "cores": oracle.max_threads(),
+    return {"value": q_tok / el, "unit": "query-tok/s", "cores": oracle.max_threads(), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{reps} whole decode step(s) of {case.name} (B={case.B}, T={case.T}, "
                       f"n={case.max_end_pos}): fp64 indexer over every key, full-sort top-"
@@ -571,7 +583,7 @@ def cpu_baseline_decode_sample(case, budget_s=10.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "query-tok/s", "cores": oracle.max_threads(),
+    return {"value": done / el, "unit": "query-tok/s", "cores": oracle.max_threads(), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{done} of the {case.B} sequences of {case.name} (mean context "
                       f"{keys // max(1, done)}), each a whole decode step; {el:.1f} s"}
@@ -608,7 +620,7 @@ def cpu_baseline_prefill_sample(case, budget_s=10.0, n_rows=1024):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "query-tok/s", "cores": oracle.max_threads(),
+    return {"value": done / el, "unit": "query-tok/s", "cores": oracle.max_threads(), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{done} of {n_rows} evenly spaced query rows of {case.name} "
                       f"(T={case.T}), each scored, selected and attended on its own; "
