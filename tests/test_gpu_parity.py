@@ -566,6 +566,57 @@ def _check_forward_rows(case, seqs):
         assert_out_close(out[sub], lse[sub], o_ref, lse_ref)
 
 
+def _random_forward_case(seed):
+    """A seeded batch drawn across the plan boundaries: query rows on either side
+    of the small-batch attention form (4 rows) and of the prefill indexer form
+    (8 queries), contexts on either side of the top-k path limits (4096, 32768),
+    ragged end_pos, k below and at 2048, both indexer dtypes."""
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.choice([1, 1, 2, 3, 7, 8, 9, 16]))
+    B = int(rng.integers(1, (6 if T == 1 else 3) + 1))
+    S = int(rng.choice([2300, 4096, 4097, 8192, 20000, 32768, 32769, 70000]))
+    k = int(rng.choice([2048, 2048, 1024, 300]))
+    dtype = str(rng.choice(["bf16", "fp8"]))
+    ep = rng.integers(T, S + 1, size=B)
+    ep[int(rng.integers(0, B))] = S  # one sequence fills the cache
+    return inputs.make_case(f"rand{seed}", B, T, [int(x) for x in ep], S, dtype=dtype,
+                            seed=2000 + seed, device=DEV, topk=k)
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_forward_random_shapes(seed):
+    """dsa_forward on seeded shapes across the plan boundaries, every query row of
+    up to two sequences checked as in the fixed-shape tests: scores within
+    tolerance of the oracle's, the selection bit-exact against the oracle's top-k
+    of the GPU's own scores, the attention within tolerance of the oracle's over
+    that selection."""
+    m = dsa()
+    case = _random_forward_case(seed)
+    B, T, k = case.B, case.T, case.topk
+    ep_all = case.end_pos.cpu().numpy()
+    banner(f"forward random seed={seed}: B={B} T={T} S_max={case.S_max} k={k} "
+           f"dtype={case.dtype} end_pos={ep_all.tolist()}")
+    topk_out = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    out, lse, _ = m.forward_case(case, topk_out=topk_out)
+    gs = _gpu_scores_like_forward(m, case)
+    torch.cuda.synchronize()
+    idx = topk_out.cpu().numpy()
+    check_topk_invariants(idx, ep_all, T, k)
+    for b in sorted({0, B - 1}):
+        sub = slice(b, b + 1)
+        h = np_case(case, rows_b=sub)
+        n = int(ep_all[b])
+        ref_s = oracle.index_scores(h["q"], h["w"], h["k_cache"], h["end_pos"], case.scale,
+                                    q_scale=h["q_scale"], k_scale=h["k_scale"])
+        g = gs[sub, :, :n].cpu().numpy()
+        assert_scores_close(g, ref_s[:, :, :n], h["end_pos"], T, SCORE_TOL[case.dtype])
+        ref_idx = oracle.topk(np.ascontiguousarray(g), h["end_pos"], k)
+        assert np.array_equal(idx[sub], ref_idx), f"sequence {b}: selection differs"
+        o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                    h["end_pos"], case.softmax_scale, indices=idx[sub])
+        assert_out_close(out[sub], lse[sub], o_ref, lse_ref)
+
+
 def test_forward_decode_32k_normal():
     """The 32K bf16 decode workload, as timed: scores within tolerance of the
     oracle's, the selection bit-exact against the oracle's top-k of the GPU's
