@@ -323,6 +323,31 @@ def test_topk_many_rows(B, T, S, kind):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_topk_random_shapes(seed):
+    """dsa_topk alone on seeded shapes across its paths: row counts on either side of
+    1024 (the candidate paths against one workgroup per row), lengths on either side
+    of 4096, 8192, 32768 and 131072, ragged end_pos, any k up to 2048 and every score
+    kind; bit-exact against the oracle's full sort."""
+    m = dsa()
+    rng = np.random.default_rng(3000 + seed)
+    rows = int(rng.choice([1, 3, 17, 700, 1024, 1025, 1500]))
+    T = int(rng.choice([1, 2, 5])) if rows > 1 else 1
+    B = max(1, rows // T)
+    S = int(rng.choice([1000, 4096, 4097, 8192, 8193, 32768, 32769, 131072, 131073]))
+    if B * T > 64:
+        S = min(S, 33000)  # keeps the oracle's sort within seconds
+    k = int(rng.choice([1, 7, 300, 2047, 2048]))
+    kind = str(rng.choice(["normal", "ties", "equal", "zeros", "relu", "wide"]))
+    ep = rng.integers(T, S + 1, size=B).astype(np.int32)
+    ep[int(rng.integers(0, B))] = S
+    banner(f"topk random seed={seed}: B={B} T={T} S={S} k={k} kind={kind}")
+    scores = inputs.make_scores(B, T, S, kind=kind, seed=4000 + seed, device=DEV)
+    out = m.topk(scores, torch.from_numpy(ep).to(DEV), k, max_end_pos=S)
+    ref = oracle.topk(scores.cpu().numpy(), ep, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_topk_rows_around_bitmap_limit():
     """Rows up to 262144 positions are selected through LDS bitmaps; longer
     ones take the general path.  Both sides of that limit, and a row whose
