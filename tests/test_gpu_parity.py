@@ -476,6 +476,53 @@ def test_sparse_mla_many_rows(B, T, S, ep, k, fill):
     assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
 
 
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_mla_random_shapes(seed):
+    """dsa_sparse_mla and dsa_dense_mla alone on seeded shapes across their plans:
+    query rows on either side of the tile form's 4 (sparse) and 16 (dense) rows,
+    list lengths k that end inside a 64-row tile or a split, selections that are
+    random, leading or trailing, some of them shuffled and with empty (-1) or
+    out-of-range slots; sampled rows against the oracle."""
+    m = dsa()
+    rng = np.random.default_rng(5000 + seed)
+    T = int(rng.choice([1, 1, 2, 3, 5, 9]))
+    B = int(rng.integers(1, (6 if T == 1 else 3) + 1))
+    S = int(rng.choice([700, 2048, 2500, 5000, 20000]))
+    k = int(rng.choice([64, 100, 1000, 2047, 2048]))
+    fill = str(rng.choice(["random", "first", "last"]))
+    ep = rng.integers(T, S + 1, size=B)
+    ep[int(rng.integers(0, B))] = S
+    ep = [int(x) for x in ep]
+    banner(f"mla random seed={seed}: B={B} T={T} S={S} k={k} fill={fill} end_pos={ep}")
+    case = _mla_inputs(B, T, S, ep, 30 + seed)
+    idx = inputs.make_indices(B, T, ep, k, seed=40 + seed, fill=fill)
+    ref_idx = idx.clone()
+    if seed % 3 == 0:  # any order; an empty slot of each row holding S_max + 5 instead of -1
+        for b in range(B):
+            for t in range(T):
+                perm = torch.from_numpy(rng.permutation(k))
+                idx[b, t] = idx[b, t, perm]
+        ref_idx = idx.clone()  # the selection the library must use: out-of-range = empty
+        empty = (idx == -1).nonzero()
+        if len(empty):
+            idx[tuple(empty[0].tolist())] = S + 5
+    idx = idx.to(DEV)
+    out, lse = m.sparse_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, idx,
+                            case.softmax_scale)
+    dout, dlse = m.dense_mla(case.q_nope, case.q_pe, case.kv_cache, case.pe_cache, case.end_pos,
+                             case.softmax_scale, max_end_pos=S)
+    h = np_case(case)
+    n = B * T
+    rows = sorted({0, n // 2, n - 1})
+    o_ref, lse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                h["end_pos"], case.softmax_scale, indices=ref_idx.numpy(),
+                                rows=rows)
+    assert_out_close(out, lse, o_ref, lse_ref, rows=rows)
+    d_ref, dlse_ref = oracle.mla(h["q_nope"], h["q_pe"], h["kv_cache"], h["pe_cache"],
+                                 h["end_pos"], case.softmax_scale, rows=rows)
+    assert_out_close(dout, dlse, d_ref, dlse_ref, rows=rows)
+
+
 def test_dense_mla_many_rows():
     """Dense attention for 40 query rows over 3000 positions: the many-row form
     with splits of 512 positions (the last one partial)."""
