@@ -1147,6 +1147,36 @@ def test_indexer_prep_random(fp8, kind):
     _check_untouched(kc, ks, ep.cpu(), T, fp8)
 
 
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_indexer_prep_random_shapes(seed):
+    """dsa_indexer_prep on seeded ragged batches: 1 to 5 sequences, 1 to 300 new
+    tokens each, caches a little or much longer than the longest sequence, fp8 or
+    bf16; every written query and key against the oracle, the rest of the cache
+    untouched."""
+    m = dsa()
+    rng = np.random.default_rng(6000 + seed)
+    B = int(rng.integers(1, 6))
+    T = int(rng.choice([1, 2, 3, 17, 64, 300]))
+    ep = [int(x) for x in rng.integers(T, T + 700, size=B)]
+    S_max = max(ep) + int(rng.choice([0, 1, 129, 5000]))
+    fp8 = bool(rng.integers(0, 2))
+    banner(f"prep random seed={seed}: B={B} T={T} S_max={S_max} fp8={fp8} end_pos={ep}")
+    q_in, k_in, cos, sin, ep_t = inputs.make_prep(B, T, ep, S_max, seed=7000 + seed, device=DEV)
+    qo, qs, kc, ks = _prep_run(m, q_in, k_in, cos, sin, ep_t, S_max, fp8)
+    rq, rqs, rk, rks, pos = oracle.indexer_prep(inputs.to_numpy(q_in), inputs.to_numpy(k_in),
+                                                cos.cpu().numpy(), sin.cpu().numpy(),
+                                                ep_t.cpu().numpy(), fp8=fp8)
+    gk = np.stack([inputs.to_numpy(kc[b])[pos[b]] for b in range(B)])
+    if fp8:
+        gks = np.stack([ks[b].cpu().numpy()[pos[b]] for b in range(B)])
+        _compare_prep_fp8(qo, qs.cpu().numpy(), rq, rqs)
+        _compare_prep_fp8(torch.from_numpy(gk).view(torch.float8_e4m3fn), gks, rk, rks)
+    else:
+        _compare_prep_bf16(qo.float().cpu().numpy(), rq)
+        _compare_prep_bf16(torch.from_numpy(gk).view(torch.bfloat16).float().numpy(), rk)
+    _check_untouched(kc, ks, ep_t.cpu(), T, fp8)
+
+
 @pytest.mark.parametrize("shape", ["prefill_8192", "decode_b64"])
 def test_indexer_prep_full_size_sampled(shape):
     """The two full-size shapes at which the preparation is timed -- one sequence
@@ -1258,6 +1288,23 @@ def test_mha_prefill_vs_oracle(B, T, k, kind):
     every query row."""
     banner(f"mha prefill B={B} T={T} k={k} {kind}")
     _mha_check(B, T, k, kind, seed=B * 1000 + T)
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_mha_prefill_random_shapes(seed):
+    """dsa_sparse_mha_prefill on seeded shapes: 1 or 2 sequences of 1 to 1100
+    tokens (query blocks of 256 with ragged tails), k from 1 to 2048, random,
+    trailing or messy selections (duplicates, future and out-of-range entries);
+    sampled rows against the oracle."""
+    rng = np.random.default_rng(8000 + seed)
+    B = int(rng.integers(1, 3))
+    T = int(rng.choice([1, 5, 63, 64, 255, 257, 600, 1100]))
+    k = int(rng.choice([1, 16, 300, 2048]))
+    kind = str(rng.choice(["random", "last", "messy"]))
+    banner(f"mha random seed={seed}: B={B} T={T} k={k} {kind}")
+    n = B * T
+    rows = sorted({0, T - 1, n // 2, n - 1} | {int(x) for x in rng.integers(0, n, size=3)})
+    _mha_check(B, T, k, kind, seed=9000 + seed, rows=rows)
 
 
 def test_mha_prefill_8192_sampled():
