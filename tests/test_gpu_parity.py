@@ -1009,10 +1009,12 @@ def test_prefill_8192_sampled():
 
 # --- query absorption and output up-projection --------------------------------------
 
-@pytest.mark.parametrize("B,T", [(1, 1), (3, 37), (1, 300)])
+@pytest.mark.parametrize("B,T", [(1, 1), (3, 37), (1, 300), (1, 2), (1, 63), (1, 64), (5, 13),
+                                 (2, 128), (1, 256), (1, 257), (4, 150)])
 def test_q_absorb_and_out_proj(B, T):
     """Both head-batched products against the oracle: one decode row, a ragged
-    batch (two 64-row workgroups, the second partial), and 300 rows."""
+    batch (two 64-row workgroups, the second partial), 300 rows, and row counts
+    around the 64-row blocks and the up-projection's switch at 256 rows."""
     m = dsa()
     banner(f"absorb / up-projection B={B} T={T}")
     qn, wkv, x = inputs.make_proj(B, T, seed=B * 100 + T, device=DEV)
