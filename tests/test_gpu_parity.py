@@ -1007,6 +1007,39 @@ def test_prefill_8192_sampled():
         assert np.abs(o_gpu - o_ref[0, 0]).max() < OUT_TOL, t
 
 
+def test_forward_chunked_prefill_long_cache_fp8():
+    """1100 new queries at the end of a 40000-position fp8 cache (a chunk of a long
+    prefill): more than 1024 query rows over rows longer than 32768 positions, so the
+    forward path's selection is the chunk-by-chunk whole-row form, behind the prefill
+    indexer form and the many-row attention.  Sampled rows as in the 8192-token test:
+    scores within tolerance, selection bit-exact on the GPU's own scores, attention
+    within tolerance over it."""
+    m = dsa()
+    banner("forward chunked prefill T=1100 over 40000 fp8")
+    B, T, S = 1, 1100, 40000
+    case = inputs.make_case("chunk", B, T, [S], S, dtype="fp8", seed=61, device=DEV)
+    k = case.topk
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    out, _, _ = m.forward_case(case, topk_out=idx)
+    gs = _gpu_scores_like_forward(m, case)
+    torch.cuda.synchronize()
+    h = np_case(case)
+    for t in (0, 1, 547, 1098, 1099):
+        bound = S - T + t
+        ep = np.array([bound + 1], np.int32)
+        ref_s = oracle.index_scores(h["q"][:, t:t + 1], h["w"][:, t:t + 1], h["k_cache"], ep,
+                                    case.scale, q_scale=h["q_scale"][:, t:t + 1],
+                                    k_scale=h["k_scale"])[0, 0, :bound + 1]
+        g_s = gs[0, t, :bound + 1].cpu().numpy()
+        err = np.abs(g_s.astype(np.float64) - ref_s).max() / max(np.abs(ref_s).max(), 1e-30)
+        assert err <= SCORE_TOL["fp8"], (t, float(err))
+        ref_i = oracle.topk(g_s.reshape(1, 1, -1), ep, k)
+        assert np.array_equal(idx[0, t].cpu().numpy(), ref_i[0, 0]), t
+        o_ref, _ = oracle.mla(h["q_nope"][:, t:t + 1], h["q_pe"][:, t:t + 1], h["kv_cache"],
+                              h["pe_cache"], ep, case.softmax_scale, indices=ref_i)
+        assert np.abs(out[0, t].float().cpu().numpy() - o_ref[0, 0]).max() < OUT_TOL, t
+
+
 # --- query absorption and output up-projection --------------------------------------
 
 @pytest.mark.parametrize("B,T", [(1, 1), (3, 37), (1, 300), (1, 2), (1, 63), (1, 64), (5, 13),
