@@ -224,16 +224,14 @@ __global__ __launch_bounds__(16 * kGroups) void indexer_prep_kernel(
   }
 }
 
-// Many tokens: 4 lanes per vector, 32 consecutive dims per lane (four 16-byte
-// loads).  The rotation's index bits 0-4 are then a lane's own elements (five
-// butterfly stages in registers) and only bits 5-6 cross lanes (two DPP
-// stages, both quad permutes), and RoPE's partner dim i+32 is in lane gl^1 (one
-// quad permute); with 8 dims per lane the same vector took four cross-lane
-// stages, one of them two DPP moves, and a two-move RoPE exchange.  A group of
-// 4 lanes takes 64 / kGroups4 heads of its token; group 0 also the key.  The
-// rotation's lane-instruction count per vector drops by about 44 %; the time
-// less (8192 tokens: 12 %), as the key's extra pass and the loads' latency
-// remain.
+// Many tokens: 4 lanes per vector, 32 dims per lane.  Lane gl holds the four
+// 8-dim chunks 32q + 8gl .. +7 (q = 0..3; four 16-byte loads), element 8q + j
+// being dim 32q + 8gl + j.  So every RoPE pair (i, i+32), i = 8gl + j, sits in
+// one lane as elements j and 8 + j, and of the rotation's index bits, 0-2 (j)
+// and 5-6 (q) are a lane's own elements (five butterfly stages in registers)
+// while only bits 3-4 (gl) cross lanes (two DPP stages, both quad permutes).  With 8 dims per lane the same vector took four cross-lane stages,
+// one of them two DPP moves, and a two-move RoPE exchange.  A group of 4 lanes
+// takes 64 / kGroups4 heads of its token; group 0 also the key.
 template <int kGroups4>
 __global__ __launch_bounds__(4 * kGroups4) void indexer_prep_wide_kernel(
     const uint16_t* __restrict__ q_in, const uint16_t* __restrict__ k_in,
@@ -250,55 +248,48 @@ __global__ __launch_bounds__(4 * kGroups4) void indexer_prep_wide_kernel(
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      raw[i][u] = ldg16(qsrc + (grp + kGroups4 * i) * kPrepDim + 32 * gl + 8 * u);
+    for (int q = 0; q < 4; ++q)
+      raw[i][q] = ldg16(qsrc + (grp + kGroups4 * i) * kPrepDim + 32 * q + 8 * gl);
   const bool has_key = grp == 0;
   uint4 kraw[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
                    make_uint4(0, 0, 0, 0)};
   if (has_key) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kraw[u] = ldg16(k_in + (size_t)token * kPrepDim + 32 * gl + 8 * u);
+    for (int q = 0; q < 4; ++q) kraw[q] = ldg16(k_in + (size_t)token * kPrepDim + 32 * q + 8 * gl);
   }
 
   const int b = token / T;
   const int t = token - b * T;
   const int pos = end_pos[b] - T + t;
   const int row = min(max(pos, 0), S_max - 1);
-  // RoPE on dims 0..63 (lanes 0 and 1): pair k (0..31) is dim k in lane 0 and
-  // dim 32 + k in lane 1.  lower: x1 c - x2 s;  upper: x1 s + x2 c, i.e.
-  // e c + p s' with s' = -s in lane 0 (p = the partner's value).
-  const bool rope = gl < 2;
-  const float ssgn = (gl & 1) ? 1.0f : -1.0f;
-  float c[32], sr[32];
-  if (rope) {
-    const float4* cs = reinterpret_cast<const float4*>(rope_cos + (size_t)row * kPrepRopeHalf);
-    const float4* sn = reinterpret_cast<const float4*>(rope_sin + (size_t)row * kPrepRopeHalf);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 cv = cs[u], sv = sn[u];
-      c[4 * u] = cv.x, c[4 * u + 1] = cv.y, c[4 * u + 2] = cv.z, c[4 * u + 3] = cv.w;
-      sr[4 * u] = ssgn * sv.x, sr[4 * u + 1] = ssgn * sv.y;
-      sr[4 * u + 2] = ssgn * sv.z, sr[4 * u + 3] = ssgn * sv.w;
-    }
-  }
+  // RoPE pairs i = 8gl + j: lower dim i is element j, upper dim i + 32 element 8 + j;
+  // lower' = x1 c - x2 s, upper' = x1 s + x2 c.
+  const float* cs = rope_cos + (size_t)row * kPrepRopeHalf + 8 * gl;
+  const float* sn = rope_sin + (size_t)row * kPrepRopeHalf + 8 * gl;
+  const float4 c0 = *reinterpret_cast<const float4*>(cs);
+  const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(sn);
+  const float4 s1 = *reinterpret_cast<const float4*>(sn + 4);
+  const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   const float sg1 = (gl & 1) ? -1.0f : 1.0f, sg2 = (gl & 2) ? -1.0f : 1.0f;
 
   auto process = [&](const uint4 (&v)[4], bool store, void* dst, float* scale_dst) {
     float e[32];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int q = 0; q < 4; ++q) {
       float f[8];
-      bf16x8_to_f32(v[u], f);
+      bf16x8_to_f32(v[q], f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[8 * u + j] = f[j];
+      for (int j = 0; j < 8; ++j) e[8 * q + j] = f[j];
     }
-    // RoPE (the partner lane gl ^ 1 holds the other half of every pair).
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float p = row_xor<1>(e[k]);
-      if (rope) e[k] = fmaf(p, sr[k], e[k] * c[k]);
+    for (int j = 0; j < 8; ++j) {
+      const float x1 = e[j], x2 = e[8 + j];
+      e[j] = fmaf(x2, -sr[j], x1 * c[j]);  // the rounding order of rotate_store's callers
+      e[8 + j] = fmaf(x1, sr[j], x2 * c[j]);
     }
-    // Rotation: index bits 0-4 in registers...
+    // Rotation: element bits (dim bits 0-2 and 5-6) in registers...
 #pragma unroll
     for (int h = 1; h < 32; h *= 2) {
 #pragma unroll
@@ -309,7 +300,7 @@ __global__ __launch_bounds__(4 * kGroups4) void indexer_prep_wide_kernel(
         e[k + h] = a - d;
       }
     }
-    // ...bits 5 and 6 across the 4 lanes.
+    // ...dim bits 3 and 4 across the 4 lanes.
 #pragma unroll
     for (int k = 0; k < 32; ++k) e[k] = fmaf(sg1, e[k], row_xor<1>(e[k]));
 #pragma unroll
@@ -321,46 +312,47 @@ __global__ __launch_bounds__(4 * kGroups4) void indexer_prep_wide_kernel(
       amax = fmaxf(amax, row_xor<1>(amax));
       amax = fmaxf(amax, row_xor<2>(amax));
       const float su = amax / kE4m3Max;
-      uint32_t w[8];
+      uint32_t w[8];  // chunk q: words 2q, 2q + 1
       if (su >= kTinyScale) {
         // Correctly rounded x / su as in rotate_store (Markstein correction).
         const float y = 1.0f / su;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          float q[4];
+        for (int m = 0; m < 8; ++m) {
+          float qv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float x = e[4 * k + j];
+            const float x = e[4 * m + j];
             const float q0 = x * y;
-            q[j] = fmaf(-fmaf(q0, su, -x), y, q0);
+            qv[j] = fmaf(-fmaf(q0, su, -x), y, q0);
           }
-          w[k] = e4m3_pack2(q[0], q[1]) | (e4m3_pack2(q[2], q[3]) << 16);
+          w[m] = e4m3_pack2(qv[0], qv[1]) | (e4m3_pack2(qv[2], qv[3]) << 16);
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          float q[4];
+        for (int m = 0; m < 8; ++m) {
+          float qv[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) q[j] = su > 0.0f ? e[4 * k + j] / su : 0.0f;
-          w[k] = su > 0.0f ? (e4m3_pack2(q[0], q[1]) | (e4m3_pack2(q[2], q[3]) << 16)) : 0u;
+          for (int j = 0; j < 4; ++j) qv[j] = su > 0.0f ? e[4 * m + j] / su : 0.0f;
+          w[m] = su > 0.0f ? (e4m3_pack2(qv[0], qv[1]) | (e4m3_pack2(qv[2], qv[3]) << 16)) : 0u;
         }
       }
       if (store) {
-        uint4* d4 = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + 32 * gl);
-        d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        uint8_t* d8 = reinterpret_cast<uint8_t*>(dst) + 8 * gl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(d8 + 32 * q) = make_uint2(w[2 * q], w[2 * q + 1]);
         if (gl == 0) *scale_dst = su * kInvSqrtDim;
       }
     } else if (store) {
-      uint4* d4 = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + 32 * gl);
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dst) + 8 * gl;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int q = 0; q < 4; ++q) {
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          w[j] = (uint32_t)f32_to_bf16_bits(e[8 * u + 2 * j] * kInvSqrtDim) |
-                 ((uint32_t)f32_to_bf16_bits(e[8 * u + 2 * j + 1] * kInvSqrtDim) << 16);
-        d4[u] = make_uint4(w[0], w[1], w[2], w[3]);
+          w[j] = (uint32_t)f32_to_bf16_bits(e[8 * q + 2 * j] * kInvSqrtDim) |
+                 ((uint32_t)f32_to_bf16_bits(e[8 * q + 2 * j + 1] * kInvSqrtDim) << 16);
+        *reinterpret_cast<uint4*>(d16 + 32 * q) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   };
@@ -384,8 +376,8 @@ __global__ __launch_bounds__(4 * kGroups4) void indexer_prep_wide_kernel(
 
 // Few tokens: 64 groups of 16 lanes (1024 lanes), one head each, to spread the
 // vectors of a token over more SIMDs; many tokens: 64 groups of 4 lanes (32 dims a
-// lane), one head each (8192 tokens: 74.4 -> 63.8 us; 600 tokens: 9.8 us either
-// way, where one 64-lane workgroup a token took 13.2 us).
+// lane), one head each (8192 tokens: 74.4 us with 8 dims a lane, 62 us with 32
+// consecutive dims, 55.8 us with the four chunks; 600 tokens: 9.8, 8.9, 7.5 us).
 constexpr int kPrepSmallTokens = 512;
 
 int launch_indexer_prep(const void* q_in, const void* k_in, const float* rope_cos,
