@@ -7,11 +7,13 @@
 // concatenated (non-interleaved) layout that "MaxText PR #2933" describes
 // for the indexer: dim i and dim i+32 are the two parts of one rotated pair.
 //
-// Work split.  One 128-dim vector per 16 lanes, 8 consecutive dims per lane
-// (one 16-byte load); one workgroup per token (64 query heads, then the key).
-// This is a streaming kernel -- 256 bytes in and 132 (fp8) or 256 (bf16)
-// bytes out per vector -- so the design goal is full 16-byte accesses, many
-// loads in flight per lane and no LDS.
+// Work split.  One workgroup per token (64 query heads, then the key).  Up
+// to 512 tokens (decode) one 128-dim vector per 16 lanes, 8 consecutive dims
+// per lane (one 16-byte load), described below; more tokens take
+// indexer_prep_wide_kernel, 4 lanes per vector and 32 dims per lane, which
+// needs fewer cross-lane exchanges (described above it).  Either way only
+// 16-byte loads, several in flight per lane, and no LDS: 256 bytes in and 132
+// (fp8) or 256 (bf16) bytes out per vector.
 //
 //   RoPE.  Lane l < 4 of a group holds dims 8l..8l+7 and lane l+4 the dims
 //     32 above them, so each pair is one xor-4 exchange away.
