@@ -1182,6 +1182,37 @@ def test_indexer_prep_random(fp8, kind):
     _check_untouched(kc, ks, ep.cpu(), T, fp8)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kind", ["normal", "zero"])
+def test_indexer_prep_many_tokens(fp8, kind):
+    """More than 512 tokens take the form with 4 lanes and 32 dims per vector (RoPE
+    pairs inside a lane, two cross-lane rotation stages): a ragged batch of 3
+    sequences with 200 new tokens each, both dtypes; "zero" adds all-zero query
+    heads and keys (scale 0, zero codes).  Every written query and key against the
+    oracle, the rest of the cache untouched."""
+    m = dsa()
+    B, T, S_max = 3, 200, 1000
+    banner(f"prep many tokens {kind} fp8={fp8} B={B} T={T}")
+    q_in, k_in, cos, sin, ep = inputs.make_prep(B, T, [200, 640, 1000], S_max, kind=kind,
+                                                seed=73, device=DEV)
+    qo, qs, kc, ks = _prep_run(m, q_in, k_in, cos, sin, ep, S_max, fp8)
+    rq, rqs, rk, rks, pos = oracle.indexer_prep(inputs.to_numpy(q_in), inputs.to_numpy(k_in),
+                                                cos.cpu().numpy(), sin.cpu().numpy(),
+                                                ep.cpu().numpy(), fp8=fp8)
+    gk = np.stack([inputs.to_numpy(kc[b])[pos[b]] for b in range(B)])
+    if fp8:
+        gks = np.stack([ks[b].cpu().numpy()[pos[b]] for b in range(B)])
+        _compare_prep_fp8(qo, qs.cpu().numpy(), rq, rqs)
+        _compare_prep_fp8(torch.from_numpy(gk).view(torch.float8_e4m3fn), gks, rk, rks)
+        if kind == "zero":
+            assert np.all(rqs[:, :, ::7] == 0) and np.all(qs.cpu().numpy()[:, :, ::7] == 0)
+            assert not inputs.to_numpy(qo)[:, :, ::7].any()
+    else:
+        _compare_prep_bf16(qo.float().cpu().numpy(), rq)
+        _compare_prep_bf16(torch.from_numpy(gk).view(torch.bfloat16).float().numpy(), rk)
+    _check_untouched(kc, ks, ep.cpu(), T, fp8)
+
+
 @pytest.mark.parametrize("seed", list(range(8)))
 def test_indexer_prep_random_shapes(seed):
     """dsa_indexer_prep on seeded ragged batches: 1 to 5 sequences, 1 to 300 new
