@@ -21,6 +21,14 @@
 
 namespace dsa {
 
+// ReLU in one instruction: the IEEE-2019 maximum (v_maximum3_f32 on gfx950),
+// which maps -0 to +0 like fmaxf but, unlike it, needs no NaN-quieting
+// instruction before it (fmaxf(x, 0) cost two per element; the 8192-query
+// prefill indexer went from 538 to 495 us with this form).
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_elementwise_maximum(x, 0.0f);
+}
+
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
 constexpr int kIdxWaves = 4;
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[mt][i], 0.f);
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * relu(acc[mt][i]);
     } else {
       const i32x8 kb = i32x8{(int)cur.v[0].x, (int)cur.v[0].y, (int)cur.v[0].z, (int)cur.v[0].w,
                              (int)cur.v[1].x, (int)cur.v[1].y, (int)cur.v[1].z, (int)cur.v[1].w};
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
                               (int)qa[mt][1].z, (int)qa[mt][1].w};
         const f32x4 acc = mfma_fp8_16x16x128(a, kb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * relu(acc[i]);
       }
     }
     v = group_sum(v);
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[mt][i], 0.f);
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * relu(acc[mt][i]);
     } else {
       const uint4 k0 = *reinterpret_cast<const uint4*>(krow + (((2 * g) ^ (r16 & 7)) << 4));
       const uint4 k1 = *reinterpret_cast<const uint4*>(krow + (((2 * g + 1) ^ (r16 & 7)) << 4));
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
                               (int)qa[mt][1].z, (int)qa[mt][1].w};
         const f32x4 acc = mfma_fp8_16x16x128(a, kb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += wv[mt][i] * fmaxf(acc[i], 0.f);
+        for (int i = 0; i < 4; ++i) v += wv[mt][i] * relu(acc[i]);
       }
       v *= reinterpret_cast<const float*>(slot + kIdxTile * kRowBytes)[r16];
     }
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x += wv[qq][mt][i] * fmaxf(acc[qq][mt][i], 0.f);
+          for (int i = 0; i < 4; ++i) x += wv[qq][mt][i] * relu(acc[qq][mt][i]);
         v[qq] = group_sum(x);
       }
       const int s = s_begin + tile * kPfTile + nt * 16 + r16;
